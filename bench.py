@@ -1,0 +1,339 @@
+"""Benchmark of the matrix-product dispatch on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME] [--no-cpu]
+
+A step is one pass of the hot path over one batch of synthetic input. The
+headline line is the f16 decode GEMV (x [1, 4096] . W[11008, 4096]^T through
+mm_gemm, which routes to the GEMV kernel): `value` is its achieved HBM
+bandwidth from algorithmic bytes (W + x + y, each moved once) over the
+measured time per step. The other four workloads (f32 GEMM 128^3, batched f16
+GEMM, f16 GEMM 8192^3, 64-expert bf16 expert-ID prefill + decode) are timed
+the same way and reported under "workloads".
+
+Timing: inputs are resident in HBM before the timed region. Each workload
+rotates through enough copies of its operands that a buffer is reused only
+after >= 1 GiB of other traffic (more than the 256 MB Infinity Cache). The
+rotated calls are captured once in a HIP graph and the graph is replayed;
+the time per step comes from HIP events recorded on the stream the kernels
+run on, bracketed by device synchronisation.
+
+cpu_baseline: the CPU oracle (test infrastructure, fp64 triple loops) timed
+on this host on the same decode GEMV, repeated to about ten seconds of work.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2516.6
+F32_PEAK_TFLOPS = 157.3
+ROTATE_BYTES = 1 << 30
+METRIC = "GEMM TFLOP/s and GEMV/matmul_id HBM GB/s, as % of MI355X roofline"
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--only", default="", help="comma list: gemm_f32_128,gemv_f16_decode,"
+                    "gemm_f16_batched,gemm_f16_large,moe_prefill,moe_decode")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-graph", action="store_true", help="time direct launches, no HIP graph")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device copy of this many bytes (counter calibration)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "gemv_expert_id_amd", "csrc"))):
+        with open(os.path.join(ROOT, "gemv_expert_id_amd", "csrc", f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+class Timer:
+    """Times `steps` launches of step(i) (i = rotation index) with HIP events."""
+
+    def __init__(self, torch, stream, use_graph):
+        self.torch = torch
+        self.stream = stream
+        self.use_graph = use_graph
+
+    def time(self, step, n_rot, steps, warmup):
+        torch = self.torch
+        with torch.cuda.stream(self.stream):
+            for i in range(warmup):
+                step(i % n_rot)
+            torch.cuda.synchronize()
+            if self.use_graph:
+                reps = max(1, steps // n_rot)
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=self.stream):
+                    for i in range(n_rot):
+                        step(i)
+                g.replay()
+                torch.cuda.synchronize()
+                t0 = torch.cuda.Event(enable_timing=True)
+                t1 = torch.cuda.Event(enable_timing=True)
+                t0.record(self.stream)
+                for _ in range(reps):
+                    g.replay()
+                t1.record(self.stream)
+                torch.cuda.synchronize()
+                n = reps * n_rot
+            else:
+                t0 = torch.cuda.Event(enable_timing=True)
+                t1 = torch.cuda.Event(enable_timing=True)
+                t0.record(self.stream)
+                for i in range(steps):
+                    step(i % n_rot)
+                t1.record(self.stream)
+                torch.cuda.synchronize()
+                n = steps
+        return t0.elapsed_time(t1) / n, n  # ms per step
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gemv_expert_id_amd as mm
+    import workloads as wl
+
+    if not os.path.exists(mm.LIB_PATH):
+        from gemv_expert_id_amd import build as mm_build
+        mm_build.build()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.Stream(dev)
+    caps = mm.mm_capabilities(0)
+    log(f"device {caps.arch.decode()} cus={caps.cu_count} max_clock={caps.max_clock_mhz} MHz")
+
+    if args.copy_bytes:
+        n = args.copy_bytes // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {n * 4} bytes x5")
+        return
+
+    def to_dev(bits):
+        bits = np.ascontiguousarray(bits)
+        view = {np.dtype(np.float32): None, np.dtype(np.uint16): np.int16,
+                np.dtype(np.uint32): np.int32}[bits.dtype]
+        return torch.from_numpy(bits if view is None else bits.view(view)).to(dev)
+
+    def rotations(nbytes):
+        # Tiny launch-bound problems stay cache-resident whatever we do; cap the graph size.
+        return min(64, max(1, math.ceil(ROTATE_BYTES / max(1, nbytes))))
+
+    timer = Timer(torch, stream, not args.no_graph)
+    only = set(filter(None, args.only.split(",")))
+    results = {}
+
+    def want(name):
+        return not only or name in only
+
+    # ---------------------------------------------------------------- GEMM family
+    def gemm_workload(name, case, bound, alg_bytes):
+        a = to_dev(case.A)
+        b = to_dev(case.B)
+        in_bytes = a.numel() * a.element_size() + b.numel() * b.element_size()
+        n_rot = rotations(in_bytes)
+        As = [a] + [a.clone() for _ in range(n_rot - 1)]
+        Bs = [b] + [b.clone() for _ in range(n_rot - 1)]
+        c = torch.empty(case.c_elems, dtype=a.dtype, device=dev)
+        d = mm.gemm_desc(case.dtype, case.m, case.n, case.k, batch=case.batch,
+                         trans_a=case.trans_a, trans_b=case.trans_b, lda=case.lda,
+                         ldb=case.ldb, ldc=case.ldc, stride_a=case.stride_a,
+                         stride_b=case.stride_b, stride_c=case.stride_c)
+        bufs = [(mm.buf(As[i]), mm.buf(Bs[i])) for i in range(n_rot)]
+        cbuf = mm.buf(c)
+        rec = mm.mm_gemm(d, bufs[0][0], bufs[0][1], cbuf, stream=stream)
+
+        def step(i):
+            mm.mm_gemm(d, bufs[i][0], bufs[i][1], cbuf, stream=stream)
+
+        steps = args.steps if case.flops < 1e11 else max(n_rot, args.steps // 10)
+        ms, n = timer.time(step, n_rot, steps, args.warmup)
+        sec = ms * 1e-3
+        tflops = case.flops / sec / 1e12
+        gbs = alg_bytes / sec / 1e9
+        if bound == "hbm":
+            achieved, peak, unit = gbs, HBM_PEAK_GBS, "GB/s"
+        elif bound == "mfma":
+            achieved, peak, unit = tflops, MFMA_F16_PEAK_TFLOPS, "TFLOP/s"
+        else:
+            achieved, peak, unit = tflops, F32_PEAK_TFLOPS, "TFLOP/s"
+        results[name] = {
+            "route": "gemv" if rec.route == mm.MM_ROUTE_GEMV else "gemm",
+            "us_per_call": ms * 1e3, "calls_timed": n, "rotations": n_rot,
+            "tflops": tflops, "alg_gbs": gbs, "alg_bytes": alg_bytes, "flops": case.flops,
+            "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+            "frac": achieved / peak,
+        }
+        log(f"{name}: {ms * 1e3:.2f} us/call  {tflops:.2f} TFLOP/s  {gbs:.1f} GB/s  "
+            f"({achieved / peak * 100:.1f}% of {bound} peak)")
+        del As, Bs, c
+        torch.cuda.empty_cache()
+
+    if want("gemv_f16_decode"):
+        case = wl.gemv_f16_decode()
+        gemm_workload("gemv_f16_decode", case, "hbm", case.B.nbytes + case.A.nbytes + 11008 * 2)
+    if want("gemm_f32_128"):
+        case = wl.gemm_f32_128()
+        gemm_workload("gemm_f32_128", case, "f32", 3 * 128 * 128 * 4)
+    if want("gemm_f16_batched"):
+        case = wl.gemm_f16_batched()
+        gemm_workload("gemm_f16_batched", case, "hbm", case.A.nbytes + case.B.nbytes + 32 * 512 * 512 * 2)
+    if want("gemm_f16_large"):
+        case = wl.gemm_f16_large()
+        gemm_workload("gemm_f16_large", case, "mfma", case.A.nbytes + case.B.nbytes + 8192 * 8192 * 2)
+
+    # ---------------------------------------------------------------- expert-ID
+    if want("moe_prefill") or want("moe_decode"):
+        moe = wl.moe_bf16()
+        pre, dec = moe.prefill, moe.decode
+        w = to_dev(pre.W)
+        wbytes = w.numel() * 2
+        n_rot = rotations(wbytes)
+        Ws = [w] + [w.clone() for _ in range(n_rot - 1)]
+        if want("moe_prefill"):
+            x = to_dev(pre.X.reshape(-1))
+            ids = to_dev(pre.ids.reshape(-1))
+            out = torch.empty(pre.m * pre.top_k * pre.n, dtype=torch.float32, device=dev)
+            cnt = torch.empty(pre.n_experts, dtype=torch.int32, device=dev)
+            rr = torch.empty(pre.n_experts * pre.m, dtype=torch.int32, device=dev)
+            p = mm.id_params(pre.m, pre.n, pre.k, pre.top_k, pre.n_experts,
+                             pre.expert_stride_bytes, 0, 0, 1)
+            wb = [mm.buf(t) for t in Ws]
+            xb, ib, ob, cb, rb = mm.buf(x), mm.buf(ids), mm.buf(out), mm.buf(cnt), mm.buf(rr)
+
+            def step(i):
+                mm.mm_id(p, wl.BF16, wb[i], xb, ib, ob, cb, rb, stream=stream)
+
+            ms, n = timer.time(step, n_rot, max(n_rot, args.steps // 4), args.warmup)
+            alg = wbytes + pre.X.nbytes + pre.ids.nbytes + out.numel() * 4
+            sec = ms * 1e-3
+            results["moe_prefill"] = {
+                "route": "map+grouped", "us_per_call": ms * 1e3, "calls_timed": n,
+                "rotations": n_rot, "tflops": pre.flops / sec / 1e12,
+                "alg_gbs": alg / sec / 1e9, "alg_bytes": alg, "flops": pre.flops, "bound": "hbm",
+                "achieved": alg / sec / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": alg / sec / 1e9 / HBM_PEAK_GBS,
+            }
+            log(f"moe_prefill: {ms * 1e3:.2f} us/call  {alg / sec / 1e9:.1f} GB/s  "
+                f"{pre.flops / sec / 1e12:.1f} TFLOP/s")
+        if want("moe_decode"):
+            x = to_dev(dec.X.reshape(-1))
+            ids = to_dev(dec.ids.reshape(-1))
+            out = torch.empty(dec.top_k * dec.n, dtype=torch.float32, device=dev)
+            p = mm.id_params(dec.m, dec.n, dec.k, dec.top_k, dec.n_experts,
+                             dec.expert_stride_bytes, 0, 1, 0)
+            u = len(set(int(v) for v in dec.ids.reshape(-1)))
+            per_call = u * dec.n * dec.k * 2
+            n_rot_d = rotations(per_call)
+            while len(Ws) < n_rot_d:
+                Ws.append(w.clone())
+            wb = [mm.buf(t) for t in Ws]
+            xb, ib, ob = mm.buf(x), mm.buf(ids), mm.buf(out)
+
+            def step(i):
+                mm.mm_id_direct(p, wl.BF16, wb[i], xb, ib, ob, stream=stream)
+
+            ms, n = timer.time(step, n_rot_d, max(n_rot_d, args.steps), args.warmup)
+            alg = per_call + dec.X.nbytes + dec.ids.nbytes + out.numel() * 4
+            sec = ms * 1e-3
+            results["moe_decode"] = {
+                "route": "direct", "distinct_experts": u, "us_per_call": ms * 1e3,
+                "calls_timed": n, "rotations": n_rot_d, "tflops": dec.flops / sec / 1e12,
+                "alg_gbs": alg / sec / 1e9, "alg_bytes": alg, "flops": dec.flops, "bound": "hbm",
+                "achieved": alg / sec / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": alg / sec / 1e9 / HBM_PEAK_GBS,
+            }
+            log(f"moe_decode: {ms * 1e3:.2f} us/call  {alg / sec / 1e9:.1f} GB/s (u={u})")
+        del Ws
+        torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    cpu = None
+    if not args.no_cpu and want("gemv_f16_decode"):
+        import oracle
+        case = wl.gemv_f16_decode()
+        alg = case.B.nbytes + case.A.nbytes + 11008 * 2
+        reps, t_total = 0, 0.0
+        while t_total < 10.0 and reps < 1000:
+            t0 = time.perf_counter()
+            oracle.gemm(case.dtype, 1, 1, case.n, case.k, False, True, case.lda, case.ldb, 0, 0,
+                        0, 0, case.A, case.B)
+            t_total += time.perf_counter() - t0
+            reps += 1
+        cpu = {"value": alg * reps / t_total / 1e9, "unit": "GB/s",
+               "cores": oracle.max_threads(), "kind": "oracle",
+               "sample": f"the full f16 decode GEMV (1 x 4096 by 11008 x 4096), "
+                         f"{reps} repetitions, {t_total:.1f} s of fp64 oracle work"}
+        log(f"cpu oracle: {cpu['value']:.3f} GB/s on {cpu['cores']} threads ({reps} reps)")
+
+    head = results.get("gemv_f16_decode")
+    traffic = None
+    if head is not None and os.path.exists(PROFILE_TRAFFIC):
+        with open(PROFILE_TRAFFIC) as f:
+            prof = json.load(f)
+        ent = prof.get("gemv_f16_decode")
+        if ent and ent.get("kernel_source_hash") == kernel_source_hash():
+            traffic = ent.get("hbm_bytes_per_launch")
+    line = {
+        "metric": METRIC,
+        "value": head["alg_gbs"] if head else None,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": head["calls_timed"] if head else args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["us_per_call"] / 1e3 if head else None,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "f16 decode GEMV: x[1,4096] . W[11008,4096]^T (W stored [N,K]), "
+                               "f32 accumulate, f16 out, seed 1",
+                   "m": 1, "n": 11008, "k": 4096, "trans_b": True,
+                   "timing": "hip graph replay" if not args.no_graph else "direct launches"},
+        "roofline": None if head is None else {
+            "bound": "hbm", "achieved": head["alg_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": head["alg_gbs"] / HBM_PEAK_GBS, "traffic": traffic,
+            "kernel": "gemv_rows_vec<f16>", "alg_bytes_per_launch": head["alg_bytes"]},
+        "cpu_baseline": cpu,
+        "workloads": results,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,65 @@
+// Kernel argument blocks and host-side launchers. The launchers (defined in
+// gemv.hip, gemm.hip, mmid.hip) pick a template instance, size the grid and
+// enqueue exactly one kernel; they never validate (the C ABI layer has done
+// that) and return the hipError_t of the enqueue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mmk {
+
+// Largest expert count of the grouped route (sizes the in-block tile table).
+constexpr int MM_GROUPED_MAX_E = 1024;
+
+// out[o * out_inc] = sum_p M(o, p) * vec[p * vec_inc] for o < rows, with
+// M(o, p) = mat[o * ld + p] (row form) or mat[p * ld + o] (column form).
+struct GemvArgs {
+    const void* mat;
+    const void* vec;
+    void* out;
+    int64_t rows, k, ld;
+    int64_t vec_inc, out_inc;
+    int64_t mat_bstride, vec_bstride, out_bstride;  // elements; 0 = shared
+    int64_t batch;
+    int32_t dtype;       // 0 f32, 1 f16, 2 bf16
+    int32_t col_form;    // 1: M(o, p) = mat[p * ld + o]
+};
+hipError_t launch_gemv(const GemvArgs& a, hipStream_t s);
+
+// C[b] = op(A[b]) . op(B[b]); pointers already include the byte offsets.
+struct GemmArgs {
+    const void* A;
+    const void* B;
+    void* C;
+    int64_t m, n, k;
+    int64_t lda, ldb, ldc;
+    int64_t sa, sb, sc;  // batch strides, elements
+    int64_t batch;
+    int32_t dtype;
+    int32_t ta, tb;
+};
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+
+// Expert-ID matmul. Byte strides locate the activation row of (token, slot).
+struct IdArgs {
+    const void* W;
+    const float* X;
+    const uint32_t* ids;
+    float* out;
+    const uint32_t* counts;       // grouped only
+    const uint32_t* routed_rows;  // grouped only
+    uint32_t* counts_w;           // map only
+    uint32_t* routed_rows_w;      // map only
+    uint32_t m, n, k, top_k, n_experts;
+    uint32_t layout;              // 0 shared per token, 1 slotted
+    uint64_t expert_stride_bytes;
+    uint64_t x_tok_stride_bytes, x_slot_stride_bytes;
+    int32_t wdtype;
+    int32_t dedup;                // direct: repeated ids of one token share one pass
+};
+hipError_t launch_id_direct(const IdArgs& a, hipStream_t s);
+hipError_t launch_id_map(const IdArgs& a, hipStream_t s);
+hipError_t launch_id_grouped(const IdArgs& a, hipStream_t s);
+
+}  // namespace mmk

@@ -1,0 +1,198 @@
+"""GPU parity of the matrix-product dispatch (GEMV and GEMM routes) against the oracle.
+
+Shapes follow the pages' tests (tract-metal mlx_gemm/mod.rs `test_mat_vec`,
+`test_mat_mul`, `gemv_wide_tests`) plus ragged multi-tile cases, every
+transpose layout, padded leading dimensions, byte offsets, batch strides and
+broadcast operands. Floating-point results meet the normalised tolerance;
+ramp and permutation inputs are compared bit for bit.
+"""
+from __future__ import annotations
+
+import itertools
+import sys
+
+import numpy as np
+import pytest
+
+import gemv_expert_id_amd as mm
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = [wl.F32, wl.F16, wl.BF16]
+LAYOUTS = list(itertools.product([False, True], [False, True]))
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    caps = mm.mm_capabilities(0)
+    _say(f"device {caps.arch.decode()} cus={caps.cu_count} clock={caps.max_clock_mhz}MHz")
+    yield
+
+
+from gpu_util import check_gemm  # noqa: E402
+
+
+# (batch, m, n, k) tuples, both readings of the pages' (b, m, k, n)-or-(b, m, n, k) order.
+PAGE_SHAPES = [
+    ((1, 4, 4, 1), False, False), ((10, 1, 4, 4), False, False), ((5, 1, 15, 7), False, True),
+    ((1, 3, 5, 4), False, False), ((1, 2, 5, 10), False, True), ((1, 4, 4, 4), False, True),
+    ((1, 4, 4, 200), False, True), ((1, 25, 1280, 32000), False, True),
+]
+
+
+@pytest.mark.parametrize("shape,ta,tb", PAGE_SHAPES)
+@pytest.mark.parametrize("order", ["bmkn", "bmnk"])
+def test_page_shapes_f32(shape, ta, tb, order):
+    b, m, x, y = shape
+    k, n = (x, y) if order == "bmkn" else (y, x)
+    if m * n * k * b > 2e8:
+        pytest.skip("too large for the CPU oracle in a test")
+    _say(f"page shape {shape} order={order} -> b={b} m={m} n={n} k={k} ta={ta} tb={tb}")
+    case = wl.random_gemm_case(7, wl.F32, b, m, n, k, ta, tb)
+    rec = check_gemm(case, what=f"{shape}")
+    assert rec.route == (mm.MM_ROUTE_GEMV if (m == 1 or n == 1) else mm.MM_ROUTE_GEMM)
+    assert rec.dispatch_count == 1
+
+
+def test_lm_head_shape_f32():
+    """(1, 25, 1280, 32000) + tB read as m=25, k=1280, n=32000 (LM-head shape)."""
+    _say("lm head f32 m=25 k=1280 n=32000")
+    case = wl.random_gemm_case(8, wl.F32, 1, 25, 32000, 1280, False, True)
+    check_gemm(case, what="lm-head")
+
+
+@pytest.mark.parametrize("dt", DTYPES)
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+@pytest.mark.parametrize("shape", [(1, 130, 260, 70), (3, 257, 129, 95), (2, 64, 48, 300),
+                                   (1, 2, 256, 128), (1, 15, 256, 128), (2, 200, 3, 17)])
+def test_gemm_layouts_ragged(dt, ta, tb, shape):
+    b, m, n, k = shape
+    _say(f"gemm dt={wl.DTYPE_NAMES[dt]} ta={ta} tb={tb} b={b} m={m} n={n} k={k}")
+    case = wl.random_gemm_case(11 + m, dt, b, m, n, k, ta, tb)
+    check_gemm(case, what=f"{dt} {ta} {tb} {shape}")
+
+
+@pytest.mark.parametrize("dt", DTYPES)
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_gemm_padded_offsets_strides(dt, ta, tb):
+    rng = np.random.default_rng(3)
+    b, m, n, k = 3, 70, 90, 45
+    a = rng.standard_normal((b, k, m) if ta else (b, m, k))
+    bb = rng.standard_normal((b, n, k) if tb else (b, k, n)) / np.sqrt(k)
+    case = wl.make_gemm_case(dt, a, bb, ta, tb, lda=a.shape[2] + 5, ldb=bb.shape[2] + 3,
+                             ldc=n + 6, off_a=3, off_b=5, off_c=1,
+                             stride_a=a.shape[1] * (a.shape[2] + 5) + 11,
+                             stride_c=m * (n + 6) + 9)
+    _say(f"gemm padded dt={wl.DTYPE_NAMES[dt]} ta={ta} tb={tb}")
+    check_gemm(case, what="padded")
+
+
+@pytest.mark.parametrize("dt", DTYPES)
+def test_gemm_broadcast_operands(dt):
+    rng = np.random.default_rng(4)
+    b, m, n, k = 4, 33, 65, 40
+    a = rng.standard_normal((1, m, k))
+    bb = rng.standard_normal((b, n, k)) / np.sqrt(k)
+    case = wl.make_gemm_case(dt, np.broadcast_to(a, (b, m, k)), bb, False, True, broadcast_a=True)
+    _say(f"gemm broadcast A dt={wl.DTYPE_NAMES[dt]}")
+    check_gemm(case, what="broadcast A")
+    bb1 = rng.standard_normal((1, k, n)) / np.sqrt(k)
+    a4 = rng.standard_normal((b, m, k))
+    case = wl.make_gemm_case(dt, a4, np.broadcast_to(bb1, (b, k, n)), False, False,
+                             broadcast_b=True)
+    _say(f"gemm broadcast B dt={wl.DTYPE_NAMES[dt]}")
+    check_gemm(case, what="broadcast B")
+
+
+@pytest.mark.parametrize("dt", DTYPES)
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+@pytest.mark.parametrize("shape", [(2, 1, 300, 129), (3, 257, 1, 64), (1, 1, 1, 77),
+                                   (1, 1, 4099, 520), (2, 1030, 1, 33)])
+def test_gemv_route(dt, ta, tb, shape):
+    b, m, n, k = shape
+    _say(f"gemv dt={wl.DTYPE_NAMES[dt]} ta={ta} tb={tb} b={b} m={m} n={n} k={k}")
+    case = wl.random_gemm_case(21 + n, dt, b, m, n, k, ta, tb)
+    rec = check_gemm(case, entry=mm.mm_gemv, what="gemv")
+    assert rec.route == mm.MM_ROUTE_GEMV
+
+
+@pytest.mark.parametrize("dt", DTYPES)
+def test_gemv_padded_strided(dt):
+    rng = np.random.default_rng(5)
+    # m == 1, A stored transposed [k, 1] with lda > 1: a strided vector.
+    b, m, n, k = 2, 1, 301, 200
+    a = rng.standard_normal((b, k, m))
+    bb = rng.standard_normal((b, n, k)) / np.sqrt(k)
+    case = wl.make_gemm_case(dt, a, bb, True, True, lda=3, ldb=k + 8, off_a=1, off_b=2, off_c=3)
+    _say(f"gemv strided vector dt={wl.DTYPE_NAMES[dt]}")
+    check_gemm(case, what="strided vector")
+    # n == 1: output stride ldc > 1.
+    b, m, n, k = 2, 150, 1, 130
+    a = rng.standard_normal((b, m, k))
+    bb = rng.standard_normal((b, k, n)) / np.sqrt(k)
+    case = wl.make_gemm_case(dt, a, bb, False, False, ldc=5, ldb=2)
+    _say(f"gemv strided output dt={wl.DTYPE_NAMES[dt]}")
+    check_gemm(case, what="strided output")
+
+
+@pytest.mark.parametrize("dt", DTYPES)
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+@pytest.mark.parametrize("shape", [(1, 3, 130, 260), (1, 7, 63, 2048), (2, 4, 2, 512),
+                                   (1, 1, 1000, 4096), (1, 1000, 1, 4096), (2, 129, 131, 257)])
+def test_ramp_bit_exact(dt, ta, tb, shape):
+    """Ramp inputs (tract-metal gemv_wide tests): all partial sums are exact in
+    f32, so every route must reproduce the rounded oracle bit for bit."""
+    b, m, n, k = shape
+    a = wl.ramp(b * m * k, 1).reshape((b, k, m) if ta else (b, m, k))
+    bb = wl.ramp(b * n * k, 2).reshape((b, n, k) if tb else (b, k, n))
+    case = wl.make_gemm_case(dt, a, bb, ta, tb)
+    _say(f"ramp dt={wl.DTYPE_NAMES[dt]} ta={ta} tb={tb} shape={shape}")
+    check_gemm(case, exact=True, what="ramp")
+
+
+@pytest.mark.parametrize("dt", DTYPES)
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_permutation_bit_exact(dt, ta, tb):
+    rng = np.random.default_rng(6)
+    b, m, k = 2, 70, 96
+    n = k
+    a_log = rng.standard_normal((b, m, k))
+    p = np.zeros((b, k, n))
+    for i in range(b):
+        p[i, rng.permutation(k), np.arange(n)] = 1.0
+    case = wl.make_gemm_case(dt, a_log.transpose(0, 2, 1) if ta else a_log,
+                             p.transpose(0, 2, 1) if tb else p, ta, tb)
+    _say(f"permutation dt={wl.DTYPE_NAMES[dt]} ta={ta} tb={tb}")
+    check_gemm(case, exact=True, what="permutation")
+
+
+def test_all_ones_page_example():
+    """(10, 32, 32, 16) all ones -> 16 everywhere (tract-metal `test_mlx_gemm`)."""
+    for dt in DTYPES:
+        case = wl.make_gemm_case(dt, np.ones((10, 32, 16)), np.ones((10, 16, 32)), False, False)
+        _say(f"all ones dt={wl.DTYPE_NAMES[dt]}")
+        check_gemm(case, exact=True, what="all ones")
+
+
+def test_worked_example_page():
+    """Ramp 0.. (2, 2, 4, 3) -> the 16 values printed in tract-metal `test_mlx_gemm`."""
+    a = np.arange(12, dtype=np.float64).reshape(2, 2, 3)
+    b = np.arange(24, dtype=np.float64).reshape(2, 3, 4)
+    for dt in DTYPES:
+        case = wl.make_gemm_case(dt, a, b, False, False)
+        _say(f"worked example dt={wl.DTYPE_NAMES[dt]}")
+        check_gemm(case, exact=True, what="worked example")
+
+
+def test_large_k_many_tiles_f16():
+    _say("f16 NT m=300 n=520 k=4100")
+    case = wl.random_gemm_case(31, wl.F16, 1, 300, 520, 4100, False, True)
+    check_gemm(case, what="large k")
