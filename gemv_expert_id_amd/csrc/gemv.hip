@@ -4,9 +4,9 @@
 // handles a matrix whose outputs are contiguous).
 //
 // HBM-bound: every matrix byte is read once. Row form (outputs along rows that
-// are contiguous in the contraction index): each wave owns R rows, lanes pull
-// 16-byte chunks with several loads in flight, the vector chunk is reused
-// across the R rows, and a wave-wide shuffle reduction finishes each row.
+// are contiguous in the contraction index): each wave owns one row, lanes pull
+// it as non-temporal 16-byte chunks with eight loads in flight, and a
+// wave-wide shuffle reduction finishes the row.
 // Column form (outputs contiguous): lanes own 16-byte runs of outputs, the
 // four waves of a block split the contraction, and LDS sums their partials in
 // a fixed order. No MFMA: the arithmetic intensity is ~1 FLOP/byte.
@@ -36,6 +36,34 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
 
 // Row form with 16-byte loads. Requires k % Elems16 == 0, ld and the batch
 // strides multiples of Elems16, 16-byte aligned bases and vec_inc == 1.
+// Each lane issues U independent 16-byte loads per row before using any;
+// the remainder of the row is walked with 4, 2 and then 1 loads in flight.
+template <class T, int R, int UU>
+__device__ __forceinline__ void rows_chunk(const typename T::store_t* const* rowp,
+                                           const typename T::store_t* vec, int64_t c,
+                                           float* acc) {
+    constexpr int CH = T::Elems16;
+    u32x4 xv[UU], wv[R][UU];
+#pragma unroll
+    for (int u = 0; u < UU; ++u) xv[u] = ld16(vec + (c + kWave * u) * CH);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int u = 0; u < UU; ++u) wv[r][u] = ld16_stream(rowp[r] + (c + kWave * u) * CH);
+#pragma unroll
+    for (int u = 0; u < UU; ++u) {
+        float xf[CH];
+        unpack<T>(xv[u], xf);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float wf[CH];
+            unpack<T>(wv[r][u], wf);
+#pragma unroll
+            for (int q = 0; q < CH; ++q) acc[r] = __builtin_fmaf(wf[q], xf[q], acc[r]);
+        }
+    }
+}
+
 template <class T, int R, int U>
 __global__ __launch_bounds__(kThreads) void gemv_rows_vec(GemvArgs a) {
     using S = typename T::store_t;
@@ -59,38 +87,16 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_vec(GemvArgs a) {
         for (int r = 0; r < R; ++r) acc[r] = 0.f;
 
         int64_t c = lane;
-        for (; c + kWave * (U - 1) < nch; c += kWave * U) {
-            u32x4 xv[U], wv[R][U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) xv[u] = ld16(vec + (c + kWave * u) * CH);
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-#pragma unroll
-                for (int u = 0; u < U; ++u) wv[r][u] = ld16_stream(rowp[r] + (c + kWave * u) * CH);
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                float xf[CH];
-                unpack<T>(xv[u], xf);
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    float wf[CH];
-                    unpack<T>(wv[r][u], wf);
-#pragma unroll
-                    for (int q = 0; q < CH; ++q) acc[r] = __builtin_fmaf(wf[q], xf[q], acc[r]);
-                }
-            }
+        for (; c + kWave * (U - 1) < nch; c += kWave * U) rows_chunk<T, R, U>(rowp, vec, c, acc);
+        if (U > 4 && c + kWave * 3 < nch) {
+            rows_chunk<T, R, 4>(rowp, vec, c, acc);
+            c += kWave * 4;
         }
-        for (; c < nch; c += kWave) {
-            float xf[CH];
-            unpack<T>(ld16(vec + c * CH), xf);
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                float wf[CH];
-                unpack<T>(ld16_stream(rowp[r] + c * CH), wf);
-#pragma unroll
-                for (int q = 0; q < CH; ++q) acc[r] = __builtin_fmaf(wf[q], xf[q], acc[r]);
-            }
+        if (U > 2 && c + kWave < nch) {
+            rows_chunk<T, R, 2>(rowp, vec, c, acc);
+            c += kWave * 2;
         }
+        for (; c < nch; c += kWave) rows_chunk<T, R, 1>(rowp, vec, c, acc);
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
 #pragma unroll
@@ -201,9 +207,9 @@ hipError_t launch_typed(const GemvArgs& a, hipStream_t s) {
         const bool vec = a.k % CH == 0 && a.ld % CH == 0 && a.vec_inc == 1 &&
                          a.mat_bstride % CH == 0 && a.vec_bstride % CH == 0 &&
                          aligned16(a.mat) && aligned16(a.vec);
-        constexpr int R = 2;
+        constexpr int R = 1;  // one row per wave, eight 16-byte loads in flight per lane
         dim3 grid((unsigned)((a.rows + kWaves * R - 1) / (kWaves * R)), gy);
-        const void* fn = vec ? reinterpret_cast<const void*>(&gemv_rows_vec<T, R, 4>)
+        const void* fn = vec ? reinterpret_cast<const void*>(&gemv_rows_vec<T, R, 8>)
                              : reinterpret_cast<const void*>(&gemv_rows_scalar<T, R>);
         return hipLaunchKernel(fn, grid, dim3(kThreads), args, 0, s);
     }

@@ -141,47 +141,171 @@ __global__ __launch_bounds__(kThreads) void id_direct(IdArgs a) {
     }
 }
 
-// ---------------------------------------------------------------------------
-// Map pass: one workgroup of 16 waves; LDS holds per-wave per-expert counters.
-// ---------------------------------------------------------------------------
-constexpr int kMapThreads = 1024;
-constexpr int kMapWaves = kMapThreads / kWave;
+// Direct route, fast form: k % (Elems16 * 64 * DU) == 0, k <= kDirectMaxK,
+// aligned operands. Block = (routed row r, 4 * DR output rows). Each wave
+// issues the non-temporal 16-byte loads of its DR weight rows first, then the
+// block stages the f32 activation row in LDS once (instead of every wave
+// pulling it from L2), and the next group of weight chunks is in flight
+// while the current one is reduced.
+constexpr int kDirectMaxK = 8192;
+constexpr int DR = 2, DU = 4;
 
-__global__ __launch_bounds__(kMapThreads) void id_map(IdArgs a) {
-    extern __shared__ uint32_t cnt[];  // [kMapWaves][n_experts]
+// ONE: the whole row is one group of DU chunks per lane (no second buffer).
+template <class T, bool ONE>
+__global__ __launch_bounds__(kThreads) void id_direct_fast(IdArgs a) {
+    using S = typename T::store_t;
+    constexpr int CH = T::Elems16;
+    constexpr int G = kWave * DU;  // chunks per group
+    extern __shared__ __attribute__((aligned(16))) float xs[];  // k floats
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int64_t per_block = (int64_t)kWaves * DR;
+    const int64_t nchunks = (a.n + per_block - 1) / per_block;
+    const int64_t rows = (int64_t)a.m * a.top_k;
+    const int64_t ngroups = (int64_t)a.k / CH / G;
+    for (int64_t work = blockIdx.x; work < rows * nchunks; work += gridDim.x) {
+        const int64_t r = work / nchunks;
+        const int64_t j0 = (work % nchunks) * per_block + (int64_t)wave * DR;
+        const uint32_t e = a.ids[r];
+        const int64_t t = r / a.top_k, s = r % a.top_k;
+        float* out_r = a.out + r * a.n;
+        if (e >= a.n_experts) {  // no weight address is formed
+            if (lane < DR && j0 + lane < a.n) out_r[j0 + lane] = 0.f;
+            continue;            // uniform across the block
+        }
+        const uint32_t* tok_ids = a.ids + t * a.top_k;
+        if (a.dedup) {
+            bool owned = false;
+            for (int64_t s2 = 0; s2 < s; ++s2) owned |= tok_ids[s2] == e;
+            if (owned) continue;  // uniform across the block
+        }
+        const S* We = reinterpret_cast<const S*>(reinterpret_cast<const char*>(a.W) +
+                                                 (uint64_t)e * a.expert_stride_bytes);
+        const S* rowp[DR];
+#pragma unroll
+        for (int q = 0; q < DR; ++q) {
+            const int64_t j = j0 + q < a.n ? j0 + q : a.n - 1;
+            rowp[q] = We + j * a.k;
+        }
+        u32x4 wv[DR][DU];
+#pragma unroll
+        for (int q = 0; q < DR; ++q)
+#pragma unroll
+            for (int u = 0; u < DU; ++u) wv[q][u] = ld16_stream(rowp[q] + (lane + kWave * u) * CH);
+        const float* x = reinterpret_cast<const float*>(reinterpret_cast<const char*>(a.X) +
+                                                        t * a.x_tok_stride_bytes +
+                                                        s * a.x_slot_stride_bytes);
+        __syncthreads();  // the previous work item's readers are done with xs
+        for (int64_t i = tid; i < a.k / 4; i += kThreads)
+            *reinterpret_cast<f32x4*>(&xs[i * 4]) = *reinterpret_cast<const f32x4*>(x + i * 4);
+        __syncthreads();
+        float acc[DR];
+#pragma unroll
+        for (int q = 0; q < DR; ++q) acc[q] = 0.f;
+        for (int64_t g = 0; g < (ONE ? 1 : ngroups); ++g) {
+            u32x4 nv[ONE ? 1 : DR][DU];
+            const bool more = !ONE && g + 1 < ngroups;
+            if constexpr (!ONE) if (more) {
+#pragma unroll
+                for (int q = 0; q < DR; ++q)
+#pragma unroll
+                    for (int u = 0; u < DU; ++u)
+                        nv[q][u] = ld16_stream(rowp[q] + ((g + 1) * G + lane + kWave * u) * CH);
+            }
+#pragma unroll
+            for (int u = 0; u < DU; ++u) {
+                const float* xc = &xs[(g * G + lane + kWave * u) * CH];
+                float xf[CH];
+#pragma unroll
+                for (int h = 0; h < CH / 4; ++h) unpack4(*reinterpret_cast<const u32x4*>(xc + 4 * h), &xf[4 * h]);
+#pragma unroll
+                for (int q = 0; q < DR; ++q) {
+                    float wf[CH];
+                    unpack_w<T>(wv[q][u], wf);
+#pragma unroll
+                    for (int c = 0; c < CH; ++c) acc[q] = __builtin_fmaf(wf[c], xf[c], acc[q]);
+                }
+            }
+            if constexpr (!ONE) if (more) {
+#pragma unroll
+                for (int q = 0; q < DR; ++q)
+#pragma unroll
+                    for (int u = 0; u < DU; ++u) wv[q][u] = nv[q][u];
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < DR; ++q) acc[q] = wave_sum(acc[q]);
+#pragma unroll
+        for (int q = 0; q < DR; ++q) {
+            if (lane == q && j0 + q < a.n) {
+                out_r[j0 + q] = acc[q];
+                if (a.dedup)
+                    for (int64_t s3 = s + 1; s3 < a.top_k; ++s3)
+                        if (tok_ids[s3] == e) a.out[(t * a.top_k + s3) * a.n + j0 + q] = acc[q];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Map pass: one workgroup of W waves (W chosen by the host so the LDS tables
+// fit). Wave w owns a contiguous segment of routed rows; LDS holds its
+// per-expert counters cnt[w][e] and 64-bit lane masks msk[w][e].
+//   1. counts: every lane adds 1 to cnt[w][ids[r]] (LDS atomics: the totals
+//      do not depend on the order of the adds).
+//   2. an exclusive scan over waves turns cnt[.][e] into each wave's first
+//      slot in expert e's list; counts[e] is the total (cut at m).
+//   3. per 64-row chunk, each lane ORs its lane bit into msk[w][v]; its slot
+//      is the wave's running base for v plus the number of lower lanes in
+//      the mask. Lists therefore come out in ascending r, independent of
+//      timing. Rows of out-of-range ids are zeroed.
+// ---------------------------------------------------------------------------
+constexpr int kMapMaxWaves = 16;
+constexpr int kMapBatch = 4;  // 64-row chunks per batch of id loads
+
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+__global__ __launch_bounds__(kMapMaxWaves * kWave) void id_map(IdArgs a) {
+    extern __shared__ uint64_t map_lds[];  // msk[W][E] (u64), then cnt[W][E] (u32)
+    const int nthreads = blockDim.x, nwaves = nthreads / kWave;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const uint32_t E = a.n_experts;
+    uint64_t* msk_all = map_lds;
+    uint32_t* cnt = reinterpret_cast<uint32_t*>(map_lds + (int64_t)nwaves * E);
     const int64_t total = (int64_t)a.m * a.top_k;
-    for (int64_t i = tid; i < (int64_t)kMapWaves * E; i += kMapThreads) cnt[i] = 0;
-    __syncthreads();
-
-    const int64_t seg = (total + kMapWaves - 1) / kMapWaves;
-    const int64_t seg0 = wave * seg;
-    const int64_t seg1 = seg0 + seg < total ? seg0 + seg : total;
-    uint32_t* my = cnt + (int64_t)wave * E;
-    const uint64_t lt_mask = (1ull << lane) - 1ull;
-
-    // Phase 1: per-wave counts over the wave's contiguous segment.
-    for (int64_t base = seg0; base < seg1; base += kWave) {
-        const int64_t r = base + lane;
-        const uint32_t v = r < seg1 ? a.ids[r] : E;
-        bool pending = r < seg1 && v < E;
-        uint64_t live = __ballot(pending);
-        while (live) {
-            const int leader = __ffsll((unsigned long long)live) - 1;
-            const uint32_t val = __shfl(v, leader);
-            const uint64_t mask = __ballot(pending && v == val);
-            if (lane == leader) my[val] += (uint32_t)__popcll(mask);
-            if (pending && v == val) pending = false;
-            live &= ~mask;
-        }
+    for (int64_t i = tid; i < (int64_t)nwaves * E; i += nthreads) {
+        cnt[i] = 0;
+        msk_all[i] = 0;
     }
     __syncthreads();
 
-    // Phase 2: exclusive scan across waves per expert; counts (cut at m).
-    for (uint32_t e = tid; e < E; e += kMapThreads) {
+    const int64_t seg = (total + nwaves - 1) / nwaves;
+    const int64_t seg0 = wave * seg;
+    const int64_t seg1 = seg0 + seg < total ? seg0 + seg : total;
+    uint32_t* my = cnt + (int64_t)wave * E;
+    uint64_t* msk = msk_all + (int64_t)wave * E;
+    const uint64_t below = (1ull << lane) - 1ull;
+
+    // Ids are read in batches of kMapBatch chunks, all loads issued before use.
+    for (int64_t b0 = seg0; b0 < seg1; b0 += (int64_t)kWave * kMapBatch) {
+        uint32_t v[kMapBatch];
+#pragma unroll
+        for (int q = 0; q < kMapBatch; ++q) {
+            const int64_t r = b0 + q * kWave + lane;
+            v[q] = a.ids[r < seg1 ? r : seg0];
+            if (r >= seg1) v[q] = E;
+        }
+#pragma unroll
+        for (int q = 0; q < kMapBatch; ++q)
+            if (v[q] < E) atomicAdd(&my[v[q]], 1u);
+    }
+    __syncthreads();
+
+    for (uint32_t e = tid; e < E; e += nthreads) {
         uint32_t run = 0;
-        for (int w = 0; w < kMapWaves; ++w) {
+        for (int w = 0; w < nwaves; ++w) {
             const uint32_t c = cnt[(int64_t)w * E + e];
             cnt[(int64_t)w * E + e] = run;
             run += c;
@@ -190,30 +314,43 @@ __global__ __launch_bounds__(kMapThreads) void id_map(IdArgs a) {
     }
     __syncthreads();
 
-    // Phase 3: place each row at its ascending rank; zero rows of bad ids.
-    for (int64_t base = seg0; base < seg1; base += kWave) {
-        const int64_t r = base + lane;
-        const uint32_t v = r < seg1 ? a.ids[r] : E;
-        bool pending = r < seg1 && v < E;
-        uint64_t live = __ballot(pending);
-        while (live) {
-            const int leader = __ffsll((unsigned long long)live) - 1;
-            const uint32_t val = __shfl(v, leader);
-            const uint64_t mask = __ballot(pending && v == val);
-            if (pending && v == val) {
-                const uint32_t pos = my[val] + (uint32_t)__popcll(mask & lt_mask);
-                if (pos < a.m) a.routed_rows_w[(int64_t)val * a.m + pos] = (uint32_t)r;
-                pending = false;
-            }
-            if (lane == leader) my[val] += (uint32_t)__popcll(mask);
-            live &= ~mask;
+    for (int64_t b0 = seg0; b0 < seg1; b0 += (int64_t)kWave * kMapBatch) {
+        uint32_t vb[kMapBatch];
+#pragma unroll
+        for (int q = 0; q < kMapBatch; ++q) {
+            const int64_t r = b0 + q * kWave + lane;
+            vb[q] = a.ids[r < seg1 ? r : seg0];
         }
-        uint64_t bad = __ballot(r < seg1 && v >= E);
-        while (bad) {
-            const int l = __ffsll((unsigned long long)bad) - 1;
-            float* row = a.out + (base + l) * (int64_t)a.n;
-            for (int64_t j = lane; j < a.n; j += kWave) row[j] = 0.f;
-            bad &= bad - 1;
+#pragma unroll
+        for (int q = 0; q < kMapBatch; ++q) {
+            const int64_t base = b0 + q * kWave;
+            if (base >= seg1) break;
+            const int64_t r = base + lane;
+            const bool in = r < seg1;
+            const uint32_t v = in ? vb[q] : E;
+            const bool valid = in && v < E;
+            // In program order within the wave: read the base, publish the lane
+            // bit, read the chunk's mask, then one lane per expert advances the
+            // base and clears the mask.
+            const uint32_t first = valid ? my[v] : 0u;
+            if (valid) atomicOr(reinterpret_cast<unsigned long long*>(&msk[v]), 1ull << lane);
+            const uint64_t mask = valid ? msk[v] : 0ull;
+            const uint32_t rank = lanes_below(mask);
+            if (valid) {
+                const uint32_t pos = first + rank;
+                if (pos < a.m) a.routed_rows_w[(int64_t)v * a.m + pos] = (uint32_t)r;
+                if ((mask & below) == 0) {
+                    my[v] = first + (uint32_t)__popcll(mask);
+                    msk[v] = 0ull;
+                }
+            }
+            uint64_t bad = __ballot(in && v >= E);
+            while (bad) {
+                const int l = __ffsll((unsigned long long)bad) - 1;
+                float* row = a.out + (base + l) * (int64_t)a.n;
+                for (int64_t j = lane; j < a.n; j += kWave) row[j] = 0.f;
+                bad &= bad - 1;
+            }
         }
     }
 }
@@ -223,16 +360,17 @@ __global__ __launch_bounds__(kMapThreads) void id_map(IdArgs a) {
 // ---------------------------------------------------------------------------
 // Rebuild the m-tile list from the counts: tile_start[e] = sum over e' < e of
 // ceil(counts[e'] / BM). Returns the total tile count. Uses s_start[E + 1].
-template <int BM>
+template <int BM, int WAVES = kWaves>
 __device__ uint32_t build_schedule(const IdArgs& a, uint32_t* s_start, uint32_t* s_part) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const uint32_t E = a.n_experts;
-    // Each thread sums 4 consecutive experts (E <= 1024 = 4 * kThreads).
-    uint32_t local[4];
+    // Each thread sums EPT consecutive experts (E <= 1024 = EPT * threads).
+    constexpr int EPT = MM_GROUPED_MAX_E / (WAVES * kWave);
+    uint32_t local[EPT];
     uint32_t sum = 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const uint32_t e = tid * 4 + q;
+    for (int q = 0; q < EPT; ++q) {
+        const uint32_t e = tid * EPT + q;
         uint32_t c = e < E ? a.counts[e] : 0u;
         c = c < a.m ? c : a.m;
         local[q] = (c + BM - 1) / BM;
@@ -251,13 +389,13 @@ __device__ uint32_t build_schedule(const IdArgs& a, uint32_t* s_start, uint32_t*
     for (int w = 0; w < wave; ++w) wave_base += s_part[w];
     uint32_t run = wave_base + incl - sum;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const uint32_t e = tid * 4 + q;
+    for (int q = 0; q < EPT; ++q) {
+        const uint32_t e = tid * EPT + q;
         if (e < E) s_start[e] = run;
         run += local[q];
     }
     uint32_t total = 0;
-    for (int w = 0; w < kWaves; ++w) total += s_part[w];
+    for (int w = 0; w < WAVES; ++w) total += s_part[w];
     if (tid == 0) s_start[E] = total;
     __syncthreads();
     return total;
@@ -284,26 +422,55 @@ __device__ __forceinline__ uint32_t find_expert(const uint32_t* s_start, uint32_
 
 // ---------------------------------------------------------------------------
 // Grouped pass, bf16 weights: MFMA with bf16 hi/lo activation split.
+//
+// Tile = (expert e, up to 128 routed rows, `bn` outputs); the host picks bn
+// (a multiple of 16, at most GW*GF*16) so that the tile count is close to the
+// CU count: every CU streams one contiguous slab of W_e once. Block = GW
+// waves; 16-output fragment f of the tile belongs to wave f % GW. Per 64-wide
+// K step:
+//   W  (read once from HBM) goes straight to registers in MFMA fragment
+//      layout, issued two K steps ahead (three register buffers);
+//   X  (the gathered f32 activation rows) is loaded two steps ahead, split
+//      into bf16 hi = rne(x) and lo = rne(x - hi) with the packed hardware
+//      convert, and written to a double-buffered LDS stage that all waves
+//      of the block share;
+//   MFMA v_mfma_f32_16x16x32_bf16: D[n][row] += W.hi + W.lo.
+// One barrier per K step. W is exact in bf16 and x - hi - lo is below
+// 2^-16 |x|, so the result is f32-accurate.
 // ---------------------------------------------------------------------------
-constexpr int QBM = 128, QBN = 128, QBK = 64;
+constexpr int QBM = 128, QBK = 64;
 constexpr int QLDK = QBK + 8;  // LDS row pitch (elements): 144 bytes
+constexpr int QXS = QBM * QLDK;  // elements per hi (or lo) stage
+constexpr int GW = 8, GF = 3;    // waves per block, fragments per wave
+constexpr int GMAXBN = GW * GF * 16;
 
-__device__ __forceinline__ uint16_t bf16_rne(float x) { return narrow(TBF16{}, x); }
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-template <bool VEC>
-__global__ __launch_bounds__(kThreads) void id_grouped_bf16(IdArgs a) {
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+// FAST: k % 64 == 0, 16-byte aligned operands, input below 4 GiB. Every
+// global load is then issued unconditionally (dead columns read a clamped,
+// valid address and are never stored), so the compiler counts outstanding
+// loads exactly and the prefetches stay in flight across the barrier.
+template <bool VEC, bool FAST>
+__global__ __launch_bounds__(GW * kWave, 1) void id_grouped_bf16(IdArgs a, uint32_t bn) {
+    constexpr int NT = GW * kWave;       // threads
+    constexpr int XRP = NT / 16;         // activation rows per staging pass
+    constexpr int XP = QBM / XRP;        // staging passes
     __shared__ uint32_t s_start[MM_GROUPED_MAX_E + 1];
-    __shared__ uint32_t s_part[kWaves];
+    __shared__ uint32_t s_part[GW];
     __shared__ uint32_t s_rows[QBM];
     __shared__ uint64_t s_xoff[QBM];
-    __shared__ __attribute__((aligned(16))) uint16_t Xhi[QBM * QLDK];
-    __shared__ __attribute__((aligned(16))) uint16_t Xlo[QBM * QLDK];
+    __shared__ __attribute__((aligned(16))) uint16_t Xs[2][2][QXS];  // [stage][hi/lo]
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const uint32_t n_tiles = (a.n + QBN - 1) / QBN;
+    const uint32_t n_tiles = (a.n + bn - 1) / bn;
     uint32_t ti, nt;
     block_to_tile(n_tiles, &ti, &nt);
-    const uint32_t T = build_schedule<QBM>(a, s_start, s_part);
+    const uint32_t T = build_schedule<QBM, GW>(a, s_start, s_part);
     if (ti >= T) return;
     const uint32_t e = find_expert(s_start, a.n_experts, ti);
     uint32_t c = a.counts[e];
@@ -329,105 +496,157 @@ __global__ __launch_bounds__(kThreads) void id_grouped_bf16(IdArgs a) {
     }
     __syncthreads();
 
-    const int64_t n0 = (int64_t)nt * QBN + wave * 32;  // this wave's 32 output columns
+    const int64_t tile_n0 = (int64_t)nt * bn;
+    const int64_t tile_n1 = tile_n0 + bn < a.n ? tile_n0 + bn : a.n;
+    const int nfr = (int)((tile_n1 - tile_n0 + 15) / 16);          // fragments in this tile
+    const int nf_live = nfr > wave ? (nfr - wave + GW - 1) / GW : 0;  // this wave's
     const uint16_t* We = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(a.W) +
                                                            (uint64_t)e * a.expert_stride_bytes);
     const int nmf = (int)((cnt + 15) / 16);  // live 16-row fragments
+    const int64_t nk = (a.k + QBK - 1) / QBK;
 
-    f32x4 acc[8][2];
+    // Columns of this wave's fragments (lane -> column of fragment j).
+    int64_t wcol[GF];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < GF; ++j) {
+        const int64_t col = tile_n0 + (int64_t)(wave + GW * j) * 16 + (lane & 15);
+        wcol[j] = col < tile_n1 ? col : tile_n1 - 1;
+    }
 
-    // Weight fragment loads: lane -> column n0 + nf*16 + lane%16, k offset
-    // kk*32 + (lane/16)*8 within the K step.
-    auto load_w = [&](int64_t k0, u32x4 (&w)[2][2]) {
+    // Activation staging: thread covers 4 consecutive k of rows p*XRP + tid/16.
+    const int xr0 = tid >> 4, xk = (tid & 15) * 4;
+    const char* xrow[FAST ? 1 : XP];
+    uint32_t xoff[XP];  // FAST: byte offset of the row from X
+    bool xlive[XP];
 #pragma unroll
-        for (int nf = 0; nf < 2; ++nf) {
-            const int64_t col = n0 + nf * 16 + (lane & 15);
+    for (int p = 0; p < XP; ++p) {
+        const int row = p * XRP + xr0;
+        xlive[p] = (uint32_t)row < cnt && s_rows[row] != 0xffffffffu;
+        const uint64_t off = xlive[p] ? s_xoff[row] : s_xoff[cnt - 1];
+        xoff[p] = (uint32_t)off + (uint32_t)xk * 4u;
+        if constexpr (!FAST) xrow[p] = reinterpret_cast<const char*>(a.X) + off;
+    }
+    auto load_x = [&](int64_t k0, f32x4 (&xv)[XP]) {
+        if constexpr (FAST) {
+            const char* xb0 = reinterpret_cast<const char*>(a.X + k0);
+#pragma unroll
+            for (int p = 0; p < XP; ++p) xv[p] = *reinterpret_cast<const f32x4*>(xb0 + xoff[p]);
+            return;
+        }
+#pragma unroll
+        for (int p = 0; p < XP; ++p) {
+            xv[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (xlive[p]) {
+                const float* x = reinterpret_cast<const float*>(xrow[p]);
+                const int64_t kb = k0 + xk;
+                if (VEC && kb + 4 <= a.k) {
+                    xv[p] = *reinterpret_cast<const f32x4*>(x + kb);
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) xv[p][q] = kb + q < a.k ? x[kb + q] : 0.f;
+                }
+            }
+        }
+    };
+    auto store_x = [&](const f32x4 (&xv)[XP], int stage) {
+#pragma unroll
+        for (int p = 0; p < XP; ++p) {
+            if (p * XRP >= (int)cnt) continue;  // no live row in this pass
+            const uint32_t h01 = cvt_pk_bf16(xv[p][0], xv[p][1]);
+            const uint32_t h23 = cvt_pk_bf16(xv[p][2], xv[p][3]);
+            const uint32_t l01 = cvt_pk_bf16(xv[p][0] - __uint_as_float(h01 << 16),
+                                             xv[p][1] - __uint_as_float(h01 & 0xffff0000u));
+            const uint32_t l23 = cvt_pk_bf16(xv[p][2] - __uint_as_float(h23 << 16),
+                                             xv[p][3] - __uint_as_float(h23 & 0xffff0000u));
+            const int o = (p * XRP + xr0) * QLDK + xk;
+            *reinterpret_cast<u32x2*>(&Xs[stage][0][o]) = u32x2{h01, h23};
+            *reinterpret_cast<u32x2*>(&Xs[stage][1][o]) = u32x2{l01, l23};
+        }
+    };
+    // Weight fragments: lane -> column wcol[j], k offset kk*32 + (lane/16)*8.
+    auto load_w = [&](int64_t k0, u32x4 (&w)[GF][2]) {
+#pragma unroll
+        for (int j = 0; j < GF; ++j) {
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 const int64_t kb = k0 + kk * 32 + (lane >> 4) * 8;
-                if (VEC && col < a.n && kb + 8 <= a.k) {
-                    w[nf][kk] = ld16_stream(We + col * a.k + kb);
+                if (FAST || (VEC && kb + 8 <= a.k)) {
+                    w[j][kk] = ld16_stream(We + wcol[j] * a.k + kb);
                 } else {
                     uint32_t h[8];
 #pragma unroll
-                    for (int q = 0; q < 8; ++q)
-                        h[q] = (col < a.n && kb + q < a.k) ? We[col * a.k + kb + q] : 0u;
-                    w[nf][kk] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16),
-                                      h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+                    for (int q = 0; q < 8; ++q) h[q] = kb + q < a.k ? We[wcol[j] * a.k + kb + q] : 0u;
+                    w[j][kk] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16),
+                                     h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
                 }
             }
         }
     };
 
-    u32x4 wcur[2][2];
-    load_w(0, wcur);
-    for (int64_t k0 = 0; k0 < a.k; k0 += QBK) {
-        // Stage the gathered activation rows for this K step as bf16 hi/lo.
-        __syncthreads();
+    f32x4 acc[8][GF];
 #pragma unroll
-        for (int pass = 0; pass < QBM / 16; ++pass) {
-            const int row = pass * 16 + (tid >> 4);
-            const int kc = (tid & 15) * 4;
-            float v[4] = {0.f, 0.f, 0.f, 0.f};
-            if ((uint32_t)row < cnt && s_rows[row] != 0xffffffffu) {
-                const float* x = reinterpret_cast<const float*>(reinterpret_cast<const char*>(a.X) + s_xoff[row]);
-                const int64_t kb = k0 + kc;
-                if (VEC && kb + 4 <= a.k) {
-                    unpack4(ld16(x + kb), v);
-                } else {
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) v[q] = kb + q < a.k ? x[kb + q] : 0.f;
-                }
-            }
-            uint16_t hi[4], lo[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                hi[q] = bf16_rne(v[q]);
-                lo[q] = bf16_rne(v[q] - __uint_as_float((uint32_t)hi[q] << 16));
-            }
-            *reinterpret_cast<u32x2*>(&Xhi[row * QLDK + kc]) =
-                u32x2{(uint32_t)hi[0] | ((uint32_t)hi[1] << 16), (uint32_t)hi[2] | ((uint32_t)hi[3] << 16)};
-            *reinterpret_cast<u32x2*>(&Xlo[row * QLDK + kc]) =
-                u32x2{(uint32_t)lo[0] | ((uint32_t)lo[1] << 16), (uint32_t)lo[2] | ((uint32_t)lo[3] << 16)};
-        }
-        __syncthreads();
-        u32x4 wnext[2][2];
-        if (k0 + QBK < a.k) load_w(k0 + QBK, wnext);
+        for (int j = 0; j < GF; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Register buffers rotate by name, never by copy: a copy would wait for
+    // loads that were just issued. W uses three buffers (two K steps ahead),
+    // X two (A/B alternate); the K loop is unrolled by 6 to close both cycles.
+    u32x4 w0[GF][2], w1[GF][2], w2[GF][2];
+    f32x4 xA[XP], xB[XP];
+    auto compute = [&](int64_t it, const u32x4 (&wc)[GF][2]) {
+        const int st = (int)(it & 1);
 #pragma unroll
         for (int mf = 0; mf < 8; ++mf) {
             if (mf < nmf) {
                 const int row = mf * 16 + (lane & 15);
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
-                    const int ko = kk * 32 + (lane >> 4) * 8;
-                    const u32x4 xh = *reinterpret_cast<const u32x4*>(&Xhi[row * QLDK + ko]);
-                    const u32x4 xl = *reinterpret_cast<const u32x4*>(&Xlo[row * QLDK + ko]);
+                    const int ko = row * QLDK + kk * 32 + (lane >> 4) * 8;
+                    const u32x4 xh = *reinterpret_cast<const u32x4*>(&Xs[st][0][ko]);
+                    const u32x4 xl = *reinterpret_cast<const u32x4*>(&Xs[st][1][ko]);
 #pragma unroll
-                    for (int nf = 0; nf < 2; ++nf) {
-                        // D[n][row] = sum_k W(n,k) X(row,k)
-                        acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8, wcur[nf][kk]), __builtin_bit_cast(bf16x8, xh),
-                            acc[mf][nf], 0, 0, 0);
-                        acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8, wcur[nf][kk]), __builtin_bit_cast(bf16x8, xl),
-                            acc[mf][nf], 0, 0, 0);
+                    for (int j = 0; j < GF; ++j) {
+                        if (j < nf_live) {
+                            acc[mf][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8, wc[j][kk]), __builtin_bit_cast(bf16x8, xh),
+                                acc[mf][j], 0, 0, 0);
+                            acc[mf][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8, wc[j][kk]), __builtin_bit_cast(bf16x8, xl),
+                                acc[mf][j], 0, 0, 0);
+                        }
                     }
                 }
             }
         }
-        if (k0 + QBK < a.k) {
-#pragma unroll
-            for (int nf = 0; nf < 2; ++nf)
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) wcur[nf][kk] = wnext[nf][kk];
-        }
+    };
+    // One K step: W(it+2) -> wf, MFMAs on W(it) = wc and stage it%2, X(it+1)
+    // (held in xbuf) -> stage (it+1)%2, then X(it+3) -> xbuf.
+    auto step = [&](int64_t it, const u32x4 (&wc)[GF][2], u32x4 (&wf)[GF][2], f32x4 (&xbuf)[XP]) {
+        if (it + 2 < nk) load_w((it + 2) * QBK, wf);
+        compute(it, wc);
+        if (it + 1 < nk) store_x(xbuf, (int)((it + 1) & 1));
+        if (it + 3 < nk) load_x((it + 3) * QBK, xbuf);
+        __syncthreads();
+    };
+
+    load_w(0, w0);
+    if (nk > 1) load_w(QBK, w1);
+    load_x(0, xA);
+    store_x(xA, 0);
+    if (nk > 1) load_x(QBK, xA);
+    if (nk > 2) load_x(2 * QBK, xB);
+    __syncthreads();
+    for (int64_t it = 0; it < nk; it += 6) {
+        step(it, w0, w2, xA);
+        if (it + 1 < nk) step(it + 1, w1, w0, xB);
+        if (it + 2 < nk) step(it + 2, w2, w1, xA);
+        if (it + 3 < nk) step(it + 3, w0, w2, xB);
+        if (it + 4 < nk) step(it + 4, w1, w0, xA);
+        if (it + 5 < nk) step(it + 5, w2, w1, xB);
     }
 
-    // Lane holds out[row = mf*16 + lane%16][n = n0 + nf*16 + 4*(lane/16) + q].
+    // Lane holds out[row = mf*16 + lane%16][n = frag column base + 4*(lane/16) + q].
 #pragma unroll
     for (int mf = 0; mf < 8; ++mf) {
         if (mf >= nmf) continue;
@@ -437,15 +656,16 @@ __global__ __launch_bounds__(kThreads) void id_grouped_bf16(IdArgs a) {
         if (r == 0xffffffffu) continue;
         float* dst_row = a.out + (uint64_t)r * a.n;
 #pragma unroll
-        for (int nf = 0; nf < 2; ++nf) {
-            const int64_t col = n0 + nf * 16 + 4 * (lane >> 4);
+        for (int j = 0; j < GF; ++j) {
+            if (j >= nf_live) continue;
+            const int64_t col = tile_n0 + (int64_t)(wave + GW * j) * 16 + 4 * (lane >> 4);
             float* dst = dst_row + col;
-            if (col + 4 <= a.n && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
-                *reinterpret_cast<f32x4*>(dst) = acc[mf][nf];
+            if (col + 4 <= tile_n1 && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+                *reinterpret_cast<f32x4*>(dst) = acc[mf][j];
             } else {
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    if (col + q < a.n) dst[q] = acc[mf][nf][q];
+                    if (col + q < tile_n1) dst[q] = acc[mf][j][q];
             }
         }
     }
@@ -553,14 +773,25 @@ inline uint64_t grid_for(const IdArgs& a, int bm, int bn) {
 
 hipError_t launch_id_direct(const IdArgs& a, hipStream_t s) {
     void* args[] = {const_cast<IdArgs*>(&a)};
+    const int64_t es = a.wdtype == 0 ? 4 : 2;
+    const int64_t ch = 16 / es;  // weights per 16-byte load
+    const bool aligned = a.expert_stride_bytes % 16 == 0 && aligned16(a.W) && aligned16(a.X) &&
+                         a.x_tok_stride_bytes % 16 == 0 && a.x_slot_stride_bytes % 16 == 0;
+    if (aligned && a.k % (ch * kWave * DU) == 0 && a.k <= kDirectMaxK) {
+        const int64_t per_block = kWaves * DR;
+        const int64_t work = (int64_t)a.m * a.top_k * ((a.n + per_block - 1) / per_block);
+        const unsigned grid = (unsigned)(work < (1ll << 30) ? work : (1ll << 30));
+        const bool one = a.k == ch * kWave * DU;
+#define MM_DF(T) (one ? (const void*)&id_direct_fast<T, true> : (const void*)&id_direct_fast<T, false>)
+        const void* fn = a.wdtype == 0 ? MM_DF(TF32) : a.wdtype == 1 ? MM_DF(TF16) : MM_DF(TBF16);
+#undef MM_DF
+        return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, (size_t)a.k * 4, s);
+    }
     constexpr int R = 2;
     const int64_t per_block = kWaves * R;
     const int64_t work = (int64_t)a.m * a.top_k * ((a.n + per_block - 1) / per_block);
     const unsigned grid = (unsigned)(work < (1ll << 30) ? work : (1ll << 30));
-    const int64_t es = a.wdtype == 0 ? 4 : 2;
-    const bool vec = a.k % 8 == 0 && a.expert_stride_bytes % 16 == 0 && aligned16(a.W) &&
-                     aligned16(a.X) && a.x_tok_stride_bytes % 16 == 0 &&
-                     a.x_slot_stride_bytes % 16 == 0 && (a.k * es) % 16 == 0;
+    const bool vec = a.k % 8 == 0 && aligned;
     const void* fn = nullptr;
     switch (a.wdtype) {
         case 0: fn = vec ? (const void*)&id_direct<TF32, R, true> : (const void*)&id_direct<TF32, R, false>; break;
@@ -573,21 +804,36 @@ hipError_t launch_id_direct(const IdArgs& a, hipStream_t s) {
 
 hipError_t launch_id_map(const IdArgs& a, hipStream_t s) {
     void* args[] = {const_cast<IdArgs*>(&a)};
-    const size_t lds = (size_t)kMapWaves * a.n_experts * sizeof(uint32_t);
-    return hipLaunchKernel(reinterpret_cast<const void*>(&id_map), dim3(1), dim3(kMapThreads), args,
-                           lds, s);
+    // 12 bytes of LDS per (wave, expert); keep the tables within 64 KiB.
+    int waves = (int)(65536 / (12ull * a.n_experts));
+    waves = waves < 1 ? 1 : (waves > kMapMaxWaves ? kMapMaxWaves : waves);
+    const size_t lds = (size_t)waves * a.n_experts * 12;
+    return hipLaunchKernel(reinterpret_cast<const void*>(&id_map), dim3(1), dim3(waves * kWave),
+                           args, lds, s);
 }
 
 hipError_t launch_id_grouped(const IdArgs& a, hipStream_t s) {
-    void* args[] = {const_cast<IdArgs*>(&a)};
     if (a.wdtype == 2) {
+        // Output tile width: as few tiles as cover n at GMAXBN each, raised until
+        // experts x tiles reaches the CU count (every CU streams one W slab).
+        const uint32_t frags = (a.n + 15) / 16;
+        uint32_t split = (a.n + GMAXBN - 1) / GMAXBN;
+        const uint32_t want = (256 + a.n_experts - 1) / a.n_experts;
+        if (split < want) split = want < frags ? want : frags;
+        uint32_t bn = ((frags + split - 1) / split) * 16;
+        void* args[] = {const_cast<IdArgs*>(&a), &bn};
         const bool vec = a.k % 8 == 0 && a.expert_stride_bytes % 16 == 0 && aligned16(a.W) &&
                          aligned16(a.X) && a.x_tok_stride_bytes % 16 == 0 &&
                          a.x_slot_stride_bytes % 16 == 0;
-        const uint64_t g = grid_for(a, QBM, QBN);
-        const void* fn = vec ? (const void*)&id_grouped_bf16<true> : (const void*)&id_grouped_bf16<false>;
-        return hipLaunchKernel(fn, dim3((unsigned)g), dim3(kThreads), args, 0, s);
+        const uint64_t in_rows = a.layout == 0 ? a.m : (uint64_t)a.m * a.top_k;
+        const bool fast = vec && a.k % QBK == 0 && in_rows * a.k * 4 < (1ull << 32);
+        const uint64_t g = grid_for(a, QBM, bn);
+        const void* fn = fast ? (const void*)&id_grouped_bf16<true, true>
+                       : vec  ? (const void*)&id_grouped_bf16<true, false>
+                              : (const void*)&id_grouped_bf16<false, false>;
+        return hipLaunchKernel(fn, dim3((unsigned)g), dim3(GW * kWave), args, 0, s);
     }
+    void* args[] = {const_cast<IdArgs*>(&a)};
     const uint64_t g = grid_for(a, FBM, FBN);
     const void* fn = a.wdtype == 0 ? (const void*)&id_grouped_fma<TF32> : (const void*)&id_grouped_fma<TF16>;
     return hipLaunchKernel(fn, dim3((unsigned)g), dim3(kThreads), args, 0, s);

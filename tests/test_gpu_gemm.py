@@ -196,3 +196,55 @@ def test_large_k_many_tiles_f16():
     _say("f16 NT m=300 n=520 k=4100")
     case = wl.random_gemm_case(31, wl.F16, 1, 300, 520, 4100, False, True)
     check_gemm(case, what="large k")
+
+
+def _sampled_check(case, n_samples, seed, exact=False):
+    from gpu_util import GemmRun, assert_close
+    import oracle
+    run = GemmRun(case)
+    run.run()
+    bits = run.c_bits()
+    rng = np.random.default_rng(seed)
+    bs = rng.integers(0, case.batch, n_samples)
+    is_ = np.concatenate([rng.integers(0, case.m, n_samples), [0, case.m - 1]])
+    js = np.concatenate([rng.integers(0, case.n, n_samples), [case.n - 1, 0]])
+    bs = np.concatenate([bs, [0, case.batch - 1]])
+    ref = oracle.gemm_at(case.dtype, case.k, case.trans_a, case.trans_b, case.lda, case.ldb,
+                         case.stride_a, case.stride_b, case.off_a, case.off_b, case.A, case.B,
+                         bs, is_, js)
+    idx = case.off_c // wl.ELT[case.dtype] + bs * case.stride_c + is_ * case.ldc + js
+    got = oracle.decode(case.dtype, bits[idx])
+    if exact:
+        np.testing.assert_array_equal(got, oracle.decode(case.dtype, oracle.round_to(case.dtype, ref)))
+    else:
+        amax, bmax = run.operand_absmax()
+        assert_close(got, ref, case.dtype, case.k, amax, bmax, "sampled")
+    vals, _ = run.logical_c(bits)
+    assert np.all(np.isfinite(vals)), "an output element was not written"
+
+
+@pytest.mark.parametrize("dt", [wl.F16, wl.BF16])
+def test_large_tile_route(dt):
+    """m, n multiples of 256 with >= 512 tiles: the 256 x 256 MFMA kernel."""
+    _say(f"large-tile NT dt={wl.DTYPE_NAMES[dt]} m=4096 n=8192 k=192")
+    case = wl.random_gemm_case(41, dt, 1, 4096, 8192, 192, False, True)
+    _sampled_check(case, 4096, 3)
+
+
+def test_large_tile_route_ramp_exact():
+    _say("large-tile NT ramp exact m=8192 n=4096 k=320")
+    m, n, k = 8192, 4096, 320
+    a = wl.ramp(m * k, 1).reshape(1, m, k)
+    b = wl.ramp(n * k, 2).reshape(1, n, k)
+    case = wl.make_gemm_case(wl.F16, a, b, False, True)
+    _sampled_check(case, 4096, 4, exact=True)
+
+
+def test_large_tile_route_batched_padded():
+    _say("large-tile NT batched, padded ld, bf16 m=2048 n=2048 k=128 batch 2")
+    rng = np.random.default_rng(9)
+    b_, m, n, k = 2, 2048, 4096, 128
+    a = rng.standard_normal((b_, m, k))
+    bb = rng.standard_normal((b_, n, k)) / np.sqrt(k)
+    case = wl.make_gemm_case(wl.BF16, a, bb, False, True, lda=k + 64, ldb=k + 8, ldc=n + 4)
+    _sampled_check(case, 4096, 5)
