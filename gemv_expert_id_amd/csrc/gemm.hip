@@ -138,13 +138,13 @@ __global__ __launch_bounds__(GThreads) void gemm_mfma_generic(GemmArgs a) {
 
 // ---------------------------------------------------------------------------
 // Large f16 / bf16 kernel: C = A . B^T with A [m,k] and B [n,k] both
-// K-contiguous, m % 256 == n % 256 == 0, k % 64 == 0, 16-byte aligned.
+// K-contiguous, m % 256 == n % 256 == 0, k % 128 == 0, 16-byte aligned.
 //
-// Block = 4 waves (2 x 2), tile 256 x 256 x 64, each wave 128 x 128 with
-// v_mfma_f32_32x32x16 (16 accumulators of 16 f32 each). Per K step every
-// thread pulls 8 + 8 16-byte chunks of the next A/B tiles into registers
-// while the MFMAs run on the current LDS stage, then writes them to the
-// other stage (double-buffered, 2 x 64 KiB). In LDS a tile row is 64 halves
+// Block = 8 waves (2 x 4, two per SIMD), tile 256 x 256 x 64, each wave
+// 128 x 64 with v_mfma_f32_32x32x16 (8 accumulators of 16 f32 each). Every
+// thread moves 4 + 4 16-byte chunks per tile: tile kt+2 is fetched into registers (buffer
+// loads) while the MFMAs run on tile kt in one LDS stage and tile kt+1 is
+// written into the other stage (double-buffered, 2 x 64 KiB). In LDS a tile row is 64 halves
 // = 8 chunks of 16 bytes and chunk c of row r sits at slot c ^ (r & 7), so
 // the fragment reads of 32 consecutive rows spread over all banks.
 // Tile order: tiles are cut into groups of 8 tile-rows (column-major inside
@@ -152,8 +152,11 @@ __global__ __launch_bounds__(GThreads) void gemm_mfma_generic(GemmArgs a) {
 // resident on one XCD share A and B panels in its L2.
 // ---------------------------------------------------------------------------
 constexpr int LBM = 256, LBN = 256, LBK = 64;
-constexpr int LThreads = 256;
-constexpr int LTILE = LBM * LBK;  // halves per operand stage
+constexpr int LWM = 2, LWN = 4;              // wave grid: 2 x 4 waves of 128 x 64
+constexpr int LThreads = LWM * LWN * 64;
+constexpr int LTILE = LBM * LBK;             // halves per operand stage
+constexpr int LROWS = LThreads / 8;          // tile rows staged per pass (8 chunks/row)
+constexpr int LPASS = LBM / LROWS;           // staging passes per operand
 
 template <class T>
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
@@ -169,7 +172,7 @@ template <class T>
 __global__ __launch_bounds__(LThreads, 1) void gemm_mfma_large(GemmArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];  // [2][A | B]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / LWN, wn = wave % LWN;
     const int64_t tiles_m = a.m / LBM, tiles_n = a.n / LBN;
     const int64_t ntiles = tiles_m * tiles_n;
 
@@ -190,7 +193,7 @@ __global__ __launch_bounds__(LThreads, 1) void gemm_mfma_large(GemmArgs a) {
         const uint16_t* A = reinterpret_cast<const uint16_t*>(a.A) + b * a.sa + m0 * a.lda;
         const uint16_t* B = reinterpret_cast<const uint16_t*>(a.B) + b * a.sb + n0 * a.ldb;
 
-        // Staging: thread covers chunk (tid & 7) of rows (tid >> 3) + 32 * i.
+        // Staging: thread covers chunk (tid & 7) of rows (tid >> 3) + LROWS * i.
         // Buffer loads: the tile base is a scalar resource, each lane adds one
         // 32-bit offset and the row step rides in the scalar offset.
         const int srow = tid >> 3, schunk = tid & 7;
@@ -200,65 +203,89 @@ __global__ __launch_bounds__(LThreads, 1) void gemm_mfma_large(GemmArgs a) {
             const_cast<uint16_t*>(B), (short)0, (int)(LBN * a.ldb * 2), 0x00020000);
         const int voa = (srow * (int)a.lda + schunk * 8) * 2;
         const int vob = (srow * (int)a.ldb + schunk * 8) * 2;
-        u32x4 ra[8], rb[8];
-        auto gload = [&](int64_t k0) {
+        // Two register staging sets (R0, R1): tile kt+2 is loaded while tile kt
+        // is multiplied and tile kt+1 waits in registers for its LDS stage. The
+        // sets alternate by name in a loop unrolled by two (never copied).
+        u32x4 ra0[LPASS], rb0[LPASS], ra1[LPASS], rb1[LPASS];
+        auto gload = [&](int64_t kt, u32x4 (&ra)[LPASS], u32x4 (&rb)[LPASS]) {
+            const int64_t k0 = kt * LBK;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < LPASS; ++i) {
                 ra[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                            rsa, voa, (int)((32 * i * a.lda + k0) * 2), 0));
+                            rsa, voa, (int)((LROWS * i * a.lda + k0) * 2), 0));
                 rb[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                            rsb, vob, (int)((32 * i * a.ldb + k0) * 2), 0));
+                            rsb, vob, (int)((LROWS * i * a.ldb + k0) * 2), 0));
             }
         };
-        // srow & 7 is the same for every i, so one lane offset plus immediates.
+        // srow & 7 is the same for every pass, so one lane offset plus immediates.
         const int sto = srow * LBK + ((schunk ^ (srow & 7)) << 3);
-        auto sstore = [&](int stage) {
+        auto sstore = [&](int stage, const u32x4 (&ra)[LPASS], const u32x4 (&rb)[LPASS]) {
             uint16_t* sa = lds + stage * 2 * LTILE + sto;
             uint16_t* sb = sa + LTILE;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                *reinterpret_cast<u32x4*>(sa + 32 * i * LBK) = ra[i];
-                *reinterpret_cast<u32x4*>(sb + 32 * i * LBK) = rb[i];
+            for (int i = 0; i < LPASS; ++i) {
+                *reinterpret_cast<u32x4*>(sa + LROWS * i * LBK) = ra[i];
+                *reinterpret_cast<u32x4*>(sb + LROWS * i * LBK) = rb[i];
             }
         };
         const int lrow = lane & 31, lhi = lane >> 5, lx = lane & 7;
 
-        f32x16 acc[4][4];
+        f32x16 acc[4][2];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-        const int64_t nk = a.k / LBK;
-        gload(0);
-        sstore(0);
-        __syncthreads();
-        for (int64_t kt = 0; kt < nk; ++kt) {
-            if (kt + 1 < nk) gload((kt + 1) * LBK);
-            const uint16_t* sa = lds + (kt & 1) * 2 * LTILE;
+        // Wave tile: rows wm*128 + [0,128) of A, rows wn*64 + [0,64) of B.
+        auto compute = [&](int stage) {
+            const uint16_t* sa = lds + stage * 2 * LTILE;
             const uint16_t* sb = sa + LTILE;
 #pragma unroll
             for (int ks = 0; ks < LBK / 16; ++ks) {
                 // Fragment: lane -> row (lane % 32), chunk 2*ks + lane / 32.
                 const int co = (((2 * ks + lhi) ^ lx) << 3) + lrow * LBK;
-                u32x4 fa[4], fb[4];
+                u32x4 fa[4], fb[2];
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     fa[i] = *reinterpret_cast<const u32x4*>(sa + (wm * 128 + i * 32) * LBK + co);
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    fb[j] = *reinterpret_cast<const u32x4*>(sb + (wn * 128 + j * 32) * LBK + co);
+                for (int j = 0; j < 2; ++j)
+                    fb[j] = *reinterpret_cast<const u32x4*>(sb + (wn * 64 + j * 32) * LBK + co);
                 // D[n][m] = sum_k B(n,k) A(m,k)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) acc[i][j] = mfma32<T>(fb[j], fa[i], acc[i][j]);
+                    for (int j = 0; j < 2; ++j) acc[i][j] = mfma32<T>(fb[j], fa[i], acc[i][j]);
             }
-            if (kt + 1 < nk) sstore((kt + 1) & 1);
+        };
+
+        // sched_barrier keeps each prefetch issued before the MFMAs it overlaps
+        // (left to itself the scheduler sinks the loads next to their use).
+        const int64_t nk = a.k / LBK;  // even and >= 2 on this path
+        gload(0, ra0, rb0);
+        gload(1, ra1, rb1);
+        sstore(0, ra0, rb0);
+        __syncthreads();
+        for (int64_t kt = 0; kt + 2 < nk; kt += 2) {
+            gload(kt + 2, ra0, rb0);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(0);
+            __builtin_amdgcn_sched_barrier(0);
+            sstore(1, ra1, rb1);
+            __syncthreads();
+            gload(kt + 3, ra1, rb1);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(1);
+            __builtin_amdgcn_sched_barrier(0);
+            sstore(0, ra0, rb0);
             __syncthreads();
         }
+        compute(0);
+        sstore(1, ra1, rb1);
+        __syncthreads();
+        compute(1);
 
         // Lane holds C[m = mfrag base + lane%32][n = nfrag base + (v/4)*8 + (lane/32)*4 + v%4].
         uint16_t* C = reinterpret_cast<uint16_t*>(a.C) + b * a.sc;
@@ -266,10 +293,10 @@ __global__ __launch_bounds__(LThreads, 1) void gemm_mfma_large(GemmArgs a) {
         for (int i = 0; i < 4; ++i) {
             const int64_t gm = m0 + wm * 128 + i * 32 + (lane & 31);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < 2; ++j) {
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    const int64_t gn = n0 + wn * 128 + j * 32 + g * 8 + (lane >> 5) * 4;
+                    const int64_t gn = n0 + wn * 64 + j * 32 + g * 8 + (lane >> 5) * 4;
                     u32x2 v;
                     v[0] = (uint32_t)narrow(T{}, acc[i][j][4 * g]) | ((uint32_t)narrow(T{}, acc[i][j][4 * g + 1]) << 16);
                     v[1] = (uint32_t)narrow(T{}, acc[i][j][4 * g + 2]) | ((uint32_t)narrow(T{}, acc[i][j][4 * g + 3]) << 16);
@@ -377,7 +404,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     const bool vec = aligned16(a.A) && aligned16(a.B) && a.lda % 8 == 0 && a.ldb % 8 == 0 &&
                      a.sa % 8 == 0 && a.sb % 8 == 0;
     const int64_t big_tiles = (a.m / LBM) * (a.n / LBN);
-    if (vec && !a.ta && a.tb && a.m % LBM == 0 && a.n % LBN == 0 && a.k % LBK == 0 &&
+    if (vec && !a.ta && a.tb && a.m % LBM == 0 && a.n % LBN == 0 && a.k % (2 * LBK) == 0 &&
         big_tiles >= 512 && a.ldc % 4 == 0 && (reinterpret_cast<uintptr_t>(a.C) & 7) == 0 &&
         a.sc % 4 == 0) {
         // Large NT products: 256 x 256 tiles (enough of them to fill the chip).
