@@ -62,9 +62,10 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash():
+def kernel_source_hash(files):
+    """Hash of the kernel sources the stored counters were taken with."""
     h = hashlib.sha256()
-    for f in sorted(os.listdir(os.path.join(ROOT, "gemv_expert_id_amd", "csrc"))):
+    for f in files:
         with open(os.path.join(ROOT, "gemv_expert_id_amd", "csrc", f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -306,7 +307,8 @@ def main():
         with open(PROFILE_TRAFFIC) as f:
             prof = json.load(f)
         ent = prof.get("gemv_f16_decode")
-        if ent and ent.get("kernel_source_hash") == kernel_source_hash():
+        # Counters are only valid for the kernel they were taken on.
+        if ent and ent.get("kernel_source_hash") == kernel_source_hash(ent["kernel_sources"]):
             traffic = ent.get("hbm_bytes_per_launch")
     line = {
         "metric": METRIC,
