@@ -141,23 +141,23 @@ __global__ __launch_bounds__(kThreads) void id_direct(IdArgs a) {
     }
 }
 
-// Direct route, fast form: k % (Elems16 * 64 * DU) == 0, k <= kDirectMaxK,
-// aligned operands. Block = (routed row r, 4 * DR output rows). Each wave
-// issues the non-temporal 16-byte loads of its DR weight rows first, then the
-// block stages the f32 activation row in LDS once (instead of every wave
-// pulling it from L2), and the next group of weight chunks is in flight
-// while the current one is reduced.
-constexpr int kDirectMaxK = 8192;
-constexpr int DR = 2, DU = 4;
+// Direct route, fast form: k % (Elems16 * 64 * DU) == 0, top_k <= 64,
+// aligned operands. Block = (routed row r, 4 * DR output rows),
+// one wave per DR rows, no barrier. The token's whole id row arrives in one
+// vector load (lane i holds slot i), so the expert, "an earlier slot owns it"
+// and "later slots repeat it" are a lane read and two ballots: one memory
+// round trip before the weight loads are issued. The activation chunks come
+// straight from L2 next to the weight chunks they multiply; the next group of
+// weight chunks is in flight while the current one is reduced.
+constexpr int DR = 2;  // weight rows per wave
+constexpr int DU = 4;  // 16-byte chunks per lane per row in flight
 
-// ONE: the whole row is one group of DU chunks per lane (no second buffer).
 template <class T, bool ONE>
 __global__ __launch_bounds__(kThreads) void id_direct_fast(IdArgs a) {
     using S = typename T::store_t;
     constexpr int CH = T::Elems16;
     constexpr int G = kWave * DU;  // chunks per group
-    extern __shared__ __attribute__((aligned(16))) float xs[];  // k floats
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int64_t per_block = (int64_t)kWaves * DR;
     const int64_t nchunks = (a.n + per_block - 1) / per_block;
     const int64_t rows = (int64_t)a.m * a.top_k;
@@ -165,19 +165,18 @@ __global__ __launch_bounds__(kThreads) void id_direct_fast(IdArgs a) {
     for (int64_t work = blockIdx.x; work < rows * nchunks; work += gridDim.x) {
         const int64_t r = work / nchunks;
         const int64_t j0 = (work % nchunks) * per_block + (int64_t)wave * DR;
-        const uint32_t e = a.ids[r];
-        const int64_t t = r / a.top_k, s = r % a.top_k;
+        const int64_t t = r / a.top_k;
+        const int s = (int)(r % a.top_k);
+        const uint32_t v = lane < a.top_k ? a.ids[t * a.top_k + lane] : 0xffffffffu;
+        const uint32_t e = __builtin_amdgcn_readlane(v, s);
         float* out_r = a.out + r * a.n;
         if (e >= a.n_experts) {  // no weight address is formed
             if (lane < DR && j0 + lane < a.n) out_r[j0 + lane] = 0.f;
-            continue;            // uniform across the block
+            continue;
         }
-        const uint32_t* tok_ids = a.ids + t * a.top_k;
-        if (a.dedup) {
-            bool owned = false;
-            for (int64_t s2 = 0; s2 < s; ++s2) owned |= tok_ids[s2] == e;
-            if (owned) continue;  // uniform across the block
-        }
+        // Slots of this token naming expert e (only the shared layout merges them).
+        const uint64_t same = a.dedup ? (uint64_t)__ballot(v == e) : (1ull << s);
+        if (same & ((1ull << s) - 1)) continue;  // an earlier slot owns this expert
         const S* We = reinterpret_cast<const S*>(reinterpret_cast<const char*>(a.W) +
                                                  (uint64_t)e * a.expert_stride_bytes);
         const S* rowp[DR];
@@ -194,10 +193,6 @@ __global__ __launch_bounds__(kThreads) void id_direct_fast(IdArgs a) {
         const float* x = reinterpret_cast<const float*>(reinterpret_cast<const char*>(a.X) +
                                                         t * a.x_tok_stride_bytes +
                                                         s * a.x_slot_stride_bytes);
-        __syncthreads();  // the previous work item's readers are done with xs
-        for (int64_t i = tid; i < a.k / 4; i += kThreads)
-            *reinterpret_cast<f32x4*>(&xs[i * 4]) = *reinterpret_cast<const f32x4*>(x + i * 4);
-        __syncthreads();
         float acc[DR];
 #pragma unroll
         for (int q = 0; q < DR; ++q) acc[q] = 0.f;
@@ -211,12 +206,16 @@ __global__ __launch_bounds__(kThreads) void id_direct_fast(IdArgs a) {
                     for (int u = 0; u < DU; ++u)
                         nv[q][u] = ld16_stream(rowp[q] + ((g + 1) * G + lane + kWave * u) * CH);
             }
+            u32x4 xv[DU][CH / 4];
+#pragma unroll
+            for (int u = 0; u < DU; ++u)
+#pragma unroll
+                for (int h = 0; h < CH / 4; ++h) xv[u][h] = ld16(x + (g * G + lane + kWave * u) * CH + 4 * h);
 #pragma unroll
             for (int u = 0; u < DU; ++u) {
-                const float* xc = &xs[(g * G + lane + kWave * u) * CH];
                 float xf[CH];
 #pragma unroll
-                for (int h = 0; h < CH / 4; ++h) unpack4(*reinterpret_cast<const u32x4*>(xc + 4 * h), &xf[4 * h]);
+                for (int h = 0; h < CH / 4; ++h) unpack4(xv[u][h], &xf[4 * h]);
 #pragma unroll
                 for (int q = 0; q < DR; ++q) {
                     float wf[CH];
@@ -234,13 +233,15 @@ __global__ __launch_bounds__(kThreads) void id_direct_fast(IdArgs a) {
         }
 #pragma unroll
         for (int q = 0; q < DR; ++q) acc[q] = wave_sum(acc[q]);
+        const uint64_t later = same & ~((2ull << s) - 1);  // s < 64
 #pragma unroll
         for (int q = 0; q < DR; ++q) {
             if (lane == q && j0 + q < a.n) {
                 out_r[j0 + q] = acc[q];
-                if (a.dedup)
-                    for (int64_t s3 = s + 1; s3 < a.top_k; ++s3)
-                        if (tok_ids[s3] == e) a.out[(t * a.top_k + s3) * a.n + j0 + q] = acc[q];
+                for (uint64_t mk = later; mk; mk &= mk - 1) {
+                    const int64_t s3 = __builtin_ctzll(mk);
+                    a.out[(t * a.top_k + s3) * a.n + j0 + q] = acc[q];
+                }
             }
         }
     }
@@ -777,7 +778,7 @@ hipError_t launch_id_direct(const IdArgs& a, hipStream_t s) {
     const int64_t ch = 16 / es;  // weights per 16-byte load
     const bool aligned = a.expert_stride_bytes % 16 == 0 && aligned16(a.W) && aligned16(a.X) &&
                          a.x_tok_stride_bytes % 16 == 0 && a.x_slot_stride_bytes % 16 == 0;
-    if (aligned && a.k % (ch * kWave * DU) == 0 && a.k <= kDirectMaxK) {
+    if (aligned && a.k % (ch * kWave * DU) == 0 && a.top_k <= kWave) {
         const int64_t per_block = kWaves * DR;
         const int64_t work = (int64_t)a.m * a.top_k * ((a.n + per_block - 1) / per_block);
         const unsigned grid = (unsigned)(work < (1ll << 30) ? work : (1ll << 30));
@@ -785,7 +786,7 @@ hipError_t launch_id_direct(const IdArgs& a, hipStream_t s) {
 #define MM_DF(T) (one ? (const void*)&id_direct_fast<T, true> : (const void*)&id_direct_fast<T, false>)
         const void* fn = a.wdtype == 0 ? MM_DF(TF32) : a.wdtype == 1 ? MM_DF(TF16) : MM_DF(TBF16);
 #undef MM_DF
-        return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, (size_t)a.k * 4, s);
+        return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
     }
     constexpr int R = 2;
     const int64_t per_block = kWaves * R;

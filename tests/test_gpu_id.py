@@ -59,7 +59,13 @@ def _with_bad_ids(case: wl.IdCase):
 @pytest.mark.parametrize("wdt", DTYPES)
 @pytest.mark.parametrize("layout", [0, 1])
 @pytest.mark.parametrize("shape", [(9, 7, 35, 2, 4), (5, 130, 260, 3, 6), (3, 1408, 2048, 8, 64),
-                                   (17, 33, 64, 4, 9)])
+                                   (17, 33, 64, 4, 9),
+                                   # many repeats per token on the one-group fast form
+                                   (3, 40, 2048, 16, 4),
+                                   # several K groups, and K past 8192
+                                   (2, 24, 4096, 3, 5), (1, 8, 12288, 2, 3),
+                                   # top_k above the wave width: element-loop form
+                                   (2, 70, 2048, 70, 8)])
 def test_direct(wdt, layout, shape):
     m, n, k, top_k, E = shape
     _say(f"direct wdt={wl.DTYPE_NAMES[wdt]} layout={layout} shape={shape}")
