@@ -110,12 +110,13 @@ mm_status finish(hipError_t err, hipStream_t s, const char* what) {
     return MM_OK;
 }
 
-void set_receipt(mm_receipt* r, uint32_t route, uint32_t dtype, uint32_t n) {
+void set_receipt(mm_receipt* r, uint32_t route, uint32_t dtype, uint32_t n, int kernel) {
     if (!r) return;
     r->schema_version = MM_ID_SCHEMA_VERSION;
     r->route = route;
     r->dtype = dtype;
     r->dispatch_count = n;
+    r->kernel = (uint32_t)kernel;
 }
 
 // ---------------------------------------------------------------------------
@@ -244,9 +245,10 @@ mm_status run_gemv(const GemmPlan& p, hipStream_t s, mm_receipt* r) {
     mm_status st = resolve("gemv");
     if (st != MM_OK) return st;
     ++g_launches;
-    st = finish(mmk::launch_gemv(gemv_args(p), s), s, "gemv");
+    int kernel = -1;
+    st = finish(mmk::launch_gemv(gemv_args(p), s, &kernel), s, "gemv");
     if (st != MM_OK) return st;
-    set_receipt(r, MM_ROUTE_GEMV, (uint32_t)p.dt, 1);
+    set_receipt(r, MM_ROUTE_GEMV, (uint32_t)p.dt, 1, kernel);
     return ok();
 }
 
@@ -256,9 +258,10 @@ mm_status run_gemm(const GemmPlan& p, hipStream_t s, mm_receipt* r) {
     mmk::GemmArgs g{p.a, p.b, p.c, p.m, p.n, p.k, p.lda, p.ldb, p.ldc, p.sa, p.sb, p.sc,
                     p.batch, p.dt, p.ta, p.tb};
     ++g_launches;
-    st = finish(mmk::launch_gemm(g, s), s, "gemm");
+    int kernel = -1;
+    st = finish(mmk::launch_gemm(g, s, &kernel), s, "gemm");
     if (st != MM_OK) return st;
-    set_receipt(r, MM_ROUTE_GEMM, (uint32_t)p.dt, 1);
+    set_receipt(r, MM_ROUTE_GEMM, (uint32_t)p.dt, 1, kernel);
     return ok();
 }
 
@@ -455,8 +458,9 @@ mm_status mm_id_direct(const mm_id_params* params, mm_dtype weight_dtype, mm_buf
     mmk::IdArgs a = fill_ptrs(id_args(params, weight_dtype), weights, input, ids, out,
                               mm_buf{nullptr, 0}, mm_buf{nullptr, 0});
     ++g_launches;
-    if ((st = finish(mmk::launch_id_direct(a, s), s, "id_direct")) != MM_OK) return st;
-    set_receipt(receipt, MM_ROUTE_ID_DIRECT, (uint32_t)weight_dtype, 1);
+    int kernel = -1;
+    if ((st = finish(mmk::launch_id_direct(a, s, &kernel), s, "id_direct")) != MM_OK) return st;
+    set_receipt(receipt, MM_ROUTE_ID_DIRECT, (uint32_t)weight_dtype, 1, kernel);
     return ok();
 }
 
@@ -472,8 +476,9 @@ mm_status mm_id_map(const mm_id_params* params, mm_buf ids, mm_buf counts, mm_bu
     mmk::IdArgs a = fill_ptrs(id_args(params, MM_F32), mm_buf{nullptr, 0}, mm_buf{nullptr, 0}, ids,
                               out, counts, routed_rows);
     ++g_launches;
-    if ((st = finish(mmk::launch_id_map(a, s), s, "id_map")) != MM_OK) return st;
-    set_receipt(receipt, MM_ROUTE_ID_MAP, (uint32_t)MM_F32, 1);
+    int kernel = -1;
+    if ((st = finish(mmk::launch_id_map(a, s, &kernel), s, "id_map")) != MM_OK) return st;
+    set_receipt(receipt, MM_ROUTE_ID_MAP, (uint32_t)MM_F32, 1, kernel);
     return ok();
 }
 
@@ -489,8 +494,9 @@ mm_status mm_id_grouped(const mm_id_params* params, mm_dtype weight_dtype, mm_bu
     mmk::IdArgs a = fill_ptrs(id_args(params, weight_dtype), weights, input, mm_buf{nullptr, 0},
                               out, counts, routed_rows);
     ++g_launches;
-    if ((st = finish(mmk::launch_id_grouped(a, s), s, "id_grouped")) != MM_OK) return st;
-    set_receipt(receipt, MM_ROUTE_ID_GROUPED, (uint32_t)weight_dtype, 1);
+    int kernel = -1;
+    if ((st = finish(mmk::launch_id_grouped(a, s, &kernel), s, "id_grouped")) != MM_OK) return st;
+    set_receipt(receipt, MM_ROUTE_ID_GROUPED, (uint32_t)weight_dtype, 1, kernel);
     return ok();
 }
 
@@ -509,11 +515,12 @@ mm_status mm_id(const mm_id_params* params, mm_dtype weight_dtype, mm_buf weight
     hipStream_t s = static_cast<hipStream_t>(stream);
     mmk::IdArgs a = fill_ptrs(id_args(params, weight_dtype), weights, input, ids, out, counts,
                               routed_rows);
+    int kernel = -1;
     ++g_launches;
-    if ((st = finish(mmk::launch_id_map(a, s), s, "id_map")) != MM_OK) return st;
+    if ((st = finish(mmk::launch_id_map(a, s, &kernel), s, "id_map")) != MM_OK) return st;
     ++g_launches;
-    if ((st = finish(mmk::launch_id_grouped(a, s), s, "id_grouped")) != MM_OK) return st;
-    set_receipt(receipt, MM_ROUTE_ID_PREFILL, (uint32_t)weight_dtype, 2);
+    if ((st = finish(mmk::launch_id_grouped(a, s, &kernel), s, "id_grouped")) != MM_OK) return st;
+    set_receipt(receipt, MM_ROUTE_ID_PREFILL, (uint32_t)weight_dtype, 2, kernel);
     return ok();
 }
 

@@ -7,6 +7,9 @@
 // tiles staged through LDS in a K-contiguous [row][k] layout; operands stored
 // with K strided are transposed while being written to LDS. f32: LDS-tiled
 // FMA. Edges in M, N and K are zero-filled on load and masked on store.
+#include <type_traits>
+#include <utility>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -138,25 +141,54 @@ __global__ __launch_bounds__(GThreads) void gemm_mfma_generic(GemmArgs a) {
 
 // ---------------------------------------------------------------------------
 // Large f16 / bf16 kernel: C = A . B^T with A [m,k] and B [n,k] both
-// K-contiguous, m % 256 == n % 256 == 0, k % 128 == 0, 16-byte aligned.
+// K-contiguous, m % 256 == n % 256 == 0, k % 128 == 0, k >= 256, 16-byte aligned.
 //
-// Block = 8 waves (2 x 4, two per SIMD), tile 256 x 256 x 64, each wave
-// 128 x 64 with v_mfma_f32_32x32x16 (8 accumulators of 16 f32 each). Every
-// thread moves 4 + 4 16-byte chunks per tile: tile kt+2 is fetched into registers (buffer
-// loads) while the MFMAs run on tile kt in one LDS stage and tile kt+1 is
-// written into the other stage (double-buffered, 2 x 64 KiB). In LDS a tile row is 64 halves
-// = 8 chunks of 16 bytes and chunk c of row r sits at slot c ^ (r & 7), so
-// the fragment reads of 32 consecutive rows spread over all banks.
-// Tile order: tiles are cut into groups of 8 tile-rows (column-major inside
-// a group) and each XCD takes a contiguous run of that order, so the blocks
-// resident on one XCD share A and B panels in its L2.
+// Block = 4 waves (one per SIMD), tile 256 x 256, each wave 128 x 128 with
+// v_mfma_f32_32x32x16 (16 accumulators of 16 f32, held in AGPRs). A 128 x 128
+// wave tile halves the LDS fragment reads per MFMA compared with 128 x 64.
+//
+// Operands go from global memory straight into LDS (buffer_load ... lds, no
+// VGPR staging) in k-tiles of 32: four LDS stages of 32 KiB (A 16 KiB, B 16 KiB).
+// One DMA instruction fills 1 KiB = 16 tile rows x 64 bytes; lane i fetches
+// the global chunk that belongs at LDS slot i, so the XOR swizzle (chunk c of
+// row r at slot c ^ ((r >> 2) & 3)) costs nothing on the write side and the
+// fragment reads of 8 or 16 consecutive rows hit distinct banks.
+//
+// Per k-tile kt (stage kt % 4), each wave runs two groups of 16 MFMAs (k 0-15
+// and 16-31). Fragments for the next group are read from LDS while the
+// current group runs. Between the two groups sits the only barrier of the
+// k-tile: after it tile kt+1 is resident and stage kt % 4 is free, so the DMA
+// of tile kt+4 into it starts there. Its eight instructions are spread one
+// per four MFMAs over the next two groups (a burst would fill the address
+// queue and stall MFMA issue behind it); tile kt+4 is needed three barriers
+// later. Loops are unrolled by the stage count so every LDS offset, stage and
+// wait count is a compile-time constant.
+//
+// Tile order: groups of 4 tile-rows, column-major inside a group, each XCD
+// (blockIdx % 8) taking a contiguous run, so resident blocks on one XCD share
+// A and B panels in its L2.
 // ---------------------------------------------------------------------------
-constexpr int LBM = 256, LBN = 256, LBK = 64;
-constexpr int LWM = 2, LWN = 4;              // wave grid: 2 x 4 waves of 128 x 64
-constexpr int LThreads = LWM * LWN * 64;
-constexpr int LTILE = LBM * LBK;             // halves per operand stage
-constexpr int LROWS = LThreads / 8;          // tile rows staged per pass (8 chunks/row)
-constexpr int LPASS = LBM / LROWS;           // staging passes per operand
+constexpr int LBM = 256, LBN = 256, LBK = 32, LSTAGES = 4;
+constexpr int LThreads = 256;
+constexpr int LSTAGE_H = (LBM + LBN) * LBK;   // halves per stage
+constexpr int LCPR = LBK / 8;                  // 16-byte chunks per tile row
+constexpr int LRPI = 64 / LCPR;                // tile rows per 1 KiB DMA instruction
+constexpr int LIPW = 64 / LRPI;                // DMA instructions per wave per operand per tile
+constexpr int LLPS = 2 * LIPW;                 // DMA instructions per wave per tile
+constexpr int LGM = 4;                         // tile-rows per group
+constexpr size_t kLargeLds = (size_t)LSTAGES * LSTAGE_H * sizeof(uint16_t);
+
+template <int... I, class F>
+__device__ __forceinline__ void static_for(std::integer_sequence<int, I...>, F&& f) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int V> using ic = std::integral_constant<int, V>;
+template <bool V> using bc = std::integral_constant<bool, V>;
+
+// s_waitcnt immediate: vmcnt <= n, lgkmcnt <= 0, expcnt untouched.
+constexpr int wait_vm_lgkm0(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4); }
+
+__device__ __forceinline__ int lswz(int r) { return (r >> 2) & 3; }
 
 template <class T>
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
@@ -168,11 +200,14 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+#define MM_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
 template <class T>
 __global__ __launch_bounds__(LThreads, 1) void gemm_mfma_large(GemmArgs a) {
-    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];  // [2][A | B]
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / LWN, wn = wave % LWN;
+    extern __shared__ __attribute__((aligned(1024))) uint16_t lds[];  // [stage][A | B][row][32]
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = w >> 1, wn = w & 1;
     const int64_t tiles_m = a.m / LBM, tiles_n = a.n / LBN;
     const int64_t ntiles = tiles_m * tiles_n;
 
@@ -181,122 +216,139 @@ __global__ __launch_bounds__(LThreads, 1) void gemm_mfma_large(GemmArgs a) {
     const int64_t per_xcd = (ntiles + 7) / 8;
     const int64_t t = (bid % 8) * per_xcd + bid / 8;
     if (t >= ntiles) return;
-    constexpr int GM = 8;
-    const int64_t group = t / (GM * tiles_n);
-    const int64_t first_m = group * GM;
-    const int64_t gsize = tiles_m - first_m < GM ? tiles_m - first_m : GM;
-    const int64_t tm = first_m + (t % (GM * tiles_n)) % gsize;
-    const int64_t tn = (t % (GM * tiles_n)) / gsize;
+    const int64_t group = t / (LGM * tiles_n);
+    const int64_t first_m = group * LGM;
+    const int64_t gsize = tiles_m - first_m < LGM ? tiles_m - first_m : LGM;
+    const int64_t tm = first_m + (t % (LGM * tiles_n)) % gsize;
+    const int64_t tn = (t % (LGM * tiles_n)) / gsize;
     const int64_t m0 = tm * LBM, n0 = tn * LBN;
+    const int nk = (int)(a.k / LBK);  // a multiple of LSTAGES, at least 2 * LSTAGES
+    const int lda = (int)a.lda, ldb = (int)a.ldb;
+
+    // DMA lane mapping: instruction j of a wave covers tile rows w*64 + j*16 +
+    // lane/4; lane writes LDS slot lane%4 of its row with the chunk that the
+    // swizzle puts there. The row's swizzle does not depend on j.
+    const int chunk = (lane % LCPR) ^ lswz(lane / LCPR);
+    const int voa = ((w * 64 + lane / LCPR) * lda + chunk * 8) * 2;
+    const int vob = ((w * 64 + lane / LCPR) * ldb + chunk * 8) * 2;
+    const int lr = lane & 31, lh = lane >> 5;
 
     for (int64_t b = blockIdx.y; b < a.batch; b += gridDim.y) {
         const uint16_t* A = reinterpret_cast<const uint16_t*>(a.A) + b * a.sa + m0 * a.lda;
         const uint16_t* B = reinterpret_cast<const uint16_t*>(a.B) + b * a.sb + n0 * a.ldb;
+        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(A), (short)0, LBM * lda * 2, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(B), (short)0, LBN * ldb * 2, 0x00020000);
 
-        // Staging: thread covers chunk (tid & 7) of rows (tid >> 3) + LROWS * i.
-        // Buffer loads: the tile base is a scalar resource, each lane adds one
-        // 32-bit offset and the row step rides in the scalar offset.
-        const int srow = tid >> 3, schunk = tid & 7;
-        const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(A), (short)0, (int)(LBM * a.lda * 2), 0x00020000);
-        const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(B), (short)0, (int)(LBN * a.ldb * 2), 0x00020000);
-        const int voa = (srow * (int)a.lda + schunk * 8) * 2;
-        const int vob = (srow * (int)a.ldb + schunk * 8) * 2;
-        // Two register staging sets (R0, R1): tile kt+2 is loaded while tile kt
-        // is multiplied and tile kt+1 waits in registers for its LDS stage. The
-        // sets alternate by name in a loop unrolled by two (never copied).
-        u32x4 ra0[LPASS], rb0[LPASS], ra1[LPASS], rb1[LPASS];
-        auto gload = [&](int64_t kt, u32x4 (&ra)[LPASS], u32x4 (&rb)[LPASS]) {
-            const int64_t k0 = kt * LBK;
+        // Half p (instructions 2p, 2p+1 of each operand) of k-tile kt into a stage.
+        auto dma_half = [&](int stage, int kt, int p) {
+            uint16_t* sa = lds + stage * LSTAGE_H + w * 64 * LBK;
+            uint16_t* sb = sa + LBM * LBK;
 #pragma unroll
-            for (int i = 0; i < LPASS; ++i) {
-                ra[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                            rsa, voa, (int)((LROWS * i * a.lda + k0) * 2), 0));
-                rb[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                            rsb, vob, (int)((LROWS * i * a.ldb + k0) * 2), 0));
+            for (int jj = 0; jj < 2; ++jj) {
+                const int j = 2 * p + jj;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, MM_LDS(sa + j * LRPI * LBK), 16, voa,
+                                                         (j * LRPI * lda + kt * LBK) * 2, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, MM_LDS(sb + j * LRPI * LBK), 16, vob,
+                                                         (j * LRPI * ldb + kt * LBK) * 2, 0, 0);
             }
         };
-        // srow & 7 is the same for every pass, so one lane offset plus immediates.
-        const int sto = srow * LBK + ((schunk ^ (srow & 7)) << 3);
-        auto sstore = [&](int stage, const u32x4 (&ra)[LPASS], const u32x4 (&rb)[LPASS]) {
-            uint16_t* sa = lds + stage * 2 * LTILE + sto;
-            uint16_t* sb = sa + LTILE;
-#pragma unroll
-            for (int i = 0; i < LPASS; ++i) {
-                *reinterpret_cast<u32x4*>(sa + LROWS * i * LBK) = ra[i];
-                *reinterpret_cast<u32x4*>(sb + LROWS * i * LBK) = rb[i];
-            }
-        };
-        const int lrow = lane & 31, lhi = lane >> 5, lx = lane & 7;
-
-        f32x16 acc[4][2];
+        f32x16 acc[4][4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-        // Wave tile: rows wm*128 + [0,128) of A, rows wn*64 + [0,64) of B.
-        auto compute = [&](int stage) {
-            const uint16_t* sa = lds + stage * 2 * LTILE;
-            const uint16_t* sb = sa + LTILE;
+        // Fragments of group ks (k 16*ks .. +16) of a stage: lane -> row lane%32
+        // of each 32-row slab, chunk 2*ks + lane/32.
+        auto rd = [&](int stage, int ks, u32x4 (&fa)[4], u32x4 (&fb)[4]) {
+            const uint16_t* sa = lds + stage * LSTAGE_H + wm * 128 * LBK;
+            const uint16_t* sb = lds + stage * LSTAGE_H + LBM * LBK + wn * 128 * LBK;
+            const int off = lr * LBK + (((2 * ks + lh) ^ lswz(lr)) << 3);
 #pragma unroll
-            for (int ks = 0; ks < LBK / 16; ++ks) {
-                // Fragment: lane -> row (lane % 32), chunk 2*ks + lane / 32.
-                const int co = (((2 * ks + lhi) ^ lx) << 3) + lrow * LBK;
-                u32x4 fa[4], fb[2];
+            for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const u32x4*>(sa + i * 32 * LBK + off);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    fa[i] = *reinterpret_cast<const u32x4*>(sa + (wm * 128 + i * 32) * LBK + co);
+            for (int j = 0; j < 4; ++j) fb[j] = *reinterpret_cast<const u32x4*>(sb + j * 32 * LBK + off);
+        };
+        // D[n][m] = sum_k B(n,k) A(m,k): the lane's four consecutive values run along n.
+        auto mm = [&](const u32x4 (&fa)[4], const u32x4 (&fb)[4]) {
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    fb[j] = *reinterpret_cast<const u32x4*>(sb + (wn * 64 + j * 32) * LBK + co);
-                // D[n][m] = sum_k B(n,k) A(m,k)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                for (int j = 0; j < 4; ++j) acc[i][j] = mfma32<T>(fb[j], fa[i], acc[i][j]);
+        };
+        // Scheduling of one group: its 8 fragment reads first, then 16 MFMAs
+        // with a DMA instruction after every fourth when ndma == 4.
+        auto weave = [&](int ndma) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-                    for (int j = 0; j < 2; ++j) acc[i][j] = mfma32<T>(fb[j], fa[i], acc[i][j]);
+            for (int q = 0; q < 4; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+                if (q < ndma) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
             }
         };
+        u32x4 fa0[4], fb0[4], fa1[4], fb1[4];
+        // One k-tile. S_: stage (kt % 4); P1: finish tile kt+3 (second half);
+        // NEXT: tile kt+1 exists; DMA0: start tile kt+4; VM: DMA instructions
+        // allowed in flight after tile kt+1's at the barrier.
+        auto ktile = [&](auto S_, auto P1, auto NEXT, auto DMA0, auto VM, int kt) {
+            constexpr int s = decltype(S_)::value;
+            rd(s, 1, fa1, fb1);
+            if constexpr (decltype(P1)::value) dma_half((s + 3) % LSTAGES, kt + 3, 1);
+            mm(fa0, fb0);
+            weave(decltype(P1)::value ? 4 : 0);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (decltype(NEXT)::value) {
+                __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(decltype(VM)::value));
+                __builtin_amdgcn_s_barrier();
+                rd((s + 1) % LSTAGES, 0, fa0, fb0);
+                if constexpr (decltype(DMA0)::value) dma_half(s, kt + LSTAGES, 0);
+            }
+            mm(fa1, fb1);
+            weave(decltype(DMA0)::value ? 4 : 0);
+            __builtin_amdgcn_sched_barrier(0);
+        };
 
-        // sched_barrier keeps each prefetch issued before the MFMAs it overlaps
-        // (left to itself the scheduler sinks the loads next to their use).
-        const int64_t nk = a.k / LBK;  // even and >= 2 on this path
-        gload(0, ra0, rb0);
-        gload(1, ra1, rb1);
-        sstore(0, ra0, rb0);
-        __syncthreads();
-        for (int64_t kt = 0; kt + 2 < nk; kt += 2) {
-            gload(kt + 2, ra0, rb0);
-            __builtin_amdgcn_sched_barrier(0);
-            compute(0);
-            __builtin_amdgcn_sched_barrier(0);
-            sstore(1, ra1, rb1);
-            __syncthreads();
-            gload(kt + 3, ra1, rb1);
-            __builtin_amdgcn_sched_barrier(0);
-            compute(1);
-            __builtin_amdgcn_sched_barrier(0);
-            sstore(0, ra0, rb0);
-            __syncthreads();
+        // Prologue: tiles 0-3 whole; wait for tile 0.
+#pragma unroll
+        for (int st = 0; st < LSTAGES; ++st) {
+            dma_half(st, st, 0);
+            dma_half(st, st, 1);
         }
-        compute(0);
-        sstore(1, ra1, rb1);
-        __syncthreads();
-        compute(1);
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(LLPS * (LSTAGES - 1)));
+        __builtin_amdgcn_s_barrier();
+        rd(0, 0, fa0, fb0);
+        constexpr int VMS = LLPS * (LSTAGES - 2);  // steady state: tiles kt+2, kt+3 in flight
+        // First round: tile 3 went out whole, so no second half at kt = 0.
+        ktile(ic<0>{}, bc<false>{}, bc<true>{}, bc<true>{}, ic<VMS>{}, 0);
+        static_for(std::integer_sequence<int, 1, 2, 3>{}, [&](auto S_) {
+            ktile(S_, bc<true>{}, bc<true>{}, bc<true>{}, ic<VMS>{}, decltype(S_)::value);
+        });
+        int kt0 = LSTAGES;
+        for (; kt0 + 2 * LSTAGES <= nk; kt0 += LSTAGES) {
+            static_for(std::make_integer_sequence<int, LSTAGES>{}, [&](auto S_) {
+                ktile(S_, bc<true>{}, bc<true>{}, bc<true>{}, ic<VMS>{}, kt0 + decltype(S_)::value);
+            });
+        }
+        // Last round: no new tiles; finish the second half of tile nk-1 at s = 0.
+        static_for(std::make_integer_sequence<int, LSTAGES>{}, [&](auto S_) {
+            constexpr int s = decltype(S_)::value;
+            ktile(S_, bc<s == 0>{}, bc<(s < LSTAGES - 1)>{}, bc<false>{},
+                  ic<LLPS * (LSTAGES - 2 - s < 0 ? 0 : LSTAGES - 2 - s)>{}, kt0 + s);
+        });
 
         // Lane holds C[m = mfrag base + lane%32][n = nfrag base + (v/4)*8 + (lane/32)*4 + v%4].
         uint16_t* C = reinterpret_cast<uint16_t*>(a.C) + b * a.sc;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int64_t gm = m0 + wm * 128 + i * 32 + (lane & 31);
+            const int64_t gm = m0 + wm * 128 + i * 32 + lr;
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
+            for (int j = 0; j < 4; ++j) {
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    const int64_t gn = n0 + wn * 64 + j * 32 + g * 8 + (lane >> 5) * 4;
+                    const int64_t gn = n0 + wn * 128 + j * 32 + g * 8 + lh * 4;
                     u32x2 v;
                     v[0] = (uint32_t)narrow(T{}, acc[i][j][4 * g]) | ((uint32_t)narrow(T{}, acc[i][j][4 * g + 1]) << 16);
                     v[1] = (uint32_t)narrow(T{}, acc[i][j][4 * g + 2]) | ((uint32_t)narrow(T{}, acc[i][j][4 * g + 3]) << 16);
@@ -304,9 +356,11 @@ __global__ __launch_bounds__(LThreads, 1) void gemm_mfma_large(GemmArgs a) {
                 }
             }
         }
+        // The next batch's prologue overwrites every stage.
         __syncthreads();
     }
 }
+#undef MM_LDS
 
 // ---------------------------------------------------------------------------
 // f32 kernel: 64 x 64 tile, BK = 16, 256 threads x (4 x 4) outputs, FMA.
@@ -393,29 +447,32 @@ const void* pick_f32(bool ta, bool tb) {
 
 }  // namespace
 
-hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, int* kernel) {
     void* args[] = {const_cast<GemmArgs*>(&a)};
     const unsigned gy = (unsigned)(a.batch < 65535 ? a.batch : 65535);
     if (a.dtype == 0) {
         const int64_t tiles = ((a.m + FBM - 1) / FBM) * ((a.n + FBN - 1) / FBN);
+        *kernel = MM_KERNEL_GEMM_F32;
         return hipLaunchKernel(pick_f32(a.ta, a.tb), dim3((unsigned)tiles, gy), dim3(256), args,
                                0, s);
     }
     const bool vec = aligned16(a.A) && aligned16(a.B) && a.lda % 8 == 0 && a.ldb % 8 == 0 &&
                      a.sa % 8 == 0 && a.sb % 8 == 0;
     const int64_t big_tiles = (a.m / LBM) * (a.n / LBN);
-    if (vec && !a.ta && a.tb && a.m % LBM == 0 && a.n % LBN == 0 && a.k % (2 * LBK) == 0 &&
-        big_tiles >= 512 && a.ldc % 4 == 0 && (reinterpret_cast<uintptr_t>(a.C) & 7) == 0 &&
-        a.sc % 4 == 0) {
+    if (vec && !a.ta && a.tb && a.m % LBM == 0 && a.n % LBN == 0 &&
+        a.k % (LSTAGES * LBK) == 0 && a.k >= 2 * LSTAGES * LBK && big_tiles * a.batch >= 512 &&
+        a.lda < (1 << 22) && a.ldb < (1 << 22) && a.ldc % 4 == 0 &&
+        (reinterpret_cast<uintptr_t>(a.C) & 7) == 0 && a.sc % 4 == 0) {
         // Large NT products: 256 x 256 tiles (enough of them to fill the chip).
         const void* fn = a.dtype == 1 ? (const void*)&gemm_mfma_large<TF16>
                                       : (const void*)&gemm_mfma_large<TBF16>;
         const unsigned grid = (unsigned)(((big_tiles + 7) / 8) * 8);
-        return hipLaunchKernel(fn, dim3(grid, gy), dim3(LThreads), args,
-                               (size_t)2 * 2 * LTILE * sizeof(uint16_t), s);
+        *kernel = MM_KERNEL_GEMM_LARGE;
+        return hipLaunchKernel(fn, dim3(grid, gy), dim3(LThreads), args, kLargeLds, s);
     }
     const int64_t tiles = ((a.m + GBM - 1) / GBM) * ((a.n + GBN - 1) / GBN);
     const void* fn = a.dtype == 1 ? pick_mfma<TF16>(a.ta, a.tb, vec) : pick_mfma<TBF16>(a.ta, a.tb, vec);
+    *kernel = MM_KERNEL_GEMM_TILED;
     return hipLaunchKernel(fn, dim3((unsigned)tiles, gy), dim3(GThreads), args, 0, s);
 }
 

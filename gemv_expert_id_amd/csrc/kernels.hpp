@@ -1,11 +1,14 @@
 // Kernel argument blocks and host-side launchers. The launchers (defined in
 // gemv.hip, gemm.hip, mmid.hip) pick a template instance, size the grid and
 // enqueue exactly one kernel; they never validate (the C ABI layer has done
-// that) and return the hipError_t of the enqueue.
+// that), report the kernel family they chose (an mm_kernel code) through
+// `kernel`, and return the hipError_t of the enqueue.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include "mm.h"
 
 namespace mmk {
 
@@ -25,7 +28,8 @@ struct GemvArgs {
     int32_t dtype;       // 0 f32, 1 f16, 2 bf16
     int32_t col_form;    // 1: M(o, p) = mat[p * ld + o]
 };
-hipError_t launch_gemv(const GemvArgs& a, hipStream_t s);
+// Launchers enqueue one kernel on `s`; `kernel` receives its mm_kernel code.
+hipError_t launch_gemv(const GemvArgs& a, hipStream_t s, int* kernel);
 
 // C[b] = op(A[b]) . op(B[b]); pointers already include the byte offsets.
 struct GemmArgs {
@@ -39,7 +43,7 @@ struct GemmArgs {
     int32_t dtype;
     int32_t ta, tb;
 };
-hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, int* kernel);
 
 // Expert-ID matmul. Byte strides locate the activation row of (token, slot).
 struct IdArgs {
@@ -58,8 +62,8 @@ struct IdArgs {
     int32_t wdtype;
     int32_t dedup;                // direct: repeated ids of one token share one pass
 };
-hipError_t launch_id_direct(const IdArgs& a, hipStream_t s);
-hipError_t launch_id_map(const IdArgs& a, hipStream_t s);
-hipError_t launch_id_grouped(const IdArgs& a, hipStream_t s);
+hipError_t launch_id_direct(const IdArgs& a, hipStream_t s, int* kernel);
+hipError_t launch_id_map(const IdArgs& a, hipStream_t s, int* kernel);
+hipError_t launch_id_grouped(const IdArgs& a, hipStream_t s, int* kernel);
 
 }  // namespace mmk

@@ -772,7 +772,7 @@ inline uint64_t grid_for(const IdArgs& a, int bm, int bn) {
 
 }  // namespace
 
-hipError_t launch_id_direct(const IdArgs& a, hipStream_t s) {
+hipError_t launch_id_direct(const IdArgs& a, hipStream_t s, int* kernel) {
     void* args[] = {const_cast<IdArgs*>(&a)};
     const int64_t es = a.wdtype == 0 ? 4 : 2;
     const int64_t ch = 16 / es;  // weights per 16-byte load
@@ -786,8 +786,10 @@ hipError_t launch_id_direct(const IdArgs& a, hipStream_t s) {
 #define MM_DF(T) (one ? (const void*)&id_direct_fast<T, true> : (const void*)&id_direct_fast<T, false>)
         const void* fn = a.wdtype == 0 ? MM_DF(TF32) : a.wdtype == 1 ? MM_DF(TF16) : MM_DF(TBF16);
 #undef MM_DF
+        *kernel = MM_KERNEL_ID_DIRECT_FAST;
         return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
     }
+    *kernel = MM_KERNEL_ID_DIRECT;
     constexpr int R = 2;
     const int64_t per_block = kWaves * R;
     const int64_t work = (int64_t)a.m * a.top_k * ((a.n + per_block - 1) / per_block);
@@ -803,7 +805,8 @@ hipError_t launch_id_direct(const IdArgs& a, hipStream_t s) {
     return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
 }
 
-hipError_t launch_id_map(const IdArgs& a, hipStream_t s) {
+hipError_t launch_id_map(const IdArgs& a, hipStream_t s, int* kernel) {
+    *kernel = MM_KERNEL_ID_MAP;
     void* args[] = {const_cast<IdArgs*>(&a)};
     // 12 bytes of LDS per (wave, expert); keep the tables within 64 KiB.
     int waves = (int)(65536 / (12ull * a.n_experts));
@@ -813,7 +816,7 @@ hipError_t launch_id_map(const IdArgs& a, hipStream_t s) {
                            args, lds, s);
 }
 
-hipError_t launch_id_grouped(const IdArgs& a, hipStream_t s) {
+hipError_t launch_id_grouped(const IdArgs& a, hipStream_t s, int* kernel) {
     if (a.wdtype == 2) {
         // Output tile width: as few tiles as cover n at GMAXBN each, raised until
         // experts x tiles reaches the CU count (every CU streams one W slab).
@@ -829,6 +832,7 @@ hipError_t launch_id_grouped(const IdArgs& a, hipStream_t s) {
         const uint64_t in_rows = a.layout == 0 ? a.m : (uint64_t)a.m * a.top_k;
         const bool fast = vec && a.k % QBK == 0 && in_rows * a.k * 4 < (1ull << 32);
         const uint64_t g = grid_for(a, QBM, bn);
+        *kernel = MM_KERNEL_ID_GROUPED_MFMA;
         const void* fn = fast ? (const void*)&id_grouped_bf16<true, true>
                        : vec  ? (const void*)&id_grouped_bf16<true, false>
                               : (const void*)&id_grouped_bf16<false, false>;
@@ -836,6 +840,7 @@ hipError_t launch_id_grouped(const IdArgs& a, hipStream_t s) {
     }
     void* args[] = {const_cast<IdArgs*>(&a)};
     const uint64_t g = grid_for(a, FBM, FBN);
+    *kernel = MM_KERNEL_ID_GROUPED_FMA;
     const void* fn = a.wdtype == 0 ? (const void*)&id_grouped_fma<TF32> : (const void*)&id_grouped_fma<TF16>;
     return hipLaunchKernel(fn, dim3((unsigned)g), dim3(kThreads), args, 0, s);
 }

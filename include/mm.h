@@ -45,7 +45,7 @@ extern "C" {
 #define MM_ABI_VERSION 1u
 /* Schema version of capability/receipt records (mlx-native
  * `DENSE_MATMUL_ID_SCHEMA_VERSION`). */
-#define MM_ID_SCHEMA_VERSION 3u
+#define MM_ID_SCHEMA_VERSION 4u
 /* Largest expert count the grouped route accepts (mlx-native
  * `GROUPED_MAX_EXPERTS`). */
 #define MM_ID_GROUPED_MAX_EXPERTS 1024u
@@ -77,11 +77,28 @@ typedef enum {
     MM_ROUTE_ID_PREFILL = 5 /* map + grouped in one call */
 } mm_route;
 
+/* Kernel family of a launch (reported in receipts; the choice depends on
+ * shape, layout and alignment). */
+typedef enum {
+    MM_KERNEL_GEMV_ROWS = 0,         /* matrix rows along K, 16-byte streaming loads */
+    MM_KERNEL_GEMV_ROWS_ELEM = 1,    /* matrix rows along K, element loads */
+    MM_KERNEL_GEMV_COLS = 2,         /* outputs contiguous in the matrix */
+    MM_KERNEL_GEMM_TILED = 3,        /* 128 x 128 MFMA tiles, any layout and edge */
+    MM_KERNEL_GEMM_LARGE = 4,        /* 256 x 256 MFMA tiles, NT, divisible shapes */
+    MM_KERNEL_GEMM_F32 = 5,          /* f32 FMA tiles */
+    MM_KERNEL_ID_DIRECT_FAST = 6,    /* direct route, 16-byte loads, one id-row load */
+    MM_KERNEL_ID_DIRECT = 7,         /* direct route, general */
+    MM_KERNEL_ID_MAP = 8,            /* map pass */
+    MM_KERNEL_ID_GROUPED_MFMA = 9,   /* grouped pass, bf16 weights on MFMA */
+    MM_KERNEL_ID_GROUPED_FMA = 10    /* grouped pass, f32 / f16 weights */
+} mm_kernel;
+
 typedef struct {
     uint32_t schema_version;  /* MM_ID_SCHEMA_VERSION */
     uint32_t route;           /* mm_route actually taken */
     uint32_t dtype;           /* mm_dtype of A/B/C or of the expert weights */
     uint32_t dispatch_count;  /* kernel launches enqueued by the call */
+    uint32_t kernel;          /* mm_kernel of the last launch */
 } mm_receipt;
 
 /* ------------------------------------------------------------------------ */

@@ -198,11 +198,13 @@ def test_large_k_many_tiles_f16():
     check_gemm(case, what="large k")
 
 
-def _sampled_check(case, n_samples, seed, exact=False):
+def _sampled_check(case, n_samples, seed, exact=False, kernel=None):
     from gpu_util import GemmRun, assert_close
     import oracle
     run = GemmRun(case)
-    run.run()
+    rec = run.run()
+    if kernel is not None:
+        assert rec.kernel == kernel, f"kernel {rec.kernel}, expected {kernel}"
     bits = run.c_bits()
     rng = np.random.default_rng(seed)
     bs = rng.integers(0, case.batch, n_samples)
@@ -224,27 +226,38 @@ def _sampled_check(case, n_samples, seed, exact=False):
 
 
 @pytest.mark.parametrize("dt", [wl.F16, wl.BF16])
-def test_large_tile_route(dt):
-    """m, n multiples of 256 with >= 512 tiles: the 256 x 256 MFMA kernel."""
-    _say(f"large-tile NT dt={wl.DTYPE_NAMES[dt]} m=4096 n=8192 k=192")
-    case = wl.random_gemm_case(41, dt, 1, 4096, 8192, 192, False, True)
-    _sampled_check(case, 4096, 3)
+@pytest.mark.parametrize("k", [256, 640])
+def test_large_tile_route(dt, k):
+    """m, n multiples of 256 with >= 512 tiles, k % 128 == 0, k >= 256: the
+    256 x 256 MFMA kernel (k = 256: first and last rounds only; k = 640: the
+    steady loop runs too)."""
+    _say(f"large-tile NT dt={wl.DTYPE_NAMES[dt]} m=4096 n=8192 k={k}")
+    case = wl.random_gemm_case(41, dt, 1, 4096, 8192, k, False, True)
+    _sampled_check(case, 4096, 3, kernel=mm.MM_KERNEL_GEMM_LARGE)
 
 
 def test_large_tile_route_ramp_exact():
-    _say("large-tile NT ramp exact m=8192 n=4096 k=320")
-    m, n, k = 8192, 4096, 320
+    _say("large-tile NT ramp exact m=8192 n=4096 k=384")
+    m, n, k = 8192, 4096, 384
     a = wl.ramp(m * k, 1).reshape(1, m, k)
     b = wl.ramp(n * k, 2).reshape(1, n, k)
     case = wl.make_gemm_case(wl.F16, a, b, False, True)
-    _sampled_check(case, 4096, 4, exact=True)
+    _sampled_check(case, 4096, 4, exact=True, kernel=mm.MM_KERNEL_GEMM_LARGE)
 
 
 def test_large_tile_route_batched_padded():
-    _say("large-tile NT batched, padded ld, bf16 m=2048 n=2048 k=128 batch 2")
+    _say("large-tile NT batched, padded ld, bf16 m=4096 n=4096 k=256 batch 2")
     rng = np.random.default_rng(9)
-    b_, m, n, k = 2, 2048, 4096, 128
+    b_, m, n, k = 2, 4096, 4096, 256
     a = rng.standard_normal((b_, m, k))
     bb = rng.standard_normal((b_, n, k)) / np.sqrt(k)
     case = wl.make_gemm_case(wl.BF16, a, bb, False, True, lda=k + 64, ldb=k + 8, ldc=n + 4)
-    _sampled_check(case, 4096, 5)
+    _sampled_check(case, 4096, 5, kernel=mm.MM_KERNEL_GEMM_LARGE)
+
+
+@pytest.mark.parametrize("k", [128, 192, 320])
+def test_large_shape_other_k_takes_tiled_kernel(k):
+    """k below 256 or not a multiple of 128: the 128 x 128 kernel, same results."""
+    _say(f"NT f16 m=4096 n=8192 k={k} (tiled kernel)")
+    case = wl.random_gemm_case(43, wl.F16, 1, 4096, 8192, k, False, True)
+    _sampled_check(case, 2048, 6, kernel=mm.MM_KERNEL_GEMM_TILED)
