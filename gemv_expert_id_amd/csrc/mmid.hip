@@ -14,6 +14,9 @@
 //              into bf16 hi + lo parts (two MFMAs, f32 accumulate); f32/f16
 //              weights run an LDS-tiled FMA kernel. The tile list is rebuilt
 //              from the counts inside every block, so the host never waits.
+#include <type_traits>
+#include <utility>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -452,7 +455,8 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
-// FAST: k % 64 == 0, 16-byte aligned operands, input below 4 GiB. Every
+// FAST: k % 256 == 0, 16-byte aligned operands, input and one expert below
+// 2 GiB. Every
 // global load is then issued unconditionally (dead columns read a clamped,
 // valid address and are never stored), so the compiler counts outstanding
 // loads exactly and the prefetches stay in flight across the barrier.
@@ -467,7 +471,8 @@ __global__ __launch_bounds__(GW * kWave, 1) void id_grouped_bf16(IdArgs a, uint3
     __shared__ uint64_t s_xoff[QBM];
     __shared__ __attribute__((aligned(16))) uint16_t Xs[2][2][QXS];  // [stage][hi/lo]
 
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform: scalar branches
     const uint32_t n_tiles = (a.n + bn - 1) / bn;
     uint32_t ti, nt;
     block_to_tile(n_tiles, &ti, &nt);
@@ -527,11 +532,20 @@ __global__ __launch_bounds__(GW * kWave, 1) void id_grouped_bf16(IdArgs a, uint3
         xoff[p] = (uint32_t)off + (uint32_t)xk * 4u;
         if constexpr (!FAST) xrow[p] = reinterpret_cast<const char*>(a.X) + off;
     }
+    // FAST: buffer loads; the lane offsets stay fixed and the K step rides in
+    // the scalar offset, so no address register is rewritten while a load
+    // that targets it may still be in flight.
+    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(a.X), (short)0, 0x7fffffff, 0x00020000);
+    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(reinterpret_cast<const char*>(a.W) + (uint64_t)e * a.expert_stride_bytes),
+        (short)0, (int)(FAST ? a.n * a.k * 2 : 0), 0x00020000);
     auto load_x = [&](int64_t k0, f32x4 (&xv)[XP]) {
         if constexpr (FAST) {
-            const char* xb0 = reinterpret_cast<const char*>(a.X + k0);
 #pragma unroll
-            for (int p = 0; p < XP; ++p) xv[p] = *reinterpret_cast<const f32x4*>(xb0 + xoff[p]);
+            for (int p = 0; p < XP; ++p)
+                xv[p] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                            xrs, (int)xoff[p], (int)(k0 * 4), 0));
             return;
         }
 #pragma unroll
@@ -565,7 +579,19 @@ __global__ __launch_bounds__(GW * kWave, 1) void id_grouped_bf16(IdArgs a, uint3
         }
     };
     // Weight fragments: lane -> column wcol[j], k offset kk*32 + (lane/16)*8.
+    int wvo[GF];
+#pragma unroll
+    for (int j = 0; j < GF; ++j) wvo[j] = (int)((wcol[j] * a.k + (lane >> 4) * 8) * 2);
     auto load_w = [&](int64_t k0, u32x4 (&w)[GF][2]) {
+        if constexpr (FAST) {
+#pragma unroll
+            for (int j = 0; j < GF; ++j)
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+                    w[j][kk] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                   wrs, wvo[j] + kk * 64, (int)(k0 * 2), 2 /* slc: streamed */));
+            return;
+        }
 #pragma unroll
         for (int j = 0; j < GF; ++j) {
 #pragma unroll
@@ -597,24 +623,24 @@ __global__ __launch_bounds__(GW * kWave, 1) void id_grouped_bf16(IdArgs a, uint3
     f32x4 xA[XP], xB[XP];
     auto compute = [&](int64_t it, const u32x4 (&wc)[GF][2]) {
         const int st = (int)(it & 1);
+        // Per 32-wide half kk: the hi products of every live (row, output)
+        // fragment, then the lo products, so the two MFMAs that update one
+        // accumulator are never issued back to back.
 #pragma unroll
-        for (int mf = 0; mf < 8; ++mf) {
-            if (mf < nmf) {
-                const int row = mf * 16 + (lane & 15);
+        for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    const int ko = row * QLDK + kk * 32 + (lane >> 4) * 8;
-                    const u32x4 xh = *reinterpret_cast<const u32x4*>(&Xs[st][0][ko]);
-                    const u32x4 xl = *reinterpret_cast<const u32x4*>(&Xs[st][1][ko]);
+            for (int part = 0; part < 2; ++part) {
 #pragma unroll
-                    for (int j = 0; j < GF; ++j) {
-                        if (j < nf_live) {
-                            acc[mf][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                __builtin_bit_cast(bf16x8, wc[j][kk]), __builtin_bit_cast(bf16x8, xh),
-                                acc[mf][j], 0, 0, 0);
-                            acc[mf][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                __builtin_bit_cast(bf16x8, wc[j][kk]), __builtin_bit_cast(bf16x8, xl),
-                                acc[mf][j], 0, 0, 0);
+                for (int mf = 0; mf < 8; ++mf) {
+                    if (mf < nmf) {
+                        const int ko = (mf * 16 + (lane & 15)) * QLDK + kk * 32 + (lane >> 4) * 8;
+                        const u32x4 xv = *reinterpret_cast<const u32x4*>(&Xs[st][part][ko]);
+#pragma unroll
+                        for (int j = 0; j < GF; ++j) {
+                            if (j < nf_live)
+                                acc[mf][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    __builtin_bit_cast(bf16x8, wc[j][kk]),
+                                    __builtin_bit_cast(bf16x8, xv), acc[mf][j], 0, 0, 0);
                         }
                     }
                 }
@@ -631,6 +657,43 @@ __global__ __launch_bounds__(GW * kWave, 1) void id_grouped_bf16(IdArgs a, uint3
         __syncthreads();
     };
 
+    if constexpr (FAST) {
+        // nk % 4 == 0. W is loaded three K steps ahead into four buffers, X two
+        // steps ahead into two; a round of four steps closes both rotations, so
+        // the steady loop is straight-line code and the compiler's load
+        // counting is exact (a conditional load would make it wait for all).
+        // X (from L2) is fetched one step ahead into one register buffer.
+        u32x4 w3[GF][2];
+        auto fstep = [&](auto LW, auto LX, auto SX, int64_t it, const u32x4 (&wc)[GF][2],
+                         u32x4 (&wf)[GF][2]) {
+            if constexpr (decltype(LW)::value) load_w((it + 3) * QBK, wf);
+            compute(it, wc);
+            if constexpr (decltype(SX)::value) store_x(xA, (int)((it + 1) & 1));
+            if constexpr (decltype(LX)::value) load_x((it + 2) * QBK, xA);
+            __syncthreads();
+        };
+        using T_ = std::integral_constant<bool, true>;
+        using F_ = std::integral_constant<bool, false>;
+        load_w(0, w0);
+        load_w(QBK, w1);
+        load_w(2 * QBK, w2);
+        load_x(0, xA);
+        store_x(xA, 0);
+        load_x(QBK, xA);
+        __syncthreads();
+        int64_t it = 0;
+        for (; it + 4 < nk; it += 4) {
+            fstep(T_{}, T_{}, T_{}, it, w0, w3);
+            fstep(T_{}, T_{}, T_{}, it + 1, w1, w0);
+            fstep(T_{}, T_{}, T_{}, it + 2, w2, w1);
+            fstep(T_{}, T_{}, T_{}, it + 3, w3, w2);
+        }
+        // Last round: W of the final step and X of the last two remain.
+        fstep(T_{}, T_{}, T_{}, it, w0, w3);
+        fstep(F_{}, T_{}, T_{}, it + 1, w1, w0);
+        fstep(F_{}, F_{}, T_{}, it + 2, w2, w1);
+        fstep(F_{}, F_{}, F_{}, it + 3, w3, w2);
+    } else {
     load_w(0, w0);
     if (nk > 1) load_w(QBK, w1);
     load_x(0, xA);
@@ -645,6 +708,7 @@ __global__ __launch_bounds__(GW * kWave, 1) void id_grouped_bf16(IdArgs a, uint3
         if (it + 3 < nk) step(it + 3, w0, w2, xB);
         if (it + 4 < nk) step(it + 4, w1, w0, xA);
         if (it + 5 < nk) step(it + 5, w2, w1, xB);
+    }
     }
 
     // Lane holds out[row = mf*16 + lane%16][n = frag column base + 4*(lane/16) + q].
@@ -830,7 +894,8 @@ hipError_t launch_id_grouped(const IdArgs& a, hipStream_t s, int* kernel) {
                          aligned16(a.X) && a.x_tok_stride_bytes % 16 == 0 &&
                          a.x_slot_stride_bytes % 16 == 0;
         const uint64_t in_rows = a.layout == 0 ? a.m : (uint64_t)a.m * a.top_k;
-        const bool fast = vec && a.k % QBK == 0 && in_rows * a.k * 4 < (1ull << 32);
+        const bool fast = vec && a.k % (4 * QBK) == 0 && in_rows * a.k * 4 < (1ull << 31) &&
+                          (uint64_t)a.n * a.k * 2 < (1ull << 31);
         const uint64_t g = grid_for(a, QBM, bn);
         *kernel = MM_KERNEL_ID_GROUPED_MFMA;
         const void* fn = fast ? (const void*)&id_grouped_bf16<true, true>

@@ -80,7 +80,11 @@ def test_direct(wdt, layout, shape):
 @pytest.mark.parametrize("wdt", DTYPES)
 @pytest.mark.parametrize("layout", [0, 1])
 @pytest.mark.parametrize("shape", [(9, 7, 35, 2, 4), (5, 130, 260, 3, 6), (40, 300, 520, 8, 16),
-                                   (300, 65, 96, 2, 3), (1, 17, 40, 4, 1024)])
+                                   (300, 65, 96, 2, 3), (1, 17, 40, 4, 1024),
+                                   # k % 256 == 0: the pipelined bf16 form (k = 256 is one round)
+                                   (33, 200, 512, 4, 8), (17, 96, 256, 2, 5),
+                                   # more than 128 rows per expert: several row tiles
+                                   (300, 64, 512, 2, 3)])
 def test_prefill_map_grouped(wdt, layout, shape):
     m, n, k, top_k, E = shape
     _say(f"prefill wdt={wl.DTYPE_NAMES[wdt]} layout={layout} shape={shape}")
