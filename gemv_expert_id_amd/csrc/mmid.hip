@@ -588,8 +588,12 @@ __global__ __launch_bounds__(GW * kWave, 1) void id_grouped_bf16(IdArgs a, uint3
             for (int j = 0; j < GF; ++j)
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk)
+                    // Plain (cached) loads: with the non-temporal hint the two
+                    // 64-byte halves of a line, fetched by kk = 0 and 1, were
+                    // each served from HBM (streaming dropped from ~4.8 to
+                    // ~3.4 TB/s in isolation).
                     w[j][kk] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                   wrs, wvo[j] + kk * 64, (int)(k0 * 2), 2 /* slc: streamed */));
+                                   wrs, wvo[j] + kk * 64, (int)(k0 * 2), 0));
             return;
         }
 #pragma unroll
