@@ -34,56 +34,86 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// Stage one BM x BK (or BN x BK) tile into LDS as [row][k].
-// kcontig: element (row, p) at base[row * ld + p]; else at base[p * ld + row].
+// Tile staging, split into a global fetch (into registers, so the next
+// k-tile is in flight while the current one is multiplied) and an LDS store.
+// A chunk is 8 elements: 8 consecutive k of one row (KCONTIG: element (row, p)
+// at base[row * ld + p]) or 8 consecutive rows at one k (else: base[p * ld +
+// row]); out-of-range elements are zero.
+constexpr int GCH = (GBM * GBK / 8) / GThreads;  // chunks per thread per operand
+
 template <bool KCONTIG, bool VEC>
-__device__ __forceinline__ void stage_tile(const uint16_t* __restrict__ base, int64_t ld,
+__device__ __forceinline__ void fetch_tile(const uint16_t* __restrict__ base, int64_t ld,
                                            int64_t nrows, int64_t K, int64_t row0, int64_t k0,
-                                           uint16_t* __restrict__ lds) {
+                                           u32x4 (&v)[GCH]) {
     const int tid = threadIdx.x;
 #pragma unroll
-    for (int u = 0; u < (GBM * GBK / 8) / GThreads; ++u) {
+    for (int u = 0; u < GCH; ++u) {
         const int q = tid + u * GThreads;
         if constexpr (KCONTIG) {
             const int row = q >> 2, kc = (q & 3) * 8;
             const int64_t gr = row0 + row, gk = k0 + kc;
-            uint16_t* dst = lds + row * GLDK + kc;
             if (VEC && gr < nrows && gk + 8 <= K) {
-                *reinterpret_cast<u32x4*>(dst) = ld16(base + gr * ld + gk);
+                v[u] = ld16(base + gr * ld + gk);
             } else {
+                uint32_t h[8];
 #pragma unroll
                 for (int t = 0; t < 8; ++t)
-                    dst[t] = (gr < nrows && gk + t < K) ? base[gr * ld + gk + t] : (uint16_t)0;
+                    h[t] = (gr < nrows && gk + t < K) ? base[gr * ld + gk + t] : 0u;
+                v[u] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                             h[6] | (h[7] << 16)};
             }
         } else {
             const int p = q >> 4, rc = (q & 15) * 8;
             const int64_t gk = k0 + p, gr = row0 + rc;
             if (VEC && gk < K && gr + 8 <= nrows) {
-                u32x4 v = ld16(base + gk * ld + gr);
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    lds[(rc + 2 * t) * GLDK + p] = (uint16_t)(v[t] & 0xffffu);
-                    lds[(rc + 2 * t + 1) * GLDK + p] = (uint16_t)(v[t] >> 16);
-                }
+                v[u] = ld16(base + gk * ld + gr);
             } else {
+                uint32_t h[8];
 #pragma unroll
                 for (int t = 0; t < 8; ++t)
-                    lds[(rc + t) * GLDK + p] =
-                        (gk < K && gr + t < nrows) ? base[gk * ld + gr + t] : (uint16_t)0;
+                    h[t] = (gk < K && gr + t < nrows) ? base[gk * ld + gr + t] : 0u;
+                v[u] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                             h[6] | (h[7] << 16)};
             }
         }
     }
 }
 
+// Write fetched chunks into LDS as [row][k] (pitch GLDK).
+template <bool KCONTIG>
+__device__ __forceinline__ void store_tile(const u32x4 (&v)[GCH], uint16_t* __restrict__ lds) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < GCH; ++u) {
+        const int q = tid + u * GThreads;
+        if constexpr (KCONTIG) {
+            const int row = q >> 2, kc = (q & 3) * 8;
+            *reinterpret_cast<u32x4*>(lds + row * GLDK + kc) = v[u];
+        } else {
+            const int p = q >> 4, rc = (q & 15) * 8;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                lds[(rc + 2 * t) * GLDK + p] = (uint16_t)(v[u][t] & 0xffffu);
+                lds[(rc + 2 * t + 1) * GLDK + p] = (uint16_t)(v[u][t] >> 16);
+            }
+        }
+    }
+}
+
+// Block = 4 waves (2 x 2), tile 128 x 128 x 32, each wave 64 x 64 with
+// v_mfma_f32_16x16x32. Double-buffered LDS: k-tile kt+1 is fetched into
+// registers before tile kt is multiplied and stored to the other LDS buffer
+// after it, so one barrier per k-tile separates the writes from the reads.
 template <class T, bool TA, bool TB, bool VEC>
 __global__ __launch_bounds__(GThreads) void gemm_mfma_generic(GemmArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t As[GBM * GLDK];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[GBN * GLDK];
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][GBM * GLDK];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][GBN * GLDK];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int64_t tiles_n = (a.n + GBN - 1) / GBN;
     const int64_t tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
     const int64_t m0 = tm * GBM, n0 = tn * GBN;
+    const int64_t nk = (a.k + GBK - 1) / GBK;
 
     for (int64_t b = blockIdx.y; b < a.batch; b += gridDim.y) {
         const uint16_t* A = reinterpret_cast<const uint16_t*>(a.A) + b * a.sa;
@@ -94,24 +124,38 @@ __global__ __launch_bounds__(GThreads) void gemm_mfma_generic(GemmArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        for (int64_t k0 = 0; k0 < a.k; k0 += GBK) {
-            __syncthreads();
-            stage_tile<!TA, VEC>(A, a.lda, a.m, a.k, m0, k0, As);
-            stage_tile<TB, VEC>(B, a.ldb, a.n, a.k, n0, k0, Bs);
-            __syncthreads();
+        u32x4 va[GCH], vb[GCH];
+        fetch_tile<!TA, VEC>(A, a.lda, a.m, a.k, m0, 0, va);
+        fetch_tile<TB, VEC>(B, a.ldb, a.n, a.k, n0, 0, vb);
+        __syncthreads();  // the previous batch's readers are done with buffer 0
+        store_tile<!TA>(va, As[0]);
+        store_tile<TB>(vb, Bs[0]);
+        __syncthreads();
+        for (int64_t kt = 0; kt < nk; ++kt) {
+            const int cur = (int)(kt & 1);
+            const bool more = kt + 1 < nk;
+            if (more) {
+                fetch_tile<!TA, VEC>(A, a.lda, a.m, a.k, m0, (kt + 1) * GBK, va);
+                fetch_tile<TB, VEC>(B, a.ldb, a.n, a.k, n0, (kt + 1) * GBK, vb);
+            }
             u32x4 af[4], bf[4];
             const int kofs = (lane >> 4) * 8;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                af[i] = *reinterpret_cast<const u32x4*>(&As[(wm * 64 + i * 16 + (lane & 15)) * GLDK + kofs]);
+                af[i] = *reinterpret_cast<const u32x4*>(&As[cur][(wm * 64 + i * 16 + (lane & 15)) * GLDK + kofs]);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                bf[j] = *reinterpret_cast<const u32x4*>(&Bs[(wn * 64 + j * 16 + (lane & 15)) * GLDK + kofs]);
+                bf[j] = *reinterpret_cast<const u32x4*>(&Bs[cur][(wn * 64 + j * 16 + (lane & 15)) * GLDK + kofs]);
             // D[n][m] = sum_k B(n,k) A(m,k): lane holds C[m = lane%16][n = 4*(lane/16) + q].
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc[i][j] = mfma16<T>(bf[j], af[i], acc[i][j]);
+            if (more) {
+                store_tile<!TA>(va, As[cur ^ 1]);
+                store_tile<TB>(vb, Bs[cur ^ 1]);
+            }
+            __syncthreads();
         }
 
         uint16_t* C = reinterpret_cast<uint16_t*>(a.C) + b * a.sc;
@@ -363,59 +407,90 @@ __global__ __launch_bounds__(LThreads, 1) void gemm_mfma_large(GemmArgs a) {
 #undef MM_LDS
 
 // ---------------------------------------------------------------------------
-// f32 kernel: 64 x 64 tile, BK = 16, 256 threads x (4 x 4) outputs, FMA.
+// f32 kernel: TILE x TILE tile (64, or 32 when there are few tiles), BK = 16,
+// 256 threads x (TILE/16)^2 outputs, FMA. Double-buffered LDS: k-tile kt+1
+// is fetched into registers before tile kt is used and stored after it.
 // ---------------------------------------------------------------------------
-constexpr int FBM = 64, FBN = 64, FBK = 16;
+constexpr int FBK = 16;
 
-template <bool TA, bool TB>
+template <bool TA, bool TB, int TILE>
 __global__ __launch_bounds__(256) void gemm_f32_fma(GemmArgs a) {
-    __shared__ float As[FBK][FBM + 4];  // [k][m]
-    __shared__ float Bs[FBK][FBN + 4];  // [k][n]
+    constexpr int R = TILE / 16;              // outputs per thread per dimension
+    constexpr int LD = TILE * FBK / 256;      // elements per thread per operand and k-tile
+    __shared__ float As[2][FBK][TILE + 4];    // [k][m]
+    __shared__ float Bs[2][FBK][TILE + 4];    // [k][n]
     const int tid = threadIdx.x;
     const int tx = tid & 15, ty = tid >> 4;
-    const int64_t tiles_n = (a.n + FBN - 1) / FBN;
-    const int64_t m0 = (blockIdx.x / tiles_n) * FBM, n0 = (blockIdx.x % tiles_n) * FBN;
+    const int64_t tiles_n = (a.n + TILE - 1) / TILE;
+    const int64_t m0 = (blockIdx.x / tiles_n) * TILE, n0 = (blockIdx.x % tiles_n) * TILE;
+    const int64_t nk = (a.k + FBK - 1) / FBK;
+    // Element u of this thread: A (i, p) and B (p, j) walk the stored-contiguous index.
+    auto a_ip = [&](int u, int& i, int& p) {
+        const int q = tid + u * 256;
+        if (TA) { i = q % TILE; p = q / TILE; } else { p = q % FBK; i = q / FBK; }
+    };
+    auto b_pj = [&](int u, int& p, int& j) {
+        const int q = tid + u * 256;
+        if (TB) { p = q % FBK; j = q / FBK; } else { j = q % TILE; p = q / TILE; }
+    };
     for (int64_t b = blockIdx.y; b < a.batch; b += gridDim.y) {
         const float* A = reinterpret_cast<const float*>(a.A) + b * a.sa;
         const float* B = reinterpret_cast<const float*>(a.B) + b * a.sb;
-        float acc[4][4] = {};
-        for (int64_t k0 = 0; k0 < a.k; k0 += FBK) {
-            __syncthreads();
+        float va[LD], vb[LD];
+        auto fetch = [&](int64_t k0) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int q = tid + u * 256;
-                // A tile element (i, p): consecutive threads walk the stored-contiguous index.
-                int i, p;
-                if (TA) { i = q & 63; p = q >> 6; } else { p = q & 15; i = q >> 4; }
+            for (int u = 0; u < LD; ++u) {
+                int i, p, j, pb;
+                a_ip(u, i, p);
                 const int64_t gi = m0 + i, gp = k0 + p;
-                As[p][i] = (gi < a.m && gp < a.k) ? A[TA ? gp * a.lda + gi : gi * a.lda + gp] : 0.f;
-                int j, pb;
-                if (TB) { pb = q & 15; j = q >> 4; } else { j = q & 63; pb = q >> 6; }
+                va[u] = (gi < a.m && gp < a.k) ? A[TA ? gp * a.lda + gi : gi * a.lda + gp] : 0.f;
+                b_pj(u, pb, j);
                 const int64_t gj = n0 + j, gpb = k0 + pb;
-                Bs[pb][j] = (gj < a.n && gpb < a.k) ? B[TB ? gj * a.ldb + gpb : gpb * a.ldb + gj] : 0.f;
+                vb[u] = (gj < a.n && gpb < a.k) ? B[TB ? gj * a.ldb + gpb : gpb * a.ldb + gj] : 0.f;
             }
-            __syncthreads();
+        };
+        auto store = [&](int buf) {
+#pragma unroll
+            for (int u = 0; u < LD; ++u) {
+                int i, p, j, pb;
+                a_ip(u, i, p);
+                As[buf][p][i] = va[u];
+                b_pj(u, pb, j);
+                Bs[buf][pb][j] = vb[u];
+            }
+        };
+        float acc[R][R] = {};
+        fetch(0);
+        __syncthreads();  // the previous batch's readers are done with buffer 0
+        store(0);
+        __syncthreads();
+        for (int64_t kt = 0; kt < nk; ++kt) {
+            const int cur = (int)(kt & 1);
+            const bool more = kt + 1 < nk;
+            if (more) fetch((kt + 1) * FBK);
 #pragma unroll
             for (int p = 0; p < FBK; ++p) {
-                float av[4], bv[4];
+                float av[R], bv[R];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) av[r] = As[p][ty * 4 + r];
+                for (int r = 0; r < R; ++r) av[r] = As[cur][p][ty * R + r];
 #pragma unroll
-                for (int c = 0; c < 4; ++c) bv[c] = Bs[p][tx * 4 + c];
+                for (int c = 0; c < R; ++c) bv[c] = Bs[cur][p][tx * R + c];
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
+                for (int r = 0; r < R; ++r)
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) acc[r][c] = __builtin_fmaf(av[r], bv[c], acc[r][c]);
+                    for (int c = 0; c < R; ++c) acc[r][c] = __builtin_fmaf(av[r], bv[c], acc[r][c]);
             }
+            if (more) store(cur ^ 1);
+            __syncthreads();
         }
         float* C = reinterpret_cast<float*>(a.C) + b * a.sc;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int64_t gi = m0 + ty * 4 + r;
+        for (int r = 0; r < R; ++r) {
+            const int64_t gi = m0 + ty * R + r;
             if (gi >= a.m) continue;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int64_t gj = n0 + tx * 4 + c;
+            for (int c = 0; c < R; ++c) {
+                const int64_t gj = n0 + tx * R + c;
                 if (gj < a.n) C[gi * a.ldc + gj] = acc[r][c];
             }
         }
@@ -438,11 +513,12 @@ const void* pick_mfma(bool ta, bool tb, bool vec) {
     return nullptr;
 }
 
+template <int TILE>
 const void* pick_f32(bool ta, bool tb) {
-    if (!ta && !tb) return reinterpret_cast<const void*>(&gemm_f32_fma<false, false>);
-    if (!ta && tb) return reinterpret_cast<const void*>(&gemm_f32_fma<false, true>);
-    if (ta && !tb) return reinterpret_cast<const void*>(&gemm_f32_fma<true, false>);
-    return reinterpret_cast<const void*>(&gemm_f32_fma<true, true>);
+    if (!ta && !tb) return reinterpret_cast<const void*>(&gemm_f32_fma<false, false, TILE>);
+    if (!ta && tb) return reinterpret_cast<const void*>(&gemm_f32_fma<false, true, TILE>);
+    if (ta && !tb) return reinterpret_cast<const void*>(&gemm_f32_fma<true, false, TILE>);
+    return reinterpret_cast<const void*>(&gemm_f32_fma<true, true, TILE>);
 }
 
 }  // namespace
@@ -451,10 +527,13 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, int* kernel) {
     void* args[] = {const_cast<GemmArgs*>(&a)};
     const unsigned gy = (unsigned)(a.batch < 65535 ? a.batch : 65535);
     if (a.dtype == 0) {
-        const int64_t tiles = ((a.m + FBM - 1) / FBM) * ((a.n + FBN - 1) / FBN);
+        // 64 x 64 tiles, or 32 x 32 when that leaves fewer blocks than CUs.
+        const int64_t t64 = ((a.m + 63) / 64) * ((a.n + 63) / 64);
+        const bool small = t64 * a.batch < 256;
+        const int64_t tiles = small ? ((a.m + 31) / 32) * ((a.n + 31) / 32) : t64;
         *kernel = MM_KERNEL_GEMM_F32;
-        return hipLaunchKernel(pick_f32(a.ta, a.tb), dim3((unsigned)tiles, gy), dim3(256), args,
-                               0, s);
+        return hipLaunchKernel(small ? pick_f32<32>(a.ta, a.tb) : pick_f32<64>(a.ta, a.tb),
+                               dim3((unsigned)tiles, gy), dim3(256), args, 0, s);
     }
     const bool vec = aligned16(a.A) && aligned16(a.B) && a.lda % 8 == 0 && a.ldb % 8 == 0 &&
                      a.sa % 8 == 0 && a.sb % 8 == 0;

@@ -69,6 +69,16 @@ def test_lm_head_shape_f32():
     check_gemm(case, what="lm-head")
 
 
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_f32_wide_tiles_ragged(ta, tb):
+    """Enough 64 x 64 tiles for the wide f32 form (smaller problems use 32 x 32),
+    ragged in m, n and k."""
+    _say(f"f32 wide tiles m=1030 n=1100 k=70 ta={ta} tb={tb}")
+    case = wl.random_gemm_case(12, wl.F32, 1, 1030, 1100, 70, ta, tb)
+    rec = check_gemm(case, what="f32 wide")
+    assert rec.kernel == mm.MM_KERNEL_GEMM_F32
+
+
 @pytest.mark.parametrize("dt", DTYPES)
 @pytest.mark.parametrize("ta,tb", LAYOUTS)
 @pytest.mark.parametrize("shape", [(1, 130, 260, 70), (3, 257, 129, 95), (2, 64, 48, 300),
