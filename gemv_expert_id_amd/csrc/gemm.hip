@@ -34,67 +34,158 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// Tile staging, split into a global fetch (into registers, so the next
-// k-tile is in flight while the current one is multiplied) and an LDS store.
+// Tile staging, split into a global fetch (into registers, so later k-tiles
+// are in flight while the current one is multiplied) and an LDS store.
 // A chunk is 8 elements: 8 consecutive k of one row (KCONTIG: element (row, p)
 // at base[row * ld + p]) or 8 consecutive rows at one k (else: base[p * ld +
 // row]); out-of-range elements are zero.
+//
+// VEC (16-byte aligned chunks): one buffer load per chunk, unconditional, over
+// a resource that spans exactly the operand's valid elements, so chunks past
+// the last row (or k) read zero from the range check; the k (or row) tail of a
+// chunk that straddles the edge is masked when the chunk is stored (`nv` keeps
+// the valid count). Nothing touches a loaded value before the store, so the
+// loads of several k-tiles stay in flight together.
 constexpr int GCH = (GBM * GBK / 8) / GThreads;  // chunks per thread per operand
+
+__device__ __forceinline__ u32x4 keep_first(u32x4 v, int64_t nvalid) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const uint32_t lo = 2 * t < nvalid ? 0x0000ffffu : 0u;
+        const uint32_t hi = 2 * t + 1 < nvalid ? 0xffff0000u : 0u;
+        v[t] &= lo | hi;
+    }
+    return v;
+}
 
 template <bool KCONTIG, bool VEC>
 __device__ __forceinline__ void fetch_tile(const uint16_t* __restrict__ base, int64_t ld,
                                            int64_t nrows, int64_t K, int64_t row0, int64_t k0,
-                                           u32x4 (&v)[GCH]) {
+                                           u32x4 (&v)[GCH], int (&nv)[GCH]) {
+    const int tid = threadIdx.x;
+    if constexpr (VEC) {
+        // Valid span: (nrows-1)*ld + K elements (KCONTIG) or (K-1)*ld + nrows.
+        const int64_t span = KCONTIG ? (nrows - 1) * ld + K : (K - 1) * ld + nrows;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(base), (short)0, (int)(span * 2), 0x00020000);
+#pragma unroll
+        for (int u = 0; u < GCH; ++u) {
+            const int q = tid + u * GThreads;
+            int64_t off, nvalid;
+            if constexpr (KCONTIG) {
+                const int row = q >> 2, kc = (q & 3) * 8;
+                off = (row0 + row) * ld + k0 + kc;
+                nvalid = K - (k0 + kc);
+            } else {
+                const int p = q >> 4, rc = (q & 15) * 8;
+                off = (k0 + p) * ld + row0 + rc;
+                nvalid = (k0 + p < K) ? nrows - (row0 + rc) : 0;
+            }
+            // Offsets past the span read zero; clamp so that 32 bits hold them.
+            off = off < span ? off : span;
+            v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                       rs, (int)(off * 2), 0, 0));
+            nv[u] = (int)(nvalid < 0 ? 0 : (nvalid > 8 ? 8 : nvalid));
+        }
+        return;
+    }
+#pragma unroll
+    for (int u = 0; u < GCH; ++u) {
+        const int q = tid + u * GThreads;
+        uint32_t h[8];
+        if constexpr (KCONTIG) {
+            const int row = q >> 2, kc = (q & 3) * 8;
+            const int64_t gr = row0 + row, gk = k0 + kc;
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                h[t] = (gr < nrows && gk + t < K) ? base[gr * ld + gk + t] : 0u;
+        } else {
+            const int p = q >> 4, rc = (q & 15) * 8;
+            const int64_t gk = k0 + p, gr = row0 + rc;
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                h[t] = (gk < K && gr + t < nrows) ? base[gk * ld + gr + t] : 0u;
+        }
+        v[u] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                     h[6] | (h[7] << 16)};
+        nv[u] = 8;
+    }
+}
+
+// Write fetched chunks into LDS as [row][k] (pitch GLDK), zeroing the
+// elements past each chunk's valid count.
+template <bool KCONTIG>
+__device__ __forceinline__ void store_tile(const u32x4 (&v)[GCH], const int (&nv)[GCH],
+                                           uint16_t* __restrict__ lds) {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int u = 0; u < GCH; ++u) {
         const int q = tid + u * GThreads;
+        const u32x4 c = keep_first(v[u], nv[u]);
         if constexpr (KCONTIG) {
             const int row = q >> 2, kc = (q & 3) * 8;
-            const int64_t gr = row0 + row, gk = k0 + kc;
-            if (VEC && gr < nrows && gk + 8 <= K) {
-                v[u] = ld16(base + gr * ld + gk);
-            } else {
-                uint32_t h[8];
-#pragma unroll
-                for (int t = 0; t < 8; ++t)
-                    h[t] = (gr < nrows && gk + t < K) ? base[gr * ld + gk + t] : 0u;
-                v[u] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                             h[6] | (h[7] << 16)};
-            }
+            *reinterpret_cast<u32x4*>(lds + row * GLDK + kc) = c;
         } else {
             const int p = q >> 4, rc = (q & 15) * 8;
-            const int64_t gk = k0 + p, gr = row0 + rc;
-            if (VEC && gk < K && gr + 8 <= nrows) {
-                v[u] = ld16(base + gk * ld + gr);
-            } else {
-                uint32_t h[8];
 #pragma unroll
-                for (int t = 0; t < 8; ++t)
-                    h[t] = (gk < K && gr + t < nrows) ? base[gk * ld + gr + t] : 0u;
-                v[u] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                             h[6] | (h[7] << 16)};
+            for (int t = 0; t < 4; ++t) {
+                lds[(rc + 2 * t) * GLDK + p] = (uint16_t)(c[t] & 0xffffu);
+                lds[(rc + 2 * t + 1) * GLDK + p] = (uint16_t)(c[t] >> 16);
             }
         }
     }
 }
 
-// Write fetched chunks into LDS as [row][k] (pitch GLDK).
-template <bool KCONTIG>
-__device__ __forceinline__ void store_tile(const u32x4 (&v)[GCH], uint16_t* __restrict__ lds) {
-    const int tid = threadIdx.x;
+// Work item of the 128 x 128 kernels: (batch, tile) in an order where each
+// XCD (blockIdx % 8) runs a contiguous run, batch-major, and within a batch
+// groups of GGM tile-rows column-major: blocks resident on one XCD at a time
+// share A and B panels in its L2. `slot` counts this block's items.
+constexpr int GGM = 4;
+
+struct TileItem {
+    int64_t b, m0, n0;
+};
+
+__device__ __forceinline__ bool tile_item(const GemmArgs& a, int64_t slot, TileItem* it) {
+    const int64_t tiles_m = (a.m + GBM - 1) / GBM, tiles_n = (a.n + GBN - 1) / GBN;
+    const int64_t tiles = tiles_m * tiles_n, total = tiles * a.batch;
+    const int64_t per_xcd = (total + 7) / 8;
+    if (slot >= per_xcd) return false;
+    const int64_t t = (int64_t)(blockIdx.x % 8) * per_xcd + slot;
+    if (t >= total) return false;
+    const int64_t r = t % tiles;
+    const int64_t group = r / (GGM * tiles_n);
+    const int64_t first_m = group * GGM;
+    const int64_t gsize = tiles_m - first_m < GGM ? tiles_m - first_m : GGM;
+    it->b = t / tiles;
+    it->m0 = (first_m + (r % (GGM * tiles_n)) % gsize) * GBM;
+    it->n0 = ((r % (GGM * tiles_n)) / gsize) * GBN;
+    return true;
+}
+
+// Epilogue of the 128 x 128 kernels: lane holds C[m = lane%16][n = 4*(lane/16) + q]
+// of each 16 x 16 fragment; rounded to the storage type, masked at the edges.
+template <class T>
+__device__ __forceinline__ void store_c(const GemmArgs& a, int64_t b, int64_t m0, int64_t n0,
+                                        int wm, int wn, int lane, const f32x4 (&acc)[4][4]) {
+    uint16_t* C = reinterpret_cast<uint16_t*>(a.C) + b * a.sc;
 #pragma unroll
-    for (int u = 0; u < GCH; ++u) {
-        const int q = tid + u * GThreads;
-        if constexpr (KCONTIG) {
-            const int row = q >> 2, kc = (q & 3) * 8;
-            *reinterpret_cast<u32x4*>(lds + row * GLDK + kc) = v[u];
-        } else {
-            const int p = q >> 4, rc = (q & 15) * 8;
+    for (int i = 0; i < 4; ++i) {
+        const int64_t gm = m0 + wm * 64 + i * 16 + (lane & 15);
+        if (gm >= a.m) continue;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                lds[(rc + 2 * t) * GLDK + p] = (uint16_t)(v[u][t] & 0xffffu);
-                lds[(rc + 2 * t + 1) * GLDK + p] = (uint16_t)(v[u][t] >> 16);
+        for (int j = 0; j < 4; ++j) {
+            const int64_t gn = n0 + wn * 64 + j * 16 + 4 * (lane >> 4);
+            uint16_t* dst = C + gm * a.ldc + gn;
+            if (gn + 4 <= a.n && (a.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(dst) & 7) == 0) {
+                u32x2 v;
+                v[0] = (uint32_t)narrow(T{}, acc[i][j][0]) | ((uint32_t)narrow(T{}, acc[i][j][1]) << 16);
+                v[1] = (uint32_t)narrow(T{}, acc[i][j][2]) | ((uint32_t)narrow(T{}, acc[i][j][3]) << 16);
+                *reinterpret_cast<u32x2*>(dst) = v;
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (gn + q < a.n) dst[q] = narrow(T{}, acc[i][j][q]);
             }
         }
     }
@@ -110,12 +201,10 @@ __global__ __launch_bounds__(GThreads) void gemm_mfma_generic(GemmArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][GBN * GLDK];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int64_t tiles_n = (a.n + GBN - 1) / GBN;
-    const int64_t tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
-    const int64_t m0 = tm * GBM, n0 = tn * GBN;
     const int64_t nk = (a.k + GBK - 1) / GBK;
-
-    for (int64_t b = blockIdx.y; b < a.batch; b += gridDim.y) {
+    TileItem it;
+    for (int64_t slot = blockIdx.x / 8; tile_item(a, slot, &it); slot += gridDim.x / 8) {
+        const int64_t b = it.b, m0 = it.m0, n0 = it.n0;
         const uint16_t* A = reinterpret_cast<const uint16_t*>(a.A) + b * a.sa;
         const uint16_t* B = reinterpret_cast<const uint16_t*>(a.B) + b * a.sb;
         f32x4 acc[4][4];
@@ -125,18 +214,19 @@ __global__ __launch_bounds__(GThreads) void gemm_mfma_generic(GemmArgs a) {
             for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
         u32x4 va[GCH], vb[GCH];
-        fetch_tile<!TA, VEC>(A, a.lda, a.m, a.k, m0, 0, va);
-        fetch_tile<TB, VEC>(B, a.ldb, a.n, a.k, n0, 0, vb);
-        __syncthreads();  // the previous batch's readers are done with buffer 0
-        store_tile<!TA>(va, As[0]);
-        store_tile<TB>(vb, Bs[0]);
+        int na[GCH], nb[GCH];
+        fetch_tile<!TA, VEC>(A, a.lda, a.m, a.k, m0, 0, va, na);
+        fetch_tile<TB, VEC>(B, a.ldb, a.n, a.k, n0, 0, vb, nb);
+        __syncthreads();  // the previous item's readers are done with buffer 0
+        store_tile<!TA>(va, na, As[0]);
+        store_tile<TB>(vb, nb, Bs[0]);
         __syncthreads();
         for (int64_t kt = 0; kt < nk; ++kt) {
             const int cur = (int)(kt & 1);
             const bool more = kt + 1 < nk;
             if (more) {
-                fetch_tile<!TA, VEC>(A, a.lda, a.m, a.k, m0, (kt + 1) * GBK, va);
-                fetch_tile<TB, VEC>(B, a.ldb, a.n, a.k, n0, (kt + 1) * GBK, vb);
+                fetch_tile<!TA, VEC>(A, a.lda, a.m, a.k, m0, (kt + 1) * GBK, va, na);
+                fetch_tile<TB, VEC>(B, a.ldb, a.n, a.k, n0, (kt + 1) * GBK, vb, nb);
             }
             u32x4 af[4], bf[4];
             const int kofs = (lane >> 4) * 8;
@@ -152,34 +242,73 @@ __global__ __launch_bounds__(GThreads) void gemm_mfma_generic(GemmArgs a) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc[i][j] = mfma16<T>(bf[j], af[i], acc[i][j]);
             if (more) {
-                store_tile<!TA>(va, As[cur ^ 1]);
-                store_tile<TB>(vb, Bs[cur ^ 1]);
+                store_tile<!TA>(va, na, As[cur ^ 1]);
+                store_tile<TB>(vb, nb, Bs[cur ^ 1]);
             }
             __syncthreads();
         }
 
-        uint16_t* C = reinterpret_cast<uint16_t*>(a.C) + b * a.sc;
+        store_c<T>(a, b, m0, n0, wm, wn, lane, acc);
+    }
+}
+
+// Short-K form (k <= 128): every k-tile is fetched up front, so the global
+// latency is paid once, the whole K slab is stored to LDS, and one barrier
+// precedes the (up to) 4 x 16 MFMAs per wave. For shallow products (a batch
+// of small GEMMs) the per-k-tile round trips of the loop above dominate.
+constexpr int GSK = 4;  // k-tiles held
+
+template <class T, bool TA, bool TB, bool VEC>
+__global__ __launch_bounds__(GThreads) void gemm_mfma_shortk(GemmArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t As[GSK][GBM * GLDK];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[GSK][GBN * GLDK];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int nk = (int)((a.k + GBK - 1) / GBK);  // 1 .. GSK
+    TileItem it;
+    for (int64_t slot = blockIdx.x / 8; tile_item(a, slot, &it); slot += gridDim.x / 8) {
+        const int64_t b = it.b, m0 = it.m0, n0 = it.n0;
+        const uint16_t* A = reinterpret_cast<const uint16_t*>(a.A) + b * a.sa;
+        const uint16_t* B = reinterpret_cast<const uint16_t*>(a.B) + b * a.sb;
+        // All GSK k-tiles are fetched and stored (those past k come out zero),
+        // so no load sits under a branch.
+        u32x4 va[GSK][GCH], vb[GSK][GCH];
+        int na[GSK][GCH], nb[GSK][GCH];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t gm = m0 + wm * 64 + i * 16 + (lane & 15);
-            if (gm >= a.m) continue;
+        for (int t = 0; t < GSK; ++t) {
+            fetch_tile<!TA, VEC>(A, a.lda, a.m, a.k, m0, t * GBK, va[t], na[t]);
+            fetch_tile<TB, VEC>(B, a.ldb, a.n, a.k, n0, t * GBK, vb[t], nb[t]);
+        }
+        __syncthreads();  // the previous item's readers are done
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t gn = n0 + wn * 64 + j * 16 + 4 * (lane >> 4);
-                uint16_t* dst = C + gm * a.ldc + gn;
-                if (gn + 4 <= a.n && (a.ldc & 3) == 0 &&
-                    (reinterpret_cast<uintptr_t>(dst) & 7) == 0) {
-                    u32x2 v;
-                    v[0] = (uint32_t)narrow(T{}, acc[i][j][0]) | ((uint32_t)narrow(T{}, acc[i][j][1]) << 16);
-                    v[1] = (uint32_t)narrow(T{}, acc[i][j][2]) | ((uint32_t)narrow(T{}, acc[i][j][3]) << 16);
-                    *reinterpret_cast<u32x2*>(dst) = v;
-                } else {
+        for (int t = 0; t < GSK; ++t) {
+            store_tile<!TA>(va[t], na[t], As[t]);
+            store_tile<TB>(vb[t], nb[t], Bs[t]);
+        }
+        __syncthreads();
+        f32x4 acc[4][4];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        if (gn + q < a.n) dst[q] = narrow(T{}, acc[i][j][q]);
-                }
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int kofs = (lane >> 4) * 8;
+#pragma unroll
+        for (int t = 0; t < GSK; ++t) {
+            if (t < nk) {
+                u32x4 af[4], bf[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    af[i] = *reinterpret_cast<const u32x4*>(&As[t][(wm * 64 + i * 16 + (lane & 15)) * GLDK + kofs]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    bf[j] = *reinterpret_cast<const u32x4*>(&Bs[t][(wn * 64 + j * 16 + (lane & 15)) * GLDK + kofs]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[i][j] = mfma16<T>(bf[j], af[i], acc[i][j]);
             }
         }
+        store_c<T>(a, b, m0, n0, wm, wn, lane, acc);
     }
 }
 
@@ -461,7 +590,7 @@ __global__ __launch_bounds__(256) void gemm_f32_fma(GemmArgs a) {
         };
         float acc[R][R] = {};
         fetch(0);
-        __syncthreads();  // the previous batch's readers are done with buffer 0
+        __syncthreads();  // the previous item's readers are done with buffer 0
         store(0);
         __syncthreads();
         for (int64_t kt = 0; kt < nk; ++kt) {
@@ -500,11 +629,15 @@ __global__ __launch_bounds__(256) void gemm_f32_fma(GemmArgs a) {
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 template <class T>
-const void* pick_mfma(bool ta, bool tb, bool vec) {
-#define MM_PICK(TA_, TB_)                                                                    \
-    if (ta == TA_ && tb == TB_)                                                              \
-        return vec ? reinterpret_cast<const void*>(&gemm_mfma_generic<T, TA_, TB_, true>)   \
-                   : reinterpret_cast<const void*>(&gemm_mfma_generic<T, TA_, TB_, false>);
+const void* pick_mfma(bool ta, bool tb, bool vec, bool shortk) {
+#define MM_PICK(TA_, TB_)                                                                     \
+    if (ta == TA_ && tb == TB_) {                                                             \
+        if (shortk)                                                                           \
+            return vec ? reinterpret_cast<const void*>(&gemm_mfma_shortk<T, TA_, TB_, true>)  \
+                       : reinterpret_cast<const void*>(&gemm_mfma_shortk<T, TA_, TB_, false>); \
+        return vec ? reinterpret_cast<const void*>(&gemm_mfma_generic<T, TA_, TB_, true>)     \
+                   : reinterpret_cast<const void*>(&gemm_mfma_generic<T, TA_, TB_, false>);   \
+    }
     MM_PICK(false, false)
     MM_PICK(false, true)
     MM_PICK(true, false)
@@ -535,8 +668,11 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, int* kernel) {
         return hipLaunchKernel(small ? pick_f32<32>(a.ta, a.tb) : pick_f32<64>(a.ta, a.tb),
                                dim3((unsigned)tiles, gy), dim3(256), args, 0, s);
     }
+    // 16-byte chunks; one batch's operand spans below 2 GiB (buffer offsets).
+    const int64_t span_a = a.ta ? (a.k - 1) * a.lda + a.m : (a.m - 1) * a.lda + a.k;
+    const int64_t span_b = a.tb ? (a.n - 1) * a.ldb + a.k : (a.k - 1) * a.ldb + a.n;
     const bool vec = aligned16(a.A) && aligned16(a.B) && a.lda % 8 == 0 && a.ldb % 8 == 0 &&
-                     a.sa % 8 == 0 && a.sb % 8 == 0;
+                     a.sa % 8 == 0 && a.sb % 8 == 0 && span_a < (1ll << 30) && span_b < (1ll << 30);
     const int64_t big_tiles = (a.m / LBM) * (a.n / LBN);
     if (vec && !a.ta && a.tb && a.m % LBM == 0 && a.n % LBN == 0 &&
         a.k % (LSTAGES * LBK) == 0 && a.k >= 2 * LSTAGES * LBK && big_tiles * a.batch >= 512 &&
@@ -549,10 +685,14 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, int* kernel) {
         *kernel = MM_KERNEL_GEMM_LARGE;
         return hipLaunchKernel(fn, dim3(grid, gy), dim3(LThreads), args, kLargeLds, s);
     }
-    const int64_t tiles = ((a.m + GBM - 1) / GBM) * ((a.n + GBN - 1) / GBN);
-    const void* fn = a.dtype == 1 ? pick_mfma<TF16>(a.ta, a.tb, vec) : pick_mfma<TBF16>(a.ta, a.tb, vec);
+    const int64_t total = ((a.m + GBM - 1) / GBM) * ((a.n + GBN - 1) / GBN) * a.batch;
+    int64_t per_xcd = (total + 7) / 8;
+    if (per_xcd > (1 << 24)) per_xcd = 1 << 24;  // blocks then loop over their items
+    const bool shortk = a.k <= GSK * GBK;
+    const void* fn = a.dtype == 1 ? pick_mfma<TF16>(a.ta, a.tb, vec, shortk)
+                                  : pick_mfma<TBF16>(a.ta, a.tb, vec, shortk);
     *kernel = MM_KERNEL_GEMM_TILED;
-    return hipLaunchKernel(fn, dim3((unsigned)tiles, gy), dim3(GThreads), args, 0, s);
+    return hipLaunchKernel(fn, dim3((unsigned)(8 * per_xcd)), dim3(GThreads), args, 0, s);
 }
 
 }  // namespace mmk
