@@ -365,7 +365,7 @@ __global__ __launch_bounds__(kMapMaxWaves * kWave) void id_map(IdArgs a) {
 // Rebuild the m-tile list from the counts: tile_start[e] = sum over e' < e of
 // ceil(counts[e'] / BM). Returns the total tile count. Uses s_start[E + 1].
 template <int BM, int WAVES = kWaves>
-__device__ uint32_t build_schedule(const IdArgs& a, uint32_t* s_start, uint32_t* s_part) {
+__device__ __forceinline__ uint32_t build_schedule(const IdArgs& a, uint32_t* s_start, uint32_t* s_part) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const uint32_t E = a.n_experts;
     // Each thread sums EPT consecutive experts (E <= 1024 = EPT * threads).
@@ -741,6 +741,285 @@ __global__ __launch_bounds__(GW * kWave, 1) void id_grouped_bf16(IdArgs a, uint3
 }
 
 // ---------------------------------------------------------------------------
+// Grouped pass, bf16 weights, pipelined form (k % 128 == 0, aligned operands,
+// input and one expert below 2 GiB).
+//
+// Block = 4 waves, one per SIMD (each wave has the whole register file; the
+// accumulators of up to 8 row groups x DF = 6 output fragments of 16 x 16 sit
+// in AGPRs). Tile = (expert, up to 128 routed rows, bn <= 384 outputs); the
+// host sizes bn so that the tile count is close to the CU count. Per K step
+// of 32 (four LDS stages, step kt in stage kt % 4):
+//   X  the gathered f32 activation rows go from global memory straight into
+//      LDS (buffer_load ... lds; each lane fetches the 16-byte chunk that
+//      belongs at its LDS slot: rows of 8 chunks, chunk c of row r at slot
+//      c ^ ((r >> 1) & 7), so the fragment reads of 16 rows hit distinct
+//      banks), three steps ahead;
+//   W  each wave's fragments (16 rows x 64 bytes per 16-byte lane load) go
+//      to registers three steps ahead, four buffers rotating by name;
+//   MFMA per row group, two 16-byte LDS reads give 8 floats that are split
+//      in registers into bf16 hi = rne(x) and lo = rne(x - hi), then
+//      v_mfma_f32_16x16x32_bf16 with W.hi and W.lo for every fragment.
+// Each step opens with one wait and one barrier. Loads complete in issue
+// order and a step's activations are issued just before its weights, so the
+// wait covers this wave's DMA for step kt; after the barrier every wave's DMA
+// for kt has landed and stage (kt - 1) % 4 is free for step kt + 3. The live
+// row-group count is a template constant, so each step is straight-line code
+// with a fixed number of loads.
+// ---------------------------------------------------------------------------
+constexpr int DW = 4;               // waves per block
+constexpr int DF = 6;               // 16-output fragments per wave
+constexpr int DMAXBN = DW * DF * 16;
+constexpr int DQM = 128;            // routed rows per tile
+constexpr int DBK = 32;             // K step
+constexpr int DST = 4;              // LDS stages = weight register buffers
+constexpr int DLA = DST - 1;        // steps fetched ahead
+constexpr int DSTAGE = DQM * DBK;   // floats per stage
+
+// s_waitcnt immediate: vmcnt <= n, lgkmcnt and expcnt untouched.
+constexpr int dwait_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+#define MM_LDSP(p) ((__attribute__((address_space(3))) void*)(p))
+
+struct DTile {
+    const uint32_t* rows;  // routed row of each tile row (0xffffffff: none)
+    const uint64_t* xoff;  // activation byte offset of each tile row
+    float* xs[DST];        // LDS stages [DQM][DBK], each its own array
+    uint32_t cnt;          // live rows
+    int64_t tile_n0, tile_n1;
+    int nf_live;           // live fragments of this wave
+    int wave, lane;
+    const char* W;         // expert base
+};
+
+template <int... I, class F>
+__device__ __forceinline__ void dstatic_for(std::integer_sequence<int, I...>, F&& f) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+
+template <int NMF>
+__device__ __attribute__((always_inline)) void grouped_dma_body(const IdArgs& a, const DTile& t) {
+    constexpr int NROW = NMF * 16;                  // LDS rows in use
+    constexpr int DPW = (NROW / 8 + DW - 1) / DW;   // DMA instructions per wave per step
+    constexpr int LPS = DPW + DF;                   // loads per wave per step
+    const int lane = t.lane, wave = t.wave;
+    const int64_t nk = a.k / DBK;                   // a multiple of DST
+    static_assert(DLA * (DF + (NROW / 8 + DW - 1) / DW) <= 63, "loads in flight exceed vmcnt");
+    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(a.X), (short)0, 0x7fffffff, 0x00020000);
+    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(t.W), (short)0, (int)(a.n * a.k * 2), 0x00020000);
+
+    // DMA: instruction d of this wave fills LDS rows r0 .. r0 + 7 with
+    // r0 = 8 * min(wave * DPW + d, NROW / 8 - 1) (a repeated instruction
+    // rewrites identical data); lane -> row r0 + lane/8, slot lane%8.
+    int xvo[DPW];
+    int xr0[DPW];
+#pragma unroll
+    for (int d = 0; d < DPW; ++d) {
+        int ins = wave * DPW + d;
+        ins = ins < NROW / 8 ? ins : NROW / 8 - 1;
+        xr0[d] = 8 * ins;
+        const int row = 8 * ins + lane / 8;
+        const bool live = (uint32_t)row < t.cnt && t.rows[row] != 0xffffffffu;
+        const uint64_t off = live ? t.xoff[row] : t.xoff[t.cnt - 1];
+        xvo[d] = (int)off + (((lane & 7) ^ ((row >> 1) & 7)) * 16);
+    }
+    // Stages are separate LDS arrays picked by a compile-time index: when the
+    // compiler cannot tell a DMA target from the stage being read, it waits
+    // for every outstanding DMA before each LDS read.
+    auto dma_x = [&](int64_t kt, auto STG) {
+        float* st = t.xs[decltype(STG)::value];
+#pragma unroll
+        for (int d = 0; d < DPW; ++d)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, MM_LDSP(st + xr0[d] * DBK), 16, xvo[d],
+                                                     (int)(kt * DBK * 4), 0, 0);
+    };
+    // Weight fragment j: lane -> output column, k chunk (lane/16)*8 of the step.
+    int wvo[DF];
+#pragma unroll
+    for (int j = 0; j < DF; ++j) {
+        int64_t col = t.tile_n0 + (int64_t)(wave + DW * j) * 16 + (lane & 15);
+        col = col < t.tile_n1 ? col : t.tile_n1 - 1;
+        wvo[j] = (int)((col * a.k + (lane >> 4) * 8) * 2);
+    }
+    auto load_w = [&](int64_t kt, u32x4 (&w)[DF]) {
+#pragma unroll
+        for (int j = 0; j < DF; ++j)
+            w[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                       wrs, wvo[j], (int)(kt * DBK * 2), 0));
+    };
+
+    f32x4 acc[NMF][DF];
+#pragma unroll
+    for (int i = 0; i < NMF; ++i)
+#pragma unroll
+        for (int j = 0; j < DF; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Activation fragment of row group mf: lane -> row mf*16 + lane%16,
+    // floats 8*(lane/16) .. +8 (chunks 2q, 2q+1 at their swizzled slots).
+    const int frow = lane & 15, fq = lane >> 4;
+    auto compute = [&](auto STG, const u32x4 (&wc)[DF]) {
+        const float* st = t.xs[decltype(STG)::value];
+        // All row groups are read and split first; then the hi products of
+        // every (row group, fragment) pair, then the lo products, so the two
+        // updates of one accumulator are NMF * DF MFMAs apart.
+        u32x4 xh[NMF], xl[NMF];
+#pragma unroll
+        for (int mf = 0; mf < NMF; ++mf) {
+            const int row = mf * 16 + frow;
+            const int sw = (row >> 1) & 7;
+            const f32x4 x0 = *reinterpret_cast<const f32x4*>(st + row * DBK + (((2 * fq) ^ sw) << 2));
+            const f32x4 x1 = *reinterpret_cast<const f32x4*>(st + row * DBK + (((2 * fq + 1) ^ sw) << 2));
+            xh[mf][0] = cvt_pk_bf16(x0[0], x0[1]);
+            xh[mf][1] = cvt_pk_bf16(x0[2], x0[3]);
+            xh[mf][2] = cvt_pk_bf16(x1[0], x1[1]);
+            xh[mf][3] = cvt_pk_bf16(x1[2], x1[3]);
+            xl[mf][0] = cvt_pk_bf16(x0[0] - __uint_as_float(xh[mf][0] << 16), x0[1] - __uint_as_float(xh[mf][0] & 0xffff0000u));
+            xl[mf][1] = cvt_pk_bf16(x0[2] - __uint_as_float(xh[mf][1] << 16), x0[3] - __uint_as_float(xh[mf][1] & 0xffff0000u));
+            xl[mf][2] = cvt_pk_bf16(x1[0] - __uint_as_float(xh[mf][2] << 16), x1[1] - __uint_as_float(xh[mf][2] & 0xffff0000u));
+            xl[mf][3] = cvt_pk_bf16(x1[2] - __uint_as_float(xh[mf][3] << 16), x1[3] - __uint_as_float(xh[mf][3] & 0xffff0000u));
+        }
+        // Every fragment slot is computed: a wave's dead slots read a clamped,
+        // valid column and are never stored.
+#pragma unroll
+        for (int mf = 0; mf < NMF; ++mf)
+#pragma unroll
+            for (int j = 0; j < DF; ++j)
+                acc[mf][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, wc[j]), __builtin_bit_cast(bf16x8, xh[mf]), acc[mf][j], 0, 0, 0);
+#pragma unroll
+        for (int mf = 0; mf < NMF; ++mf)
+#pragma unroll
+            for (int j = 0; j < DF; ++j)
+                acc[mf][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, wc[j]), __builtin_bit_cast(bf16x8, xl[mf]), acc[mf][j], 0, 0, 0);
+    };
+    // Step kt: wait until this wave's X(kt) DMA is done (AHEAD: the loads of
+    // that many later steps may stay in flight behind W(kt)), barrier, issue
+    // step kt + DLA into the buffer step kt - 1 used, multiply.
+    u32x4 wb[DST][DF];
+    // Step kt = kt0 + S (kt0 a multiple of DST, so stage S): S_ carries S.
+    auto step = [&](auto AHEAD, auto LOAD, auto S_, int64_t kt, const u32x4 (&wc)[DF],
+                    u32x4 (&wf)[DF]) {
+        constexpr int S = decltype(S_)::value;
+        __builtin_amdgcn_s_waitcnt(dwait_vm(DF + decltype(AHEAD)::value * LPS));
+        __builtin_amdgcn_s_barrier();
+        if constexpr (decltype(LOAD)::value) {
+            dma_x(kt + DLA, std::integral_constant<int, (S + DLA) % DST>{});
+            load_w(kt + DLA, wf);
+        }
+        compute(S_, wc);
+    };
+    dstatic_for(std::make_integer_sequence<int, DLA>{}, [&](auto S_) {
+        constexpr int s = decltype(S_)::value;
+        dma_x(s, S_);
+        load_w(s, wb[s]);
+    });
+    int64_t kt = 0;
+    for (; kt + DST < nk; kt += DST) {
+        dstatic_for(std::make_integer_sequence<int, DST>{}, [&](auto S_) {
+            constexpr int s = decltype(S_)::value;
+            step(std::integral_constant<int, DLA - 1>{}, std::integral_constant<bool, true>{}, S_,
+                 kt + s, wb[s], wb[(s + DLA) % DST]);
+        });
+    }
+    // Last DST steps: only step kt + DLA remains to be fetched (at s = 0).
+    dstatic_for(std::make_integer_sequence<int, DST>{}, [&](auto S_) {
+        constexpr int s = decltype(S_)::value;
+        constexpr int ahead = (DST - 1 - s) < (DLA - 1) ? (DST - 1 - s) : (DLA - 1);
+        step(std::integral_constant<int, ahead>{}, std::integral_constant<bool, s == 0>{}, S_,
+             kt + s, wb[s], wb[(s + DLA) % DST]);
+    });
+
+    // Lane holds out[row = mf*16 + lane%16][n = fragment base + 4*(lane/16) + q].
+#pragma unroll
+    for (int mf = 0; mf < NMF; ++mf) {
+        const int row = mf * 16 + frow;
+        if ((uint32_t)row >= t.cnt) continue;
+        const uint32_t r = t.rows[row];
+        if (r == 0xffffffffu) continue;
+        float* dst_row = a.out + (uint64_t)r * a.n;
+#pragma unroll
+        for (int j = 0; j < DF; ++j) {
+            if (j >= t.nf_live) continue;
+            const int64_t col = t.tile_n0 + (int64_t)(wave + DW * j) * 16 + 4 * fq;
+            float* dst = dst_row + col;
+            if (col + 4 <= t.tile_n1 && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+                *reinterpret_cast<f32x4*>(dst) = acc[mf][j];
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (col + q < t.tile_n1) dst[q] = acc[mf][j][q];
+            }
+        }
+    }
+}
+#undef MM_LDSP
+
+__global__ __launch_bounds__(DW * kWave, 1) void id_grouped_dma(IdArgs a, uint32_t bn) {
+    __shared__ uint32_t s_start[MM_GROUPED_MAX_E + 1];
+    __shared__ uint32_t s_part[DW];
+    __shared__ uint32_t s_rows[DQM];
+    __shared__ uint64_t s_xoff[DQM];
+    __shared__ __attribute__((aligned(1024))) float Xs0[DSTAGE], Xs1[DSTAGE], Xs2[DSTAGE],
+        Xs3[DSTAGE];
+    static_assert(DST == 4, "one LDS array per stage");
+
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const uint32_t n_tiles = (a.n + bn - 1) / bn;
+    uint32_t ti, nt;
+    block_to_tile(n_tiles, &ti, &nt);
+    const uint32_t T = build_schedule<DQM, DW>(a, s_start, s_part);
+    if (ti >= T) return;
+    const uint32_t e = find_expert(s_start, a.n_experts, ti);
+    uint32_t c = a.counts[e];
+    c = c < a.m ? c : a.m;
+    const uint32_t row_begin = (ti - s_start[e]) * DQM;
+    const uint32_t cnt = c - row_begin < (uint32_t)DQM ? c - row_begin : (uint32_t)DQM;
+    const uint64_t total = (uint64_t)a.m * a.top_k;
+    if (tid < DQM) {
+        uint32_t r = 0xffffffffu;
+        uint64_t off = 0;
+        if ((uint32_t)tid < cnt) {
+            r = a.routed_rows[(uint64_t)e * a.m + row_begin + tid];
+            if (r < total) {
+                const uint64_t tk = r / a.top_k, sl = r % a.top_k;
+                off = tk * a.x_tok_stride_bytes + sl * a.x_slot_stride_bytes;
+            } else {
+                r = 0xffffffffu;
+            }
+        }
+        s_rows[tid] = r;
+        s_xoff[tid] = off;
+    }
+    __syncthreads();
+
+    DTile t;
+    t.rows = s_rows;
+    t.xoff = s_xoff;
+    t.xs[0] = Xs0; t.xs[1] = Xs1; t.xs[2] = Xs2; t.xs[3] = Xs3;
+    t.cnt = cnt;
+    t.tile_n0 = (int64_t)nt * bn;
+    t.tile_n1 = t.tile_n0 + bn < a.n ? t.tile_n0 + bn : a.n;
+    const int nfr = (int)((t.tile_n1 - t.tile_n0 + 15) / 16);
+    t.nf_live = nfr > wave ? (nfr - wave + DW - 1) / DW : 0;
+    t.wave = wave;
+    t.lane = lane;
+    t.W = reinterpret_cast<const char*>(a.W) + (uint64_t)e * a.expert_stride_bytes;
+    switch ((cnt + 15) / 16) {
+        case 1: grouped_dma_body<1>(a, t); break;
+        case 2: grouped_dma_body<2>(a, t); break;
+        case 3: grouped_dma_body<3>(a, t); break;
+        case 4: grouped_dma_body<4>(a, t); break;
+        case 5: grouped_dma_body<5>(a, t); break;
+        case 6: grouped_dma_body<6>(a, t); break;
+        case 7: grouped_dma_body<7>(a, t); break;
+        default: grouped_dma_body<8>(a, t); break;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Grouped pass, any weight dtype: LDS-tiled FMA (64 rows x 64 outputs).
 // ---------------------------------------------------------------------------
 constexpr int FBM = 64, FBN = 64, FBK = 16;
@@ -898,13 +1177,15 @@ hipError_t launch_id_grouped(const IdArgs& a, hipStream_t s, int* kernel) {
                          aligned16(a.X) && a.x_tok_stride_bytes % 16 == 0 &&
                          a.x_slot_stride_bytes % 16 == 0;
         const uint64_t in_rows = a.layout == 0 ? a.m : (uint64_t)a.m * a.top_k;
-        const bool fast = vec && a.k % (4 * QBK) == 0 && in_rows * a.k * 4 < (1ull << 31) &&
+        const bool fast = vec && a.k % (DST * DBK) == 0 && in_rows * a.k * 4 < (1ull << 31) &&
                           (uint64_t)a.n * a.k * 2 < (1ull << 31);
-        const uint64_t g = grid_for(a, QBM, bn);
         *kernel = MM_KERNEL_ID_GROUPED_MFMA;
-        const void* fn = fast ? (const void*)&id_grouped_bf16<true, true>
-                       : vec  ? (const void*)&id_grouped_bf16<true, false>
-                              : (const void*)&id_grouped_bf16<false, false>;
+        if (fast)
+            return hipLaunchKernel((const void*)&id_grouped_dma, dim3((unsigned)grid_for(a, DQM, bn)),
+                                   dim3(DW * kWave), args, 0, s);
+        const uint64_t g = grid_for(a, QBM, bn);
+        const void* fn = vec ? (const void*)&id_grouped_bf16<true, false>
+                             : (const void*)&id_grouped_bf16<false, false>;
         return hipLaunchKernel(fn, dim3((unsigned)g), dim3(GW * kWave), args, 0, s);
     }
     void* args[] = {const_cast<IdArgs*>(&a)};
