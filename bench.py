@@ -193,7 +193,7 @@ def main():
         else:
             achieved, peak, unit = tflops, F32_PEAK_TFLOPS, "TFLOP/s"
         results[name] = {
-            "route": "gemv" if rec.route == mm.MM_ROUTE_GEMV else "gemm",
+            "route": {mm.MM_ROUTE_GEMV: "gemv", mm.MM_ROUTE_GEMV_WIDE: "gemv_wide"}.get(rec.route, "gemm"),
             "us_per_call": ms * 1e3, "calls_timed": n, "rotations": n_rot,
             "tflops": tflops, "alg_gbs": gbs, "alg_bytes": alg_bytes, "flops": case.flops,
             "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
@@ -207,6 +207,9 @@ def main():
     if want("gemv_f16_decode"):
         case = wl.gemv_f16_decode()
         gemm_workload("gemv_f16_decode", case, "hbm", case.B.nbytes + case.A.nbytes + 11008 * 2)
+    if want("gemv_f16_skinny"):
+        case = wl.gemv_f16_skinny()
+        gemm_workload("gemv_f16_skinny", case, "hbm", case.B.nbytes + case.A.nbytes + 8 * 11008 * 2)
     if want("gemm_f32_128"):
         case = wl.gemm_f32_128()
         gemm_workload("gemm_f32_128", case, "f32", 3 * 128 * 128 * 4)

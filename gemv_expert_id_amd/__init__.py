@@ -22,10 +22,12 @@ LIB_PATH = os.path.join(HERE, "libmm.so")
 MM_F32, MM_F16, MM_BF16 = 0, 1, 2
 MM_ROUTE_GEMV, MM_ROUTE_GEMM, MM_ROUTE_ID_DIRECT = 0, 1, 2
 MM_ROUTE_ID_MAP, MM_ROUTE_ID_GROUPED, MM_ROUTE_ID_PREFILL = 3, 4, 5
+MM_ROUTE_GEMV_WIDE = 6
 # mm_kernel: kernel family reported in receipts
 (MM_KERNEL_GEMV_ROWS, MM_KERNEL_GEMV_ROWS_ELEM, MM_KERNEL_GEMV_COLS, MM_KERNEL_GEMM_TILED,
  MM_KERNEL_GEMM_LARGE, MM_KERNEL_GEMM_F32, MM_KERNEL_ID_DIRECT_FAST, MM_KERNEL_ID_DIRECT,
- MM_KERNEL_ID_MAP, MM_KERNEL_ID_GROUPED_MFMA, MM_KERNEL_ID_GROUPED_FMA) = range(11)
+ MM_KERNEL_ID_MAP, MM_KERNEL_ID_GROUPED_MFMA, MM_KERNEL_ID_GROUPED_FMA,
+ MM_KERNEL_GEMV_WIDE) = range(12)
 MM_ID_SCHEMA_VERSION = 4
 MM_ID_GROUPED_MAX_EXPERTS = 1024
 

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libmm.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["gemv.hip", "gemm.hip", "mmid.hip", "abi.cpp"]
+SOURCES = ["gemv.hip", "skinny.hip", "gemm.hip", "mmid.hip", "abi.cpp"]
 ARCH = "gfx950"
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

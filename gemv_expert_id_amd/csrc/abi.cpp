@@ -252,6 +252,55 @@ mm_status run_gemv(const GemmPlan& p, hipStream_t s, mm_receipt* r) {
     return ok();
 }
 
+// tract-metal `gemv_wide_config`: a skinny product (2..16 rows on one side)
+// against a matrix with rows along k streams that matrix once for all rows.
+// Both operands must be stored with rows along k (trans_a = 0, trans_b = 1)
+// and allow 16-byte chunks that never straddle a row end.
+bool skinny_args(const GemmPlan& p, mmk::SkinnyArgs* g) {
+    if (p.ta || !p.tb) return false;
+    const bool x_is_a = p.m >= 2 && p.m <= 16 && p.n >= 2;
+    const bool x_is_b = !x_is_a && p.n >= 2 && p.n <= 16 && p.m >= 2;
+    if (!x_is_a && !x_is_b) return false;
+    const int64_t ch = 16 / (int64_t)elt_size(p.dt);
+    const auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
+    if (p.k % ch || p.lda % ch || p.ldb % ch || p.sa % ch || p.sb % ch || !al16(p.a) || !al16(p.b))
+        return false;
+    *g = mmk::SkinnyArgs{};
+    g->dtype = p.dt;
+    g->k = p.k;
+    g->batch = p.batch;
+    g->out = p.c;
+    g->so = p.sc;
+    if (x_is_a) {  // C[i][j] = X(i) . W(j): W = B [n,k], X = A [m,k]
+        g->W = p.b; g->ldw = p.ldb; g->sw = p.sb; g->nw = p.n;
+        g->X = p.a; g->ldx = p.lda; g->sx = p.sa; g->nx = p.m;
+        g->out_sx = p.ldc; g->out_sw = 1;
+    } else {       // C[i][j] = W(i) . X(j): W = A [m,k], X = B [n,k]
+        g->W = p.a; g->ldw = p.lda; g->sw = p.sa; g->nw = p.m;
+        g->X = p.b; g->ldx = p.ldb; g->sx = p.sb; g->nx = p.n;
+        g->out_sx = 1; g->out_sw = p.ldc;
+    }
+    // One batch's extents are addressed with 32-bit offsets.
+    const uint64_t es = elt_size(p.dt);
+    const uint64_t wb = ((uint64_t)(g->nw - 1) * g->ldw + p.k) * es;
+    const uint64_t xb = ((uint64_t)(g->nx - 1) * g->ldx + p.k) * es;
+    if (wb >= (1ull << 31) || xb >= (1ull << 31)) return false;
+    g->w_bytes = (int64_t)wb;
+    g->x_bytes = (int64_t)xb;
+    return true;
+}
+
+mm_status run_skinny(const mmk::SkinnyArgs& g, int dt, hipStream_t s, mm_receipt* r) {
+    mm_status st = resolve("gemv_wide");
+    if (st != MM_OK) return st;
+    ++g_launches;
+    int kernel = -1;
+    st = finish(mmk::launch_gemv_wide(g, s, &kernel), s, "gemv_wide");
+    if (st != MM_OK) return st;
+    set_receipt(r, MM_ROUTE_GEMV_WIDE, (uint32_t)dt, 1, kernel);
+    return ok();
+}
+
 mm_status run_gemm(const GemmPlan& p, hipStream_t s, mm_receipt* r) {
     mm_status st = resolve("gemm");
     if (st != MM_OK) return st;
@@ -426,6 +475,8 @@ mm_status mm_gemm(const mm_gemm_desc* desc, mm_buf a, mm_buf b, mm_buf c, void* 
     mm_status st = plan_gemm(desc, a, b, c, &p);
     if (st != MM_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    mmk::SkinnyArgs g;
+    if (skinny_args(p, &g)) return run_skinny(g, p.dt, s, receipt);
     if (p.m == 1 || p.n == 1) return run_gemv(p, s, receipt);
     return run_gemm(p, s, receipt);
 }

@@ -31,6 +31,22 @@ struct GemvArgs {
 // Launchers enqueue one kernel on `s`; `kernel` receives its mm_kernel code.
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t s, int* kernel);
 
+// Skinny product: out[b][x * out_sx + w * out_sw] = sum_p W[b](w, p) * X[b](x, p)
+// for w < nw, x < nx (nx <= 16); W(w, p) = W[w * ldw + p], X(x, p) = X[x * ldx + p].
+struct SkinnyArgs {
+    const void* W;
+    const void* X;
+    void* out;
+    int64_t nw, nx, k;
+    int64_t ldw, ldx;
+    int64_t out_sx, out_sw;
+    int64_t sw, sx, so;  // batch strides, elements; 0 = shared
+    int64_t batch;
+    int64_t w_bytes, x_bytes;  // extent of one batch's W and X (each below 2^31)
+    int32_t dtype;
+};
+hipError_t launch_gemv_wide(const SkinnyArgs& a, hipStream_t s, int* kernel);
+
 // C[b] = op(A[b]) . op(B[b]); pointers already include the byte offsets.
 struct GemmArgs {
     const void* A;

@@ -74,7 +74,8 @@ typedef enum {
     MM_ROUTE_ID_DIRECT = 2,
     MM_ROUTE_ID_MAP = 3,
     MM_ROUTE_ID_GROUPED = 4,
-    MM_ROUTE_ID_PREFILL = 5 /* map + grouped in one call */
+    MM_ROUTE_ID_PREFILL = 5, /* map + grouped in one call */
+    MM_ROUTE_GEMV_WIDE = 6   /* skinny product: 2..16 rows on one side */
 } mm_route;
 
 /* Kernel family of a launch (reported in receipts; the choice depends on
@@ -90,7 +91,8 @@ typedef enum {
     MM_KERNEL_ID_DIRECT = 7,         /* direct route, general */
     MM_KERNEL_ID_MAP = 8,            /* map pass */
     MM_KERNEL_ID_GROUPED_MFMA = 9,   /* grouped pass, bf16 weights on MFMA */
-    MM_KERNEL_ID_GROUPED_FMA = 10    /* grouped pass, f32 / f16 weights */
+    MM_KERNEL_ID_GROUPED_FMA = 10,   /* grouped pass, f32 / f16 weights */
+    MM_KERNEL_GEMV_WIDE = 11         /* skinny route, one 16 x 16 MFMA fragment per block */
 } mm_kernel;
 
 typedef struct {
@@ -138,9 +140,16 @@ typedef struct {
 } mm_gemm_desc;
 
 /*
- * Dispatch: the GEMV route when m == 1 or n == 1 (the matrix operand is B when
- * n != 1, else A), the tiled MFMA GEMM route otherwise (tract-metal
- * `dispatch_eval`). Errors: INVALID_ARGUMENT (dims, flags, ld, strides),
+ * Dispatch (tract-metal `dispatch_eval`, with `gemv_wide_config` deciding the
+ * skinny case first):
+ *   - skinny route (MM_ROUTE_GEMV_WIDE) when trans_a == 0, trans_b == 1, one
+ *     of m, n is in 2..16 and the other is >= 2, and the 16-byte layout holds:
+ *     k, lda, ldb, stride_a and stride_b multiples of 16 / element size and
+ *     16-byte aligned A and B (after their offsets);
+ *   - the GEMV route when m == 1 or n == 1 (the matrix operand is B when
+ *     n != 1, else A);
+ *   - the tiled MFMA GEMM route otherwise.
+ * All routes compute the same product. Errors: INVALID_ARGUMENT (dims, flags, ld, strides),
  * UNSUPPORTED (dtype), MISALIGNED (ptr + offset not element aligned),
  * BUFFER_TOO_SMALL, OVERLAP (C's range meets A's or B's), DEVICE.
  */

@@ -37,7 +37,7 @@ def _gpu():
     yield
 
 
-from gpu_util import check_gemm  # noqa: E402
+from gpu_util import check_gemm, expected_gemm_route  # noqa: E402
 
 
 # (batch, m, n, k) tuples, both readings of the pages' (b, m, k, n)-or-(b, m, n, k) order.
@@ -58,7 +58,7 @@ def test_page_shapes_f32(shape, ta, tb, order):
     _say(f"page shape {shape} order={order} -> b={b} m={m} n={n} k={k} ta={ta} tb={tb}")
     case = wl.random_gemm_case(7, wl.F32, b, m, n, k, ta, tb)
     rec = check_gemm(case, what=f"{shape}")
-    assert rec.route == (mm.MM_ROUTE_GEMV if (m == 1 or n == 1) else mm.MM_ROUTE_GEMM)
+    assert rec.route == expected_gemm_route(case)
     assert rec.dispatch_count == 1
 
 

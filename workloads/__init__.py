@@ -279,6 +279,17 @@ def gemv_f16_decode() -> GemmCase:
     return make_gemm_case(F16, x, w, False, True)
 
 
+def gemv_f16_skinny() -> GemmCase:
+    """Skinny f16 product (a short batch of decode tokens): x [8, 4096] ~ N(0,1),
+    W [11008, 4096] ~ 0.02 N(0,1) stored [N, K] and used transposed (trans_b),
+    seed 5 (x drawn first). Not one of the five named workloads: it measures
+    the skinny route at the decode GEMV's weight shape."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((1, 8, 4096))
+    w = 0.02 * rng.standard_normal((1, 11008, 4096))
+    return make_gemm_case(F16, x, w, False, True)
+
+
 def gemm_f16_batched() -> GemmCase:
     """Batched strided f16 GEMM C = A.B^T: batch 32, A and B [32, 512, 128],
     entries N(0,1)/sqrt(128), contiguous batch strides, seed 2."""
