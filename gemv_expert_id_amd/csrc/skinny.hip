@@ -10,15 +10,24 @@
 // (X = A) and C = W . X^T (W = A).
 //
 // One block computes one 16 x 16 MFMA fragment: 16 weight rows against all
-// activation rows (padded to 16 by repeating the last one; padded results
-// are never stored; rows past the end repeat the last row the same way). Per contraction step of four 16-byte chunks, lane l
-// loads chunk (l / 16) of weight row l % 16 and of activation row l % 16 and
-// feeds them to one MFMA (f16/bf16: 16x16x32; f32: four 16x16x4, component q
-// of every lane's chunk being contraction slot q for both operands). The
-// four waves take steps w, w + 4, w + 8, ..., so at any moment a block reads
-// 256 contiguous bytes of each of its 16 rows; each wave keeps SD steps in
-// flight. The four partial fragments are summed in a fixed order through LDS.
-// HBM-bound: ~M FLOP per weight byte, far below the MFMA ridge.
+// activation rows (padded to 16 by repeating the last one; padded results are
+// never stored; weight rows past the end repeat the last row the same way).
+// The weight rows stream through a ring of SST LDS stages, each 16 rows x 1 KB:
+// one DMA instruction (buffer_load ... lds) moves 1 KB of one row, so HBM
+// sees whole contiguous row pieces as in the GEMV row form. Lane i of that
+// instruction fetches chunk i ^ row so that, later, the 16 lanes reading one
+// chunk index of 16 different rows hit 16 different bank groups. A stage holds
+// 16 contraction steps of four 16-byte chunks; wave w multiplies steps
+// 4w .. 4w + 3 of every stage: it reads the weight fragment (lane l: row l % 16,
+// chunk 4 * step + l / 16) from LDS and the matching activation fragment,
+// prefetched into registers with the stage's DMA, and issues one MFMA
+// (f16/bf16: 16x16x32; f32: four 16x16x4, component q of every lane's chunk
+// being contraction slot q for both operands). Each stage opens with one
+// wait and one barrier; the stage computed two steps earlier is then free
+// for the next DMA. The four partial fragments are summed in a fixed order
+// through LDS. HBM-bound: about 2 * rows FLOP per weight byte.
+#include <utility>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -28,7 +37,21 @@ namespace {
 
 constexpr int SThreads = 256;
 constexpr int SWaves = SThreads / kWave;
-constexpr int SD = 8;  // steps in flight per wave
+constexpr int SST = 3;             // LDS stages
+constexpr int SROW = 1024;         // bytes of one weight row per stage
+constexpr int SCH = SROW / 16;     // 16-byte chunks of one row per stage
+constexpr int SOPS = 8;            // loads per wave per stage: 4 row pieces + 4 activation chunks
+static_assert(SWaves * 4 == 16 && SCH == 4 * 4 * SWaves, "one fragment, four steps per wave");
+
+// s_waitcnt immediate: vmcnt <= n; lgkmcnt and expcnt untouched.
+constexpr int swait_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+#define MM_LDSP(p) ((__attribute__((address_space(3))) void*)(p))
+
+template <int... I, class F>
+__device__ __forceinline__ void sk_for(std::integer_sequence<int, I...>, F&& f) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
 
 template <class T>
 __device__ __forceinline__ f32x4 frag_mma(u32x4 w, u32x4 x, f32x4 acc) {
@@ -49,58 +72,112 @@ __device__ __forceinline__ f32x4 frag_mma(u32x4 w, u32x4 x, f32x4 acc) {
 
 // Requires k, ldw, ldx and the batch strides to be multiples of Elems16,
 // 16-byte aligned W and X, and each batch's W and X extents below 2 GiB:
-// every 16-byte chunk is then wholly inside a row or wholly past its end, and
-// a chunk that must not contribute is read through an offset past the buffer
-// resource's range, which returns zeros without touching memory.
+// every 16-byte chunk is then wholly inside a row or wholly past its end.
+// Chunks past the end are fetched through an offset beyond the buffer
+// resource's range, which yields zeros without touching memory; weight
+// chunks past the end are also zeroed after the LDS read.
 template <class T>
 __global__ __launch_bounds__(SThreads) void gemv_wide(SkinnyArgs a) {
     using S = typename T::store_t;
     constexpr int CH = T::Elems16;
     constexpr uint32_t kOff = 0x80000000u;  // past every resource range
-    __shared__ f32x4 part[SWaves - 1][kWave];
+    __shared__ __attribute__((aligned(1024))) uint8_t ring0[16 * SROW], ring1[16 * SROW],
+        ring2[16 * SROW];
+    static_assert(SST == 3, "one LDS array per stage");
+    uint8_t* const ring[SST] = {ring0, ring1, ring2};
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int r = lane & 15, g = lane >> 4;
     const int64_t w0 = (int64_t)blockIdx.x * 16;
-    const int64_t wrow = w0 + r < a.nw ? w0 + r : a.nw - 1;
+    const int64_t nch = a.k / CH;               // chunks per row
+    const int64_t nst = (nch + SCH - 1) / SCH;  // stages
+    // DMA rows of this wave: 4 * wave + d.
+    uint32_t dbyte[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const int64_t gr = w0 + 4 * wave + d < a.nw ? w0 + 4 * wave + d : a.nw - 1;
+        dbyte[d] = (uint32_t)(gr * a.ldw * (int64_t)sizeof(S));
+    }
     const int64_t xrow = r < a.nx ? r : a.nx - 1;
-    const int64_t nch = a.k / CH;           // 16-byte chunks per row
-    const int64_t ns = (nch + 3) / 4;       // contraction steps
-    const int64_t mine = ns > wave ? (ns - wave + SWaves - 1) / SWaves : 0;
-    const uint32_t wbyte = (uint32_t)(wrow * a.ldw * (int64_t)sizeof(S));
     const uint32_t xbyte = (uint32_t)(xrow * a.ldx * (int64_t)sizeof(S));
+
     for (int64_t b = blockIdx.y; b < a.batch; b += gridDim.y) {
         const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<S*>(static_cast<const S*>(a.W) + b * a.sw), (short)0, (int)a.w_bytes, 0x00020000);
         const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<S*>(static_cast<const S*>(a.X) + b * a.sx), (short)0, (int)a.x_bytes, 0x00020000);
-        // The i-th step of this wave: lane chunk 4 s + g, zeros when past the
-        // row end or past this wave's steps.
-        auto load = [&](int64_t i, u32x4& wv, u32x4& xv) {
-            const int64_t c = 4 * (wave + (int64_t)SWaves * i) + g;
-            const bool live = i < mine && c < nch;
-            const uint32_t cb = (uint32_t)(c * 16);
-            wv = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                     wrs, live ? wbyte + cb : kOff, 0, 0));
-            xv = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                     xrs, live ? xbyte + cb : kOff, 0, 0));
+        // Stage st into ring slot SLOT: this wave's four row pieces and the
+        // activation chunks of its four steps.
+        auto issue = [&](int64_t st, auto SLOT, u32x4 (&xv)[4]) {
+            uint8_t* base = ring[decltype(SLOT)::value];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const int row = 4 * wave + d;
+                const int64_t c = st * SCH + (lane ^ row);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    wrs, MM_LDSP(base + row * SROW), 16,
+                    c < nch ? dbyte[d] + (uint32_t)(c * 16) : kOff, 0, 0, 0);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t c = st * SCH + 4 * (4 * wave + j) + g;
+                xv[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                            xrs, c < nch ? xbyte + (uint32_t)(c * 16) : kOff, 0, 0));
+            }
         };
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        u32x4 wv[SD], xv[SD];
+        auto compute = [&](int64_t st, auto SLOT, const u32x4 (&xv)[4]) {
+            const uint8_t* base = ring[decltype(SLOT)::value];
 #pragma unroll
-        for (int j = 0; j < SD; ++j) load(j, wv[j], xv[j]);
-        for (int64_t i0 = 0; i0 < mine; i0 += SD) {
-#pragma unroll
-            for (int j = 0; j < SD; ++j) {
-                acc = frag_mma<T>(wv[j], xv[j], acc);
-                load(i0 + j + SD, wv[j], xv[j]);
+            for (int j = 0; j < 4; ++j) {
+                const int cl = 4 * (4 * wave + j) + g;
+                u32x4 wv = *reinterpret_cast<const u32x4*>(base + r * SROW + ((cl ^ r) << 4));
+                if (st * SCH + cl >= nch) wv = u32x4{0u, 0u, 0u, 0u};
+                acc = frag_mma<T>(wv, xv[j], acc);
             }
+        };
+        u32x4 xb[SST][4];
+        sk_for(std::make_integer_sequence<int, SST - 1>{}, [&](auto P) {
+            if (decltype(P)::value < nst) issue(decltype(P)::value, P, xb[decltype(P)::value]);
+        });
+        // Stage st sits in slot st % SST; after its wait and barrier, stage
+        // st + SST - 1 goes into the slot stage st - 1 used. Rounds in which
+        // every such stage exists run without conditions (so the compiler's
+        // own waits stay exact); the last few stages take the checked form.
+        int64_t st0 = 0;
+        for (; st0 + 2 * SST - 2 < nst; st0 += SST) {
+            sk_for(std::make_integer_sequence<int, SST>{}, [&](auto Q) {
+                constexpr int q = decltype(Q)::value;
+                constexpr int nq = (q + SST - 1) % SST;
+                __builtin_amdgcn_s_waitcnt(swait_vm(SOPS * (SST - 2)));
+                __builtin_amdgcn_s_barrier();
+                issue(st0 + q + SST - 1, std::integral_constant<int, nq>{}, xb[nq]);
+                compute(st0 + q, Q, xb[q]);
+            });
         }
-        if (wave > 0) part[wave - 1][lane] = acc;
+        for (; st0 < nst; st0 += SST) {
+            sk_for(std::make_integer_sequence<int, SST>{}, [&](auto Q) {
+                constexpr int q = decltype(Q)::value;
+                const int64_t st = st0 + q;
+                if (st < nst) {
+                    if (nst - 1 - st >= SST - 2)
+                        __builtin_amdgcn_s_waitcnt(swait_vm(SOPS * (SST - 2)));
+                    else
+                        __builtin_amdgcn_s_waitcnt(swait_vm(0));
+                    __builtin_amdgcn_s_barrier();
+                    constexpr int nq = (q + SST - 1) % SST;
+                    if (st + SST - 1 < nst) issue(st + SST - 1, std::integral_constant<int, nq>{}, xb[nq]);
+                    compute(st, Q, xb[q]);
+                }
+            });
+        }
+        __syncthreads();
+        f32x4* part = reinterpret_cast<f32x4*>(ring0);
+        if (wave > 0) part[(wave - 1) * kWave + lane] = acc;
         __syncthreads();
         if (wave == 0) {
 #pragma unroll
-            for (int w = 0; w < SWaves - 1; ++w) acc += part[w][lane];
+            for (int w = 0; w < SWaves - 1; ++w) acc += part[w * kWave + lane];
             // Lane holds out(x_row = lane % 16, w_row = w0 + 4 * (lane / 16) + q).
             if (r < a.nx) {
                 S* o = static_cast<S*>(a.out) + b * a.so + (int64_t)r * a.out_sx;
@@ -114,6 +191,7 @@ __global__ __launch_bounds__(SThreads) void gemv_wide(SkinnyArgs a) {
         __syncthreads();
     }
 }
+#undef MM_LDSP
 
 }  // namespace
 
