@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="time direct launches, no HIP graph")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
+    ap.add_argument("--calibrate-id", action="store_true",
+                    help="only time the expert-ID direct route against map + grouped over a "
+                         "range of token counts (route crossover) and print one JSON line")
     return ap.parse_args()
 
 
@@ -113,6 +116,67 @@ class Timer:
         return t0.elapsed_time(t1) / n, n  # ms per step
 
 
+def calibrate_id(torch, mm, wl, dev, stream, args):
+    """Direct route vs map + grouped route for expert-ID layers of a few shapes,
+    over token counts m: bf16 weights, distinct ids per token (a prefix of a
+    fresh permutation of the experts), shared activations. Weights rotate
+    through enough stacks to defeat the caches, as in the main benchmark."""
+    timer = Timer(torch, stream, True)
+    # (experts, top_k, n, k, weight dtype)
+    layers = [(64, 8, 1408, 2048, wl.BF16), (16, 4, 2048, 2048, wl.BF16),
+              (64, 8, 1408, 2048, wl.F16)]
+    table = []
+    for (E, top_k, n, k, wdt) in layers:
+        rng = np.random.default_rng(11)
+        w = to_dev_bits(torch, dev, wl.to_storage(0.02 * rng.standard_normal(E * n * k), wdt))
+        wbytes = E * n * k * 2
+        n_rot = max(2, math.ceil(ROTATE_BYTES / wbytes))
+        Ws = [w] + [w.clone() for _ in range(n_rot - 1)]
+        wb = [mm.buf(t) for t in Ws]
+        for m in [1, 2, 4, 8, 16, 32, 64, 128, 256, 512]:
+            ids_np = wl.distinct_ids(np.random.default_rng(m), m, top_k, E)
+            x = torch.from_numpy(rng.standard_normal((m, k)).astype(np.float32)).to(dev)
+            ids = torch.from_numpy(ids_np.reshape(-1).view(np.int32)).to(dev)
+            out = torch.empty(m * top_k * n, dtype=torch.float32, device=dev)
+            cnt = torch.empty(E, dtype=torch.int32, device=dev)
+            rr = torch.empty(E * m, dtype=torch.int32, device=dev)
+            pd = mm.id_params(m, n, k, top_k, E, n * k * 2, 0, 0, 0)
+            pg = mm.id_params(m, n, k, top_k, E, n * k * 2, 0, 0, 1)
+            xb, ib, ob, cb, rb = mm.buf(x), mm.buf(ids), mm.buf(out), mm.buf(cnt), mm.buf(rr)
+
+            def direct(i):
+                mm.mm_id_direct(pd, wdt, wb[i], xb, ib, ob, stream=stream)
+
+            def grouped(i):
+                mm.mm_id(pg, wdt, wb[i], xb, ib, ob, cb, rb, stream=stream)
+
+            steps = max(n_rot, 2 * n_rot * max(1, 64 // m))
+            td, _ = timer.time(direct, n_rot, steps, 3)
+            tg, _ = timer.time(grouped, n_rot, steps, 3)
+            used = len(set(int(v) for v in ids_np.reshape(-1)))
+            row = {"experts": E, "top_k": top_k, "n": n, "k": k, "m": m,
+                   "weights": wl.DTYPE_NAMES[wdt],
+                   "rows_per_expert": m * top_k / E, "experts_used": used,
+                   "direct_us": td * 1e3, "grouped_us": tg * 1e3,
+                   "faster": "direct" if td <= tg else "grouped"}
+            table.append(row)
+            log(f"{wl.DTYPE_NAMES[wdt]} E={E:3d} top_k={top_k} n={n} k={k} m={m:4d} "
+                f"rows/expert={m * top_k / E:7.3f} "
+                f"used={used:3d}  direct {td * 1e3:8.2f} us  grouped {tg * 1e3:8.2f} us  "
+                f"-> {row['faster']}")
+            del x, ids, out, cnt, rr
+        del Ws, wb, w
+        torch.cuda.empty_cache()
+    print(json.dumps({"calibration": "matmul_id direct vs map+grouped", "rows": table}))
+
+
+def to_dev_bits(torch, dev, bits):
+    bits = np.ascontiguousarray(bits)
+    view = {np.dtype(np.float32): None, np.dtype(np.uint16): np.int16,
+            np.dtype(np.uint32): np.int32}[bits.dtype]
+    return torch.from_numpy(bits if view is None else bits.view(view)).to(dev)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -142,6 +206,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         log(f"copied {n * 4} bytes x5")
+        return
+
+    if args.calibrate_id:
+        calibrate_id(torch, mm, wl, dev, stream, args)
         return
 
     def to_dev(bits):

@@ -796,7 +796,23 @@ __device__ __forceinline__ void dstatic_for(std::integer_sequence<int, I...>, F&
     (f(std::integral_constant<int, I>{}), ...);
 }
 
-template <int NMF>
+// f16 weight fragment (8 values) -> exact bf16 pair: hi = rne(w), lo = w - hi.
+// w has at most 11 significant bits and hi keeps 8, so w - hi has at most 3
+// and is a bf16 value; both stay in range because bf16 shares f32's exponents.
+__device__ __forceinline__ void split_f16_bf16(u32x4 w, u32x4& hi, u32x4& lo) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float a = widen(TF16{}, (uint16_t)(w[i] & 0xffffu));
+        const float b = widen(TF16{}, (uint16_t)(w[i] >> 16));
+        hi[i] = cvt_pk_bf16(a, b);
+        lo[i] = cvt_pk_bf16(a - __uint_as_float(hi[i] << 16), b - __uint_as_float(hi[i] & 0xffff0000u));
+    }
+}
+
+// WT: TBF16 (W used as stored: two MFMAs, W.x_hi + W.x_lo) or TF16 (W split
+// exactly into bf16 hi + lo: three MFMAs, W_hi.x_hi + W_hi.x_lo + W_lo.x_hi;
+// the dropped W_lo.x_lo is below 2^-18 |w| |x|).
+template <int NMF, class WT>
 __device__ __attribute__((always_inline)) void grouped_dma_body(const IdArgs& a, const DTile& t) {
     constexpr int NROW = NMF * 16;                  // LDS rows in use
     constexpr int DPW = (NROW / 8 + DW - 1) / DW;   // DMA instructions per wave per step
@@ -860,40 +876,69 @@ __device__ __attribute__((always_inline)) void grouped_dma_body(const IdArgs& a,
     const int frow = lane & 15, fq = lane >> 4;
     auto compute = [&](auto STG, const u32x4 (&wc)[DF]) {
         const float* st = t.xs[decltype(STG)::value];
-        // All row groups are read and split first; then the hi products of
-        // every (row group, fragment) pair, then the lo products, so the two
-        // updates of one accumulator are NMF * DF MFMAs apart.
-        u32x4 xh[NMF], xl[NMF];
+        auto mma = [&](u32x4 w, u32x4 x, f32x4 c) __attribute__((always_inline)) {
+            return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w),
+                                                           __builtin_bit_cast(bf16x8, x), c, 0, 0, 0);
+        };
+        // f16 weights: the exact bf16 halves of every fragment, once per step.
+        u32x4 wh[DF], wl[DF];
+        if constexpr (WT::code == 1) {
 #pragma unroll
-        for (int mf = 0; mf < NMF; ++mf) {
-            const int row = mf * 16 + frow;
-            const int sw = (row >> 1) & 7;
-            const f32x4 x0 = *reinterpret_cast<const f32x4*>(st + row * DBK + (((2 * fq) ^ sw) << 2));
-            const f32x4 x1 = *reinterpret_cast<const f32x4*>(st + row * DBK + (((2 * fq + 1) ^ sw) << 2));
-            xh[mf][0] = cvt_pk_bf16(x0[0], x0[1]);
-            xh[mf][1] = cvt_pk_bf16(x0[2], x0[3]);
-            xh[mf][2] = cvt_pk_bf16(x1[0], x1[1]);
-            xh[mf][3] = cvt_pk_bf16(x1[2], x1[3]);
-            xl[mf][0] = cvt_pk_bf16(x0[0] - __uint_as_float(xh[mf][0] << 16), x0[1] - __uint_as_float(xh[mf][0] & 0xffff0000u));
-            xl[mf][1] = cvt_pk_bf16(x0[2] - __uint_as_float(xh[mf][1] << 16), x0[3] - __uint_as_float(xh[mf][1] & 0xffff0000u));
-            xl[mf][2] = cvt_pk_bf16(x1[0] - __uint_as_float(xh[mf][2] << 16), x1[1] - __uint_as_float(xh[mf][2] & 0xffff0000u));
-            xl[mf][3] = cvt_pk_bf16(x1[2] - __uint_as_float(xh[mf][3] << 16), x1[3] - __uint_as_float(xh[mf][3] & 0xffff0000u));
+            for (int j = 0; j < DF; ++j) split_f16_bf16(wc[j], wh[j], wl[j]);
         }
-        // Every fragment slot is computed: a wave's dead slots read a clamped,
-        // valid column and are never stored.
+        // Row groups in chunks of up to four (bounded register use): the
+        // chunk's rows are read and split first, then its hi products of every
+        // (row group, fragment) pair, then the lo products, so the updates of
+        // one accumulator are at least 4 * DF MFMAs apart when the chunk is
+        // full.
+        constexpr int NCH = (NMF + 3) / 4;
+        dstatic_for(std::make_integer_sequence<int, NCH>{}, [&](auto C_) {
+            constexpr int m0 = 4 * decltype(C_)::value;
+            constexpr int mn = NMF - m0 < 4 ? NMF - m0 : 4;
+            u32x4 xh[mn], xl[mn];
 #pragma unroll
-        for (int mf = 0; mf < NMF; ++mf)
+            for (int i = 0; i < mn; ++i) {
+                const int row = (m0 + i) * 16 + frow;
+                const int sw = (row >> 1) & 7;
+                const f32x4 x0 = *reinterpret_cast<const f32x4*>(st + row * DBK + (((2 * fq) ^ sw) << 2));
+                const f32x4 x1 = *reinterpret_cast<const f32x4*>(st + row * DBK + (((2 * fq + 1) ^ sw) << 2));
+                xh[i][0] = cvt_pk_bf16(x0[0], x0[1]);
+                xh[i][1] = cvt_pk_bf16(x0[2], x0[3]);
+                xh[i][2] = cvt_pk_bf16(x1[0], x1[1]);
+                xh[i][3] = cvt_pk_bf16(x1[2], x1[3]);
+                xl[i][0] = cvt_pk_bf16(x0[0] - __uint_as_float(xh[i][0] << 16), x0[1] - __uint_as_float(xh[i][0] & 0xffff0000u));
+                xl[i][1] = cvt_pk_bf16(x0[2] - __uint_as_float(xh[i][1] << 16), x0[3] - __uint_as_float(xh[i][1] & 0xffff0000u));
+                xl[i][2] = cvt_pk_bf16(x1[0] - __uint_as_float(xh[i][2] << 16), x1[1] - __uint_as_float(xh[i][2] & 0xffff0000u));
+                xl[i][3] = cvt_pk_bf16(x1[2] - __uint_as_float(xh[i][3] << 16), x1[3] - __uint_as_float(xh[i][3] & 0xffff0000u));
+            }
+            // Every fragment slot is computed: a wave's dead slots read a
+            // clamped, valid column and are never stored.
+            if constexpr (WT::code == 2) {
 #pragma unroll
-            for (int j = 0; j < DF; ++j)
-                acc[mf][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8, wc[j]), __builtin_bit_cast(bf16x8, xh[mf]), acc[mf][j], 0, 0, 0);
+                for (int i = 0; i < mn; ++i)
 #pragma unroll
-        for (int mf = 0; mf < NMF; ++mf)
+                    for (int j = 0; j < DF; ++j) acc[m0 + i][j] = mma(wc[j], xh[i], acc[m0 + i][j]);
 #pragma unroll
-            for (int j = 0; j < DF; ++j)
-                acc[mf][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8, wc[j]), __builtin_bit_cast(bf16x8, xl[mf]), acc[mf][j], 0, 0, 0);
+                for (int i = 0; i < mn; ++i)
+#pragma unroll
+                    for (int j = 0; j < DF; ++j) acc[m0 + i][j] = mma(wc[j], xl[i], acc[m0 + i][j]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < mn; ++i)
+#pragma unroll
+                    for (int j = 0; j < DF; ++j) acc[m0 + i][j] = mma(wh[j], xh[i], acc[m0 + i][j]);
+#pragma unroll
+                for (int i = 0; i < mn; ++i)
+#pragma unroll
+                    for (int j = 0; j < DF; ++j) acc[m0 + i][j] = mma(wh[j], xl[i], acc[m0 + i][j]);
+#pragma unroll
+                for (int i = 0; i < mn; ++i)
+#pragma unroll
+                    for (int j = 0; j < DF; ++j) acc[m0 + i][j] = mma(wl[j], xh[i], acc[m0 + i][j]);
+            }
+        });
     };
+
     // Step kt: wait until this wave's X(kt) DMA is done (AHEAD: the loads of
     // that many later steps may stay in flight behind W(kt)), barrier, issue
     // step kt + DLA into the buffer step kt - 1 used, multiply.
@@ -956,6 +1001,7 @@ __device__ __attribute__((always_inline)) void grouped_dma_body(const IdArgs& a,
 }
 #undef MM_LDSP
 
+template <class WT>
 __global__ __launch_bounds__(DW * kWave, 1) void id_grouped_dma(IdArgs a, uint32_t bn) {
     __shared__ uint32_t s_start[MM_GROUPED_MAX_E + 1];
     __shared__ uint32_t s_part[DW];
@@ -1008,14 +1054,14 @@ __global__ __launch_bounds__(DW * kWave, 1) void id_grouped_dma(IdArgs a, uint32
     t.lane = lane;
     t.W = reinterpret_cast<const char*>(a.W) + (uint64_t)e * a.expert_stride_bytes;
     switch ((cnt + 15) / 16) {
-        case 1: grouped_dma_body<1>(a, t); break;
-        case 2: grouped_dma_body<2>(a, t); break;
-        case 3: grouped_dma_body<3>(a, t); break;
-        case 4: grouped_dma_body<4>(a, t); break;
-        case 5: grouped_dma_body<5>(a, t); break;
-        case 6: grouped_dma_body<6>(a, t); break;
-        case 7: grouped_dma_body<7>(a, t); break;
-        default: grouped_dma_body<8>(a, t); break;
+        case 1: grouped_dma_body<1, WT>(a, t); break;
+        case 2: grouped_dma_body<2, WT>(a, t); break;
+        case 3: grouped_dma_body<3, WT>(a, t); break;
+        case 4: grouped_dma_body<4, WT>(a, t); break;
+        case 5: grouped_dma_body<5, WT>(a, t); break;
+        case 6: grouped_dma_body<6, WT>(a, t); break;
+        case 7: grouped_dma_body<7, WT>(a, t); break;
+        default: grouped_dma_body<8, WT>(a, t); break;
     }
 }
 
@@ -1110,9 +1156,12 @@ __global__ __launch_bounds__(kThreads) void id_grouped_fma(IdArgs a) {
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Upper bound of the m-tile count: sum_e ceil(c_e / BM) < total / BM + E.
+// Upper bound on the tile count: every expert in use adds at most one
+// partial row tile, and at most min(E, routed rows) experts are in use.
 inline uint64_t grid_for(const IdArgs& a, int bm, int bn) {
     const uint64_t total = (uint64_t)a.m * a.top_k;
-    const uint64_t tmax = (total + bm - 1) / bm + a.n_experts;
+    const uint64_t used = total < a.n_experts ? total : a.n_experts;
+    const uint64_t tmax = (total + bm - 1) / bm + used;
     const uint64_t n_tiles = (a.n + bn - 1) / bn;
     return 8ull * n_tiles * ((tmax + 7) / 8);
 }
@@ -1164,13 +1213,19 @@ hipError_t launch_id_map(const IdArgs& a, hipStream_t s, int* kernel) {
 }
 
 hipError_t launch_id_grouped(const IdArgs& a, hipStream_t s, int* kernel) {
-    if (a.wdtype == 2) {
+    if (a.wdtype != 0) {
         // Output tile width: as few tiles as cover n at GMAXBN each, raised until
-        // experts x tiles reaches the CU count (every CU streams one W slab).
+        // (experts that can be in use) x tiles reaches the CU count, so every
+        // CU streams one W slab even when few tokens touch few experts.
         const uint32_t frags = (a.n + 15) / 16;
         uint32_t split = (a.n + GMAXBN - 1) / GMAXBN;
-        const uint32_t want = (256 + a.n_experts - 1) / a.n_experts;
-        if (split < want) split = want < frags ? want : frags;
+        const uint64_t rows = (uint64_t)a.m * a.top_k;
+        const uint32_t used = (uint32_t)(rows < a.n_experts ? rows : a.n_experts);
+        const uint32_t want = (256 + used - 1) / used;
+        // At least one live 16-output fragment per wave of a block.
+        const uint32_t most = frags / 4 > 1 ? frags / 4 : 1;
+        if (split < want) split = want < most ? want : most;
+        if (split < 1) split = 1;
         uint32_t bn = ((frags + split - 1) / split) * 16;
         void* args[] = {const_cast<IdArgs*>(&a), &bn};
         const bool vec = a.k % 8 == 0 && a.expert_stride_bytes % 16 == 0 && aligned16(a.W) &&
@@ -1179,14 +1234,19 @@ hipError_t launch_id_grouped(const IdArgs& a, hipStream_t s, int* kernel) {
         const uint64_t in_rows = a.layout == 0 ? a.m : (uint64_t)a.m * a.top_k;
         const bool fast = vec && a.k % (DST * DBK) == 0 && in_rows * a.k * 4 < (1ull << 31) &&
                           (uint64_t)a.n * a.k * 2 < (1ull << 31);
-        *kernel = MM_KERNEL_ID_GROUPED_MFMA;
-        if (fast)
-            return hipLaunchKernel((const void*)&id_grouped_dma, dim3((unsigned)grid_for(a, DQM, bn)),
-                                   dim3(DW * kWave), args, 0, s);
-        const uint64_t g = grid_for(a, QBM, bn);
-        const void* fn = vec ? (const void*)&id_grouped_bf16<true, false>
-                             : (const void*)&id_grouped_bf16<false, false>;
-        return hipLaunchKernel(fn, dim3((unsigned)g), dim3(GW * kWave), args, 0, s);
+        if (fast) {
+            *kernel = MM_KERNEL_ID_GROUPED_MFMA;
+            const void* fn = a.wdtype == 2 ? (const void*)&id_grouped_dma<TBF16>
+                                           : (const void*)&id_grouped_dma<TF16>;
+            return hipLaunchKernel(fn, dim3((unsigned)grid_for(a, DQM, bn)), dim3(DW * kWave), args, 0, s);
+        }
+        if (a.wdtype == 2) {
+            *kernel = MM_KERNEL_ID_GROUPED_MFMA;
+            const uint64_t g = grid_for(a, QBM, bn);
+            const void* fn = vec ? (const void*)&id_grouped_bf16<true, false>
+                                 : (const void*)&id_grouped_bf16<false, false>;
+            return hipLaunchKernel(fn, dim3((unsigned)g), dim3(GW * kWave), args, 0, s);
+        }
     }
     void* args[] = {const_cast<IdArgs*>(&a)};
     const uint64_t g = grid_for(a, FBM, FBN);

@@ -90,8 +90,8 @@ typedef enum {
     MM_KERNEL_ID_DIRECT_FAST = 6,    /* direct route, 16-byte loads, one id-row load */
     MM_KERNEL_ID_DIRECT = 7,         /* direct route, general */
     MM_KERNEL_ID_MAP = 8,            /* map pass */
-    MM_KERNEL_ID_GROUPED_MFMA = 9,   /* grouped pass, bf16 weights on MFMA */
-    MM_KERNEL_ID_GROUPED_FMA = 10,   /* grouped pass, f32 / f16 weights */
+    MM_KERNEL_ID_GROUPED_MFMA = 9,   /* grouped pass on MFMA: bf16 weights, or aligned f16 weights */
+    MM_KERNEL_ID_GROUPED_FMA = 10,   /* grouped pass, f32 weights or unaligned f16 weights */
     MM_KERNEL_GEMV_WIDE = 11         /* skinny route, one 16 x 16 MFMA fragment per block */
 } mm_kernel;
 

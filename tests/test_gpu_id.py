@@ -132,6 +132,29 @@ def test_ramp_bit_exact(route, wdt):
     np.testing.assert_array_equal(got, ref)
 
 
+@pytest.mark.parametrize("wdt", DTYPES)
+def test_ramp_bit_exact_pipelined_grouped(wdt):
+    """k = 512 takes the pipelined MFMA grouped kernel for bf16 and for f16
+    weights (f16 split exactly into bf16 halves, activations into hi + lo);
+    on ramp inputs every term is exact, so the output matches the rounded
+    oracle bit for bit. More than 128 rows land on one expert, so full
+    128-row tiles (eight row groups) are covered too."""
+    m, n, k, top_k, E = 150, 72, 512, 2, 2
+    rng = np.random.default_rng(71)
+    w = wl.ramp(E * n * k, 3).reshape(E, n, k)
+    x = wl.ramp(m * k, 4).reshape(m, k)
+    ids = wl.distinct_ids(rng, m, top_k, E)
+    case = wl.make_id_case(wdt, w, x, ids)
+    _say(f"ramp pipelined grouped wdt={wl.DTYPE_NAMES[wdt]}")
+    run = IdRun(case, route=1)
+    rec = run.run()
+    want = mm.MM_KERNEL_ID_GROUPED_FMA if wdt == wl.F32 else mm.MM_KERNEL_ID_GROUPED_MFMA
+    assert rec.kernel == want, rec.kernel
+    got = from_dev(run.out, np.float32).reshape(m * top_k, n)
+    ref = oracle.round_to(wl.F32, run.oracle())
+    np.testing.assert_array_equal(got, ref)
+
+
 def test_direct_repeats_and_dedup_rows_identical():
     m, n, k, top_k, E = 2, 300, 512, 8, 5
     _say("direct repeats")
