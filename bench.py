@@ -124,12 +124,12 @@ def calibrate_id(torch, mm, wl, dev, stream, args):
     timer = Timer(torch, stream, True)
     # (experts, top_k, n, k, weight dtype)
     layers = [(64, 8, 1408, 2048, wl.BF16), (16, 4, 2048, 2048, wl.BF16),
-              (64, 8, 1408, 2048, wl.F16)]
+              (64, 8, 1408, 2048, wl.F16), (16, 4, 2048, 2048, wl.F32)]
     table = []
     for (E, top_k, n, k, wdt) in layers:
         rng = np.random.default_rng(11)
         w = to_dev_bits(torch, dev, wl.to_storage(0.02 * rng.standard_normal(E * n * k), wdt))
-        wbytes = E * n * k * 2
+        wbytes = E * n * k * wl.ELT[wdt]
         n_rot = max(2, math.ceil(ROTATE_BYTES / wbytes))
         Ws = [w] + [w.clone() for _ in range(n_rot - 1)]
         wb = [mm.buf(t) for t in Ws]
@@ -140,8 +140,9 @@ def calibrate_id(torch, mm, wl, dev, stream, args):
             out = torch.empty(m * top_k * n, dtype=torch.float32, device=dev)
             cnt = torch.empty(E, dtype=torch.int32, device=dev)
             rr = torch.empty(E * m, dtype=torch.int32, device=dev)
-            pd = mm.id_params(m, n, k, top_k, E, n * k * 2, 0, 0, 0)
-            pg = mm.id_params(m, n, k, top_k, E, n * k * 2, 0, 0, 1)
+            es = wl.ELT[wdt]
+            pd = mm.id_params(m, n, k, top_k, E, n * k * es, 0, 0, 0)
+            pg = mm.id_params(m, n, k, top_k, E, n * k * es, 0, 0, 1)
             xb, ib, ob, cb, rb = mm.buf(x), mm.buf(ids), mm.buf(out), mm.buf(cnt), mm.buf(rr)
 
             def direct(i):
@@ -154,8 +155,9 @@ def calibrate_id(torch, mm, wl, dev, stream, args):
             td, _ = timer.time(direct, n_rot, steps, 3)
             tg, _ = timer.time(grouped, n_rot, steps, 3)
             used = len(set(int(v) for v in ids_np.reshape(-1)))
+            hint = mm.mm_id_route_hint(wdt, pd)
             row = {"experts": E, "top_k": top_k, "n": n, "k": k, "m": m,
-                   "weights": wl.DTYPE_NAMES[wdt],
+                   "weights": wl.DTYPE_NAMES[wdt], "hint": "grouped" if hint else "direct",
                    "rows_per_expert": m * top_k / E, "experts_used": used,
                    "direct_us": td * 1e3, "grouped_us": tg * 1e3,
                    "faster": "direct" if td <= tg else "grouped"}
@@ -163,7 +165,7 @@ def calibrate_id(torch, mm, wl, dev, stream, args):
             log(f"{wl.DTYPE_NAMES[wdt]} E={E:3d} top_k={top_k} n={n} k={k} m={m:4d} "
                 f"rows/expert={m * top_k / E:7.3f} "
                 f"used={used:3d}  direct {td * 1e3:8.2f} us  grouped {tg * 1e3:8.2f} us  "
-                f"-> {row['faster']}")
+                f"-> {row['faster']} (hint {row['hint']})")
             del x, ids, out, cnt, rr
         del Ws, wb, w
         torch.cuda.empty_cache()

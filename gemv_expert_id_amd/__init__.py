@@ -39,7 +39,8 @@ STATUS_NAMES = {
 
 # Every symbol include/mm.h declares.
 EXPORTS = [
-    "mm_gemm", "mm_gemv", "mm_id_query", "mm_id_direct", "mm_id_map", "mm_id_grouped",
+    "mm_gemm", "mm_gemv", "mm_id_query", "mm_id_route_hint", "mm_id_direct", "mm_id_map",
+    "mm_id_grouped",
     "mm_id", "mm_capabilities", "mm_status_string", "mm_last_error",
     "mm_test_inject_resolve_failure", "mm_test_launch_count",
 ]
@@ -117,6 +118,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.mm_gemv.restype = st
     lib.mm_id_query.argtypes = [ctypes.c_int, P(IdParams), P(IdCapability)]
     lib.mm_id_query.restype = st
+    lib.mm_id_route_hint.argtypes = [ctypes.c_int, P(IdParams), P(ctypes.c_uint32)]
+    lib.mm_id_route_hint.restype = st
     lib.mm_id_direct.argtypes = [P(IdParams), ctypes.c_int, Buf, Buf, Buf, Buf, vp, P(Receipt)]
     lib.mm_id_direct.restype = st
     lib.mm_id_map.argtypes = [P(IdParams), Buf, Buf, Buf, Buf, vp, P(Receipt)]
@@ -192,6 +195,13 @@ def mm_id_query(weight_dtype: int, params: IdParams) -> IdCapability:
     cap = IdCapability()
     _raise(load().mm_id_query(weight_dtype, ctypes.byref(params), ctypes.byref(cap)))
     return cap
+
+
+def mm_id_route_hint(weight_dtype: int, params: IdParams) -> int:
+    """0 (direct) or 1 (grouped prefill): the route measured faster for this problem."""
+    r = ctypes.c_uint32(0)
+    _raise(load().mm_id_route_hint(weight_dtype, ctypes.byref(params), ctypes.byref(r)))
+    return int(r.value)
 
 
 def mm_id_direct(params: IdParams, weight_dtype: int, weights: Buf, inp: Buf, ids: Buf,

@@ -498,6 +498,28 @@ mm_status mm_id_query(mm_dtype weight_dtype, const mm_id_params* params, mm_id_c
     return st == MM_OK ? ok() : st;
 }
 
+// Crossover between the routes, in routed rows per expert (m * top_k /
+// n_experts), measured on MI355X over token counts 1..512 for 64-expert
+// 1408 x 2048 and 16-expert 2048 x 2048 layers: with bf16 or f16 weights the
+// grouped route wins from 2 rows per expert on (the direct route then reads
+// each expert's weights about twice); with f32 weights the grouped pass runs
+// FMA tiles and wins only from about 16 rows per expert.
+mm_status mm_id_route_hint(mm_dtype weight_dtype, const mm_id_params* params, uint32_t* route) {
+    if (!params || !route) return fail(MM_ERR_INVALID_ARGUMENT, "matmul_id route hint: null argument");
+    mm_id_params q = *params;
+    q.route = 0;
+    mm_id_capability tmp;
+    mm_status st = id_query(weight_dtype, &q, &tmp);
+    if (st != MM_OK) return st;
+    uint32_t r = 0;
+    if (q.multiplicity == 0 && q.n_experts <= MM_ID_GROUPED_MAX_EXPERTS) {
+        const uint64_t per_expert = weight_dtype == MM_F32 ? 16 : 2;
+        if ((uint64_t)q.m * q.top_k >= per_expert * q.n_experts) r = 1;
+    }
+    *route = r;
+    return ok();
+}
+
 mm_status mm_id_direct(const mm_id_params* params, mm_dtype weight_dtype, mm_buf weights,
                        mm_buf input, mm_buf ids, mm_buf out, void* stream, mm_receipt* receipt) {
     mm_id_capability cap;

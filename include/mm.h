@@ -210,6 +210,18 @@ typedef struct {
 mm_status mm_id_query(mm_dtype weight_dtype, const mm_id_params *params, mm_id_capability *out);
 
 /*
+ * Route suggestion (host only). The pages leave the route to the caller
+ * (mlx-native `DenseMatmulIdParams`: route chosen by the caller); this
+ * reports the one measured to be faster on MI355X for the given problem:
+ * 1 (grouped prefill) when the grouped route is allowed (distinct ids per
+ * token, n_experts <= MM_ID_GROUPED_MAX_EXPERTS) and
+ * m * top_k >= c * n_experts, with c = 2 for bf16/f16 weights and c = 16 for
+ * f32 weights; otherwise 0 (direct). params->route is ignored. Errors as
+ * mm_id_query (validation of everything but the route).
+ */
+mm_status mm_id_route_hint(mm_dtype weight_dtype, const mm_id_params *params, uint32_t *route);
+
+/*
  * Direct route: one launch computes every routed row
  * (mlx-native `DenseMatmulIdRoute::Direct`). Requires params->route == 0.
  * Repeated ids are allowed. Buffers: weights (weight_dtype), input f32, ids

@@ -171,6 +171,30 @@ def _id_bufs(cap, base=0x40000000):
     return w, x, ids, out, cnt, rr
 
 
+def test_id_route_hint():
+    """Host-only route suggestion: grouped from 2 routed rows per expert
+    (16 with f32 weights), never with may-repeat ids or above the grouped
+    expert limit; params.route is ignored; invalid params are rejected."""
+    def hint(wdt, m, top_k, E, mult=0, route=0, n=1408, k=2048):
+        es = 4 if wdt == mm.MM_F32 else 2
+        return mm.mm_id_route_hint(wdt, mm.id_params(m, n, k, top_k, E, n * k * es, 0, mult, route))
+    assert hint(mm.MM_BF16, 1, 8, 64) == 0
+    assert hint(mm.MM_BF16, 15, 8, 64) == 0
+    assert hint(mm.MM_BF16, 16, 8, 64) == 1
+    assert hint(mm.MM_F16, 16, 8, 64, route=1) == 1
+    assert hint(mm.MM_BF16, 512, 8, 64) == 1
+    assert hint(mm.MM_BF16, 512, 8, 64, mult=1) == 0
+    assert hint(mm.MM_BF16, 4096, 2, 2000) == 0      # above the grouped expert limit
+    assert hint(mm.MM_F32, 64, 8, 64) == 0
+    assert hint(mm.MM_F32, 128, 8, 64) == 1
+    assert hint(mm.MM_BF16, 8, 4, 16) == 1 and hint(mm.MM_BF16, 7, 4, 16) == 0
+    with pytest.raises(mm.MmError) as e:
+        hint(mm.MM_BF16, 0, 8, 64)
+    assert e.value.status == 1
+    with pytest.raises(mm.MmError):
+        hint(mm.MM_BF16, 4, 9, 8)                     # distinct top_k > n_experts
+
+
 def test_id_call_rejects():
     pd = mm.id_params(9, 7, 35, 2, 4, 7 * 35 * 4, 0, 1, 0)
     pg = mm.id_params(9, 7, 35, 2, 4, 7 * 35 * 4, 0, 0, 1)
