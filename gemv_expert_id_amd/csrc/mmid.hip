@@ -741,13 +741,14 @@ __global__ __launch_bounds__(GW * kWave, 1) void id_grouped_bf16(IdArgs a, uint3
 }
 
 // ---------------------------------------------------------------------------
-// Grouped pass, bf16 weights, pipelined form (k % 128 == 0, aligned operands,
-// input and one expert below 2 GiB).
+// Grouped pass, bf16 or f16 weights, pipelined form (k % 128 == 0, aligned
+// operands, input and one expert below 2 GiB).
 //
 // Block = 4 waves, one per SIMD (each wave has the whole register file; the
-// accumulators of up to 8 row groups x DF = 6 output fragments of 16 x 16 sit
-// in AGPRs). Tile = (expert, up to 128 routed rows, bn <= 384 outputs); the
-// host sizes bn so that the tile count is close to the CU count. Per K step
+// accumulators of up to 8 row groups x DF output fragments of 16 x 16 sit in
+// AGPRs, DF = 2, 4 or 6 picked by the host as the fewest slots that cover the
+// tile). Tile = (expert, up to 128 routed rows, bn <= 384 outputs); the host
+// sizes bn so that the tile count is close to the CU count. Per K step
 // of 32 (four LDS stages, step kt in stage kt % 4):
 //   X  the gathered f32 activation rows go from global memory straight into
 //      LDS (buffer_load ... lds; each lane fetches the 16-byte chunk that
@@ -767,8 +768,8 @@ __global__ __launch_bounds__(GW * kWave, 1) void id_grouped_bf16(IdArgs a, uint3
 // with a fixed number of loads.
 // ---------------------------------------------------------------------------
 constexpr int DW = 4;               // waves per block
-constexpr int DF = 6;               // 16-output fragments per wave
-constexpr int DMAXBN = DW * DF * 16;
+constexpr int DFMAX = 6;            // 16-output fragments per wave, at most
+constexpr int DMAXBN = DW * DFMAX * 16;
 constexpr int DQM = 128;            // routed rows per tile
 constexpr int DBK = 32;             // K step
 constexpr int DST = 4;              // LDS stages = weight register buffers
@@ -812,7 +813,7 @@ __device__ __forceinline__ void split_f16_bf16(u32x4 w, u32x4& hi, u32x4& lo) {
 // WT: TBF16 (W used as stored: two MFMAs, W.x_hi + W.x_lo) or TF16 (W split
 // exactly into bf16 hi + lo: three MFMAs, W_hi.x_hi + W_hi.x_lo + W_lo.x_hi;
 // the dropped W_lo.x_lo is below 2^-18 |w| |x|).
-template <int NMF, class WT>
+template <int NMF, class WT, int DF>
 __device__ __attribute__((always_inline)) void grouped_dma_body(const IdArgs& a, const DTile& t) {
     constexpr int NROW = NMF * 16;                  // LDS rows in use
     constexpr int DPW = (NROW / 8 + DW - 1) / DW;   // DMA instructions per wave per step
@@ -1001,7 +1002,7 @@ __device__ __attribute__((always_inline)) void grouped_dma_body(const IdArgs& a,
 }
 #undef MM_LDSP
 
-template <class WT>
+template <class WT, int DF>
 __global__ __launch_bounds__(DW * kWave, 1) void id_grouped_dma(IdArgs a, uint32_t bn) {
     __shared__ uint32_t s_start[MM_GROUPED_MAX_E + 1];
     __shared__ uint32_t s_part[DW];
@@ -1054,14 +1055,14 @@ __global__ __launch_bounds__(DW * kWave, 1) void id_grouped_dma(IdArgs a, uint32
     t.lane = lane;
     t.W = reinterpret_cast<const char*>(a.W) + (uint64_t)e * a.expert_stride_bytes;
     switch ((cnt + 15) / 16) {
-        case 1: grouped_dma_body<1, WT>(a, t); break;
-        case 2: grouped_dma_body<2, WT>(a, t); break;
-        case 3: grouped_dma_body<3, WT>(a, t); break;
-        case 4: grouped_dma_body<4, WT>(a, t); break;
-        case 5: grouped_dma_body<5, WT>(a, t); break;
-        case 6: grouped_dma_body<6, WT>(a, t); break;
-        case 7: grouped_dma_body<7, WT>(a, t); break;
-        default: grouped_dma_body<8, WT>(a, t); break;
+        case 1: grouped_dma_body<1, WT, DF>(a, t); break;
+        case 2: grouped_dma_body<2, WT, DF>(a, t); break;
+        case 3: grouped_dma_body<3, WT, DF>(a, t); break;
+        case 4: grouped_dma_body<4, WT, DF>(a, t); break;
+        case 5: grouped_dma_body<5, WT, DF>(a, t); break;
+        case 6: grouped_dma_body<6, WT, DF>(a, t); break;
+        case 7: grouped_dma_body<7, WT, DF>(a, t); break;
+        default: grouped_dma_body<8, WT, DF>(a, t); break;
     }
 }
 
@@ -1236,8 +1237,14 @@ hipError_t launch_id_grouped(const IdArgs& a, hipStream_t s, int* kernel) {
                           (uint64_t)a.n * a.k * 2 < (1ull << 31);
         if (fast) {
             *kernel = MM_KERNEL_ID_GROUPED_MFMA;
-            const void* fn = a.wdtype == 2 ? (const void*)&id_grouped_dma<TBF16>
-                                           : (const void*)&id_grouped_dma<TF16>;
+            // Fragment slots per wave: the fewest of 2, 4, 6 that cover the tile.
+            const uint32_t per_wave = (bn / 16 + DW - 1) / DW;
+            const int df = per_wave <= 2 ? 2 : per_wave <= 4 ? 4 : 6;
+#define MM_GD(T) (df == 2 ? (const void*)&id_grouped_dma<T, 2>   \
+                  : df == 4 ? (const void*)&id_grouped_dma<T, 4> \
+                            : (const void*)&id_grouped_dma<T, 6>)
+            const void* fn = a.wdtype == 2 ? MM_GD(TBF16) : MM_GD(TF16);
+#undef MM_GD
             return hipLaunchKernel(fn, dim3((unsigned)grid_for(a, DQM, bn)), dim3(DW * kWave), args, 0, s);
         }
         if (a.wdtype == 2) {
