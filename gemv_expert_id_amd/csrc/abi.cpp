@@ -500,10 +500,11 @@ mm_status mm_id_query(mm_dtype weight_dtype, const mm_id_params* params, mm_id_c
 
 // Crossover between the routes, in routed rows per expert (m * top_k /
 // n_experts), measured on MI355X over token counts 1..512 for 64-expert
-// 1408 x 2048 and 16-expert 2048 x 2048 layers: with bf16 or f16 weights the
-// grouped route wins from 2 rows per expert on (the direct route then reads
-// each expert's weights about twice); with f32 weights the grouped pass runs
-// FMA tiles and wins only from about 16 rows per expert.
+// 1408 x 2048 and 16-expert 2048 x 2048 layers with bf16, f16 and f32
+// weights: the grouped route wins from 2 rows per expert on, where the
+// direct route would read each expert's weights about twice. Layouts that
+// leave the grouped pass on FMA tiles (f16/f32 weights with k % 128 != 0 or
+// unaligned operands) need about 16 rows per expert.
 mm_status mm_id_route_hint(mm_dtype weight_dtype, const mm_id_params* params, uint32_t* route) {
     if (!params || !route) return fail(MM_ERR_INVALID_ARGUMENT, "matmul_id route hint: null argument");
     mm_id_params q = *params;
@@ -513,7 +514,8 @@ mm_status mm_id_route_hint(mm_dtype weight_dtype, const mm_id_params* params, ui
     if (st != MM_OK) return st;
     uint32_t r = 0;
     if (q.multiplicity == 0 && q.n_experts <= MM_ID_GROUPED_MAX_EXPERTS) {
-        const uint64_t per_expert = weight_dtype == MM_F32 ? 16 : 2;
+        const bool fma_tiles = weight_dtype != MM_BF16 && q.k % 128 != 0;
+        const uint64_t per_expert = fma_tiles ? 16 : 2;
         if ((uint64_t)q.m * q.top_k >= per_expert * q.n_experts) r = 1;
     }
     *route = r;

@@ -741,7 +741,7 @@ __global__ __launch_bounds__(GW * kWave, 1) void id_grouped_bf16(IdArgs a, uint3
 }
 
 // ---------------------------------------------------------------------------
-// Grouped pass, bf16 or f16 weights, pipelined form (k % 128 == 0, aligned
+// Grouped pass, pipelined form for every weight dtype (k % 128 == 0, aligned
 // operands, input and one expert below 2 GiB).
 //
 // Block = 4 waves, one per SIMD (each wave has the whole register file; the
@@ -810,21 +810,26 @@ __device__ __forceinline__ void split_f16_bf16(u32x4 w, u32x4& hi, u32x4& lo) {
     }
 }
 
-// WT: TBF16 (W used as stored: two MFMAs, W.x_hi + W.x_lo) or TF16 (W split
+// WT: TBF16 (W used as stored: two MFMAs, W.x_hi + W.x_lo), TF16 (W split
 // exactly into bf16 hi + lo: three MFMAs, W_hi.x_hi + W_hi.x_lo + W_lo.x_hi;
-// the dropped W_lo.x_lo is below 2^-18 |w| |x|).
+// the dropped W_lo.x_lo is below 2^-18 |w| |x|) or TF32 (f32 MFMA 16x16x4 on
+// the values as stored: a fragment is two 16-byte loads per lane, 8 k values,
+// and MFMA q of a step takes value q of every lane for both operands).
 template <int NMF, class WT, int DF>
 __device__ __attribute__((always_inline)) void grouped_dma_body(const IdArgs& a, const DTile& t) {
     constexpr int NROW = NMF * 16;                  // LDS rows in use
     constexpr int DPW = (NROW / 8 + DW - 1) / DW;   // DMA instructions per wave per step
-    constexpr int LPS = DPW + DF;                   // loads per wave per step
+    constexpr int WL = WT::code == 0 ? 2 : 1;       // 16-byte loads per weight fragment
+    constexpr int NWR = DF * WL;                    // weight loads per wave per step
+    constexpr int ES = WT::code == 0 ? 4 : 2;       // weight element bytes
+    constexpr int LPS = DPW + NWR;                  // loads per wave per step
     const int lane = t.lane, wave = t.wave;
     const int64_t nk = a.k / DBK;                   // a multiple of DST
-    static_assert(DLA * (DF + (NROW / 8 + DW - 1) / DW) <= 63, "loads in flight exceed vmcnt");
+    static_assert(DLA * LPS <= 63, "loads in flight exceed vmcnt");
     const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(a.X), (short)0, 0x7fffffff, 0x00020000);
     const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(t.W), (short)0, (int)(a.n * a.k * 2), 0x00020000);
+        const_cast<char*>(t.W), (short)0, (int)(a.n * a.k * ES), 0x00020000);
 
     // DMA: instruction d of this wave fills LDS rows r0 .. r0 + 7 with
     // r0 = 8 * min(wave * DPW + d, NROW / 8 - 1) (a repeated instruction
@@ -857,13 +862,15 @@ __device__ __attribute__((always_inline)) void grouped_dma_body(const IdArgs& a,
     for (int j = 0; j < DF; ++j) {
         int64_t col = t.tile_n0 + (int64_t)(wave + DW * j) * 16 + (lane & 15);
         col = col < t.tile_n1 ? col : t.tile_n1 - 1;
-        wvo[j] = (int)((col * a.k + (lane >> 4) * 8) * 2);
+        wvo[j] = (int)((col * a.k + (lane >> 4) * 8) * ES);
     }
-    auto load_w = [&](int64_t kt, u32x4 (&w)[DF]) {
+    auto load_w = [&](int64_t kt, u32x4 (&w)[NWR]) {
 #pragma unroll
         for (int j = 0; j < DF; ++j)
-            w[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                       wrs, wvo[j], (int)(kt * DBK * 2), 0));
+#pragma unroll
+            for (int h = 0; h < WL; ++h)
+                w[j * WL + h] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                    wrs, wvo[j] + 16 * h, (int)(kt * DBK * ES), 0));
     };
 
     f32x4 acc[NMF][DF];
@@ -875,8 +882,35 @@ __device__ __attribute__((always_inline)) void grouped_dma_body(const IdArgs& a,
     // Activation fragment of row group mf: lane -> row mf*16 + lane%16,
     // floats 8*(lane/16) .. +8 (chunks 2q, 2q+1 at their swizzled slots).
     const int frow = lane & 15, fq = lane >> 4;
-    auto compute = [&](auto STG, const u32x4 (&wc)[DF]) {
+    auto compute = [&](auto STG, const u32x4 (&wc)[NWR]) {
         const float* st = t.xs[decltype(STG)::value];
+        if constexpr (WT::code == 0) {
+            // f32: row groups in chunks of four; value q of the lane's 8
+            // activations and weights is contraction slot q of MFMA q.
+            constexpr int NCH = (NMF + 3) / 4;
+            dstatic_for(std::make_integer_sequence<int, NCH>{}, [&](auto C_) {
+                constexpr int m0 = 4 * decltype(C_)::value;
+                constexpr int mn = NMF - m0 < 4 ? NMF - m0 : 4;
+                f32x4 x0[mn], x1[mn];
+#pragma unroll
+                for (int i = 0; i < mn; ++i) {
+                    const int row = (m0 + i) * 16 + frow;
+                    const int sw = (row >> 1) & 7;
+                    x0[i] = *reinterpret_cast<const f32x4*>(st + row * DBK + (((2 * fq) ^ sw) << 2));
+                    x1[i] = *reinterpret_cast<const f32x4*>(st + row * DBK + (((2 * fq + 1) ^ sw) << 2));
+                }
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+#pragma unroll
+                    for (int i = 0; i < mn; ++i)
+#pragma unroll
+                        for (int j = 0; j < DF; ++j)
+                            acc[m0 + i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                __uint_as_float(wc[j * 2 + q / 4][q % 4]),
+                                q < 4 ? x0[i][q % 4] : x1[i][q % 4], acc[m0 + i][j], 0, 0, 0);
+            });
+            return;
+        }
         auto mma = [&](u32x4 w, u32x4 x, f32x4 c) __attribute__((always_inline)) {
             return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w),
                                                            __builtin_bit_cast(bf16x8, x), c, 0, 0, 0);
@@ -943,12 +977,12 @@ __device__ __attribute__((always_inline)) void grouped_dma_body(const IdArgs& a,
     // Step kt: wait until this wave's X(kt) DMA is done (AHEAD: the loads of
     // that many later steps may stay in flight behind W(kt)), barrier, issue
     // step kt + DLA into the buffer step kt - 1 used, multiply.
-    u32x4 wb[DST][DF];
+    u32x4 wb[DST][NWR];
     // Step kt = kt0 + S (kt0 a multiple of DST, so stage S): S_ carries S.
-    auto step = [&](auto AHEAD, auto LOAD, auto S_, int64_t kt, const u32x4 (&wc)[DF],
-                    u32x4 (&wf)[DF]) {
+    auto step = [&](auto AHEAD, auto LOAD, auto S_, int64_t kt, const u32x4 (&wc)[NWR],
+                    u32x4 (&wf)[NWR]) {
         constexpr int S = decltype(S_)::value;
-        __builtin_amdgcn_s_waitcnt(dwait_vm(DF + decltype(AHEAD)::value * LPS));
+        __builtin_amdgcn_s_waitcnt(dwait_vm(NWR + decltype(AHEAD)::value * LPS));
         __builtin_amdgcn_s_barrier();
         if constexpr (decltype(LOAD)::value) {
             dma_x(kt + DLA, std::integral_constant<int, (S + DLA) % DST>{});
@@ -1214,52 +1248,56 @@ hipError_t launch_id_map(const IdArgs& a, hipStream_t s, int* kernel) {
 }
 
 hipError_t launch_id_grouped(const IdArgs& a, hipStream_t s, int* kernel) {
-    if (a.wdtype != 0) {
-        // Output tile width: as few tiles as cover n at GMAXBN each, raised until
-        // (experts that can be in use) x tiles reaches the CU count, so every
-        // CU streams one W slab even when few tokens touch few experts.
-        const uint32_t frags = (a.n + 15) / 16;
-        uint32_t split = (a.n + GMAXBN - 1) / GMAXBN;
-        const uint64_t rows = (uint64_t)a.m * a.top_k;
-        const uint32_t used = (uint32_t)(rows < a.n_experts ? rows : a.n_experts);
-        const uint32_t want = (256 + used - 1) / used;
-        // At least one live 16-output fragment per wave of a block.
-        const uint32_t most = frags / 4 > 1 ? frags / 4 : 1;
-        if (split < want) split = want < most ? want : most;
-        if (split < 1) split = 1;
-        uint32_t bn = ((frags + split - 1) / split) * 16;
-        void* args[] = {const_cast<IdArgs*>(&a), &bn};
-        const bool vec = a.k % 8 == 0 && a.expert_stride_bytes % 16 == 0 && aligned16(a.W) &&
-                         aligned16(a.X) && a.x_tok_stride_bytes % 16 == 0 &&
-                         a.x_slot_stride_bytes % 16 == 0;
-        const uint64_t in_rows = a.layout == 0 ? a.m : (uint64_t)a.m * a.top_k;
-        const bool fast = vec && a.k % (DST * DBK) == 0 && in_rows * a.k * 4 < (1ull << 31) &&
-                          (uint64_t)a.n * a.k * 2 < (1ull << 31);
-        if (fast) {
-            *kernel = MM_KERNEL_ID_GROUPED_MFMA;
-            // Fragment slots per wave: the fewest of 2, 4, 6 that cover the tile.
-            const uint32_t per_wave = (bn / 16 + DW - 1) / DW;
-            const int df = per_wave <= 2 ? 2 : per_wave <= 4 ? 4 : 6;
+    // Output tile width: as few tiles as cover n at the widest tile each,
+    // raised until (experts that can be in use) x tiles reaches the CU count,
+    // so every CU streams one W slab even when few tokens touch few experts.
+    // f32 weight fragments take twice the registers: at most four per wave.
+    const uint32_t maxbn = a.wdtype == 0 ? (uint32_t)(DW * 4 * 16) : (uint32_t)GMAXBN;
+    const uint32_t frags = (a.n + 15) / 16;
+    uint32_t split = (a.n + maxbn - 1) / maxbn;
+    const uint64_t rows = (uint64_t)a.m * a.top_k;
+    const uint32_t used = (uint32_t)(rows < a.n_experts ? rows : a.n_experts);
+    const uint32_t want = (256 + used - 1) / used;
+    // At least one live 16-output fragment per wave of a block.
+    const uint32_t most = frags / 4 > 1 ? frags / 4 : 1;
+    if (split < want) split = want < most ? want : most;
+    if (split < 1) split = 1;
+    uint32_t bn = ((frags + split - 1) / split) * 16;
+    void* args[] = {const_cast<IdArgs*>(&a), &bn};
+    const uint64_t es = a.wdtype == 0 ? 4 : 2;
+    const bool vec = a.k % 8 == 0 && a.expert_stride_bytes % 16 == 0 && aligned16(a.W) &&
+                     aligned16(a.X) && a.x_tok_stride_bytes % 16 == 0 &&
+                     a.x_slot_stride_bytes % 16 == 0;
+    const uint64_t in_rows = a.layout == 0 ? a.m : (uint64_t)a.m * a.top_k;
+    const bool fast = vec && a.k % (DST * DBK) == 0 && in_rows * a.k * 4 < (1ull << 31) &&
+                      (uint64_t)a.n * a.k * es < (1ull << 31);
+    if (fast) {
+        *kernel = MM_KERNEL_ID_GROUPED_MFMA;
+        // Fragment slots per wave: the fewest of 2, 4, 6 that cover the tile.
+        const uint32_t per_wave = (bn / 16 + DW - 1) / DW;
+        const int df = per_wave <= 2 ? 2 : per_wave <= 4 ? 4 : 6;
 #define MM_GD(T) (df == 2 ? (const void*)&id_grouped_dma<T, 2>   \
                   : df == 4 ? (const void*)&id_grouped_dma<T, 4> \
                             : (const void*)&id_grouped_dma<T, 6>)
-            const void* fn = a.wdtype == 2 ? MM_GD(TBF16) : MM_GD(TF16);
+        const void* fn = a.wdtype == 2   ? MM_GD(TBF16)
+                         : a.wdtype == 1 ? MM_GD(TF16)
+                         : df == 2       ? (const void*)&id_grouped_dma<TF32, 2>
+                                         : (const void*)&id_grouped_dma<TF32, 4>;
 #undef MM_GD
-            return hipLaunchKernel(fn, dim3((unsigned)grid_for(a, DQM, bn)), dim3(DW * kWave), args, 0, s);
-        }
-        if (a.wdtype == 2) {
-            *kernel = MM_KERNEL_ID_GROUPED_MFMA;
-            const uint64_t g = grid_for(a, QBM, bn);
-            const void* fn = vec ? (const void*)&id_grouped_bf16<true, false>
-                                 : (const void*)&id_grouped_bf16<false, false>;
-            return hipLaunchKernel(fn, dim3((unsigned)g), dim3(GW * kWave), args, 0, s);
-        }
+        return hipLaunchKernel(fn, dim3((unsigned)grid_for(a, DQM, bn)), dim3(DW * kWave), args, 0, s);
     }
-    void* args[] = {const_cast<IdArgs*>(&a)};
+    if (a.wdtype == 2) {
+        *kernel = MM_KERNEL_ID_GROUPED_MFMA;
+        const uint64_t g = grid_for(a, QBM, bn);
+        const void* fn = vec ? (const void*)&id_grouped_bf16<true, false>
+                             : (const void*)&id_grouped_bf16<false, false>;
+        return hipLaunchKernel(fn, dim3((unsigned)g), dim3(GW * kWave), args, 0, s);
+    }
+    void* fargs[] = {const_cast<IdArgs*>(&a)};
     const uint64_t g = grid_for(a, FBM, FBN);
     *kernel = MM_KERNEL_ID_GROUPED_FMA;
     const void* fn = a.wdtype == 0 ? (const void*)&id_grouped_fma<TF32> : (const void*)&id_grouped_fma<TF16>;
-    return hipLaunchKernel(fn, dim3((unsigned)g), dim3(kThreads), args, 0, s);
+    return hipLaunchKernel(fn, dim3((unsigned)g), dim3(kThreads), fargs, 0, s);
 }
 
 }  // namespace mmk

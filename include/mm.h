@@ -90,8 +90,8 @@ typedef enum {
     MM_KERNEL_ID_DIRECT_FAST = 6,    /* direct route, 16-byte loads, one id-row load */
     MM_KERNEL_ID_DIRECT = 7,         /* direct route, general */
     MM_KERNEL_ID_MAP = 8,            /* map pass */
-    MM_KERNEL_ID_GROUPED_MFMA = 9,   /* grouped pass on MFMA: bf16 weights, or aligned f16 weights */
-    MM_KERNEL_ID_GROUPED_FMA = 10,   /* grouped pass, f32 weights or unaligned f16 weights */
+    MM_KERNEL_ID_GROUPED_MFMA = 9,   /* grouped pass on MFMA (bf16 weights; f16/f32 when k % 128 == 0 and aligned) */
+    MM_KERNEL_ID_GROUPED_FMA = 10,   /* grouped pass, FMA tiles (other f16/f32 layouts) */
     MM_KERNEL_GEMV_WIDE = 11         /* skinny route, one 16 x 16 MFMA fragment per block */
 } mm_kernel;
 
@@ -215,8 +215,9 @@ mm_status mm_id_query(mm_dtype weight_dtype, const mm_id_params *params, mm_id_c
  * reports the one measured to be faster on MI355X for the given problem:
  * 1 (grouped prefill) when the grouped route is allowed (distinct ids per
  * token, n_experts <= MM_ID_GROUPED_MAX_EXPERTS) and
- * m * top_k >= c * n_experts, with c = 2 for bf16/f16 weights and c = 16 for
- * f32 weights; otherwise 0 (direct). params->route is ignored. Errors as
+ * m * top_k >= c * n_experts, with c = 2, or c = 16 for f16/f32 weights
+ * when k % 128 != 0 (the grouped pass then runs FMA tiles); otherwise 0
+ * (direct). params->route is ignored. Errors as
  * mm_id_query (validation of everything but the route).
  */
 mm_status mm_id_route_hint(mm_dtype weight_dtype, const mm_id_params *params, uint32_t *route);

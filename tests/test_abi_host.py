@@ -173,8 +173,9 @@ def _id_bufs(cap, base=0x40000000):
 
 def test_id_route_hint():
     """Host-only route suggestion: grouped from 2 routed rows per expert
-    (16 with f32 weights), never with may-repeat ids or above the grouped
-    expert limit; params.route is ignored; invalid params are rejected."""
+    (16 when f16/f32 weights would take FMA tiles, k % 128 != 0), never with
+    may-repeat ids or above the grouped expert limit; params.route is
+    ignored; invalid params are rejected."""
     def hint(wdt, m, top_k, E, mult=0, route=0, n=1408, k=2048):
         es = 4 if wdt == mm.MM_F32 else 2
         return mm.mm_id_route_hint(wdt, mm.id_params(m, n, k, top_k, E, n * k * es, 0, mult, route))
@@ -185,8 +186,9 @@ def test_id_route_hint():
     assert hint(mm.MM_BF16, 512, 8, 64) == 1
     assert hint(mm.MM_BF16, 512, 8, 64, mult=1) == 0
     assert hint(mm.MM_BF16, 4096, 2, 2000) == 0      # above the grouped expert limit
-    assert hint(mm.MM_F32, 64, 8, 64) == 0
-    assert hint(mm.MM_F32, 128, 8, 64) == 1
+    assert hint(mm.MM_F32, 15, 8, 64) == 0 and hint(mm.MM_F32, 16, 8, 64) == 1
+    assert hint(mm.MM_F32, 64, 8, 64, k=2000) == 0 and hint(mm.MM_F32, 128, 8, 64, k=2000) == 1
+    assert hint(mm.MM_F16, 64, 8, 64, k=2000) == 0 and hint(mm.MM_BF16, 16, 8, 64, k=2000) == 1
     assert hint(mm.MM_BF16, 8, 4, 16) == 1 and hint(mm.MM_BF16, 7, 4, 16) == 0
     with pytest.raises(mm.MmError) as e:
         hint(mm.MM_BF16, 0, 8, 64)

@@ -134,11 +134,12 @@ def test_ramp_bit_exact(route, wdt):
 
 @pytest.mark.parametrize("wdt", DTYPES)
 def test_ramp_bit_exact_pipelined_grouped(wdt):
-    """k = 512 takes the pipelined MFMA grouped kernel for bf16 and for f16
-    weights (f16 split exactly into bf16 halves, activations into hi + lo);
-    on ramp inputs every term is exact, so the output matches the rounded
-    oracle bit for bit. More than 128 rows land on one expert, so full
-    128-row tiles (eight row groups) are covered too."""
+    """k = 512 takes the pipelined MFMA grouped kernel for every weight dtype
+    (bf16 as stored, f16 split exactly into bf16 halves, f32 on 16x16x4 f32
+    MFMA; activations into bf16 hi + lo for the first two); on ramp inputs
+    every term is exact, so the output matches the rounded oracle bit for
+    bit. More than 128 rows land on one expert, so full 128-row tiles (eight
+    row groups) are covered too."""
     m, n, k, top_k, E = 150, 72, 512, 2, 2
     rng = np.random.default_rng(71)
     w = wl.ramp(E * n * k, 3).reshape(E, n, k)
@@ -148,8 +149,7 @@ def test_ramp_bit_exact_pipelined_grouped(wdt):
     _say(f"ramp pipelined grouped wdt={wl.DTYPE_NAMES[wdt]}")
     run = IdRun(case, route=1)
     rec = run.run()
-    want = mm.MM_KERNEL_ID_GROUPED_FMA if wdt == wl.F32 else mm.MM_KERNEL_ID_GROUPED_MFMA
-    assert rec.kernel == want, rec.kernel
+    assert rec.kernel == mm.MM_KERNEL_ID_GROUPED_MFMA, rec.kernel
     got = from_dev(run.out, np.float32).reshape(m * top_k, n)
     ref = oracle.round_to(wl.F32, run.oracle())
     np.testing.assert_array_equal(got, ref)
