@@ -191,6 +191,49 @@ __device__ __forceinline__ void store_c(const GemmArgs& a, int64_t b, int64_t m0
     }
 }
 
+// Epilogue through LDS for interior tiles (the whole 128 x 128 tile inside C,
+// ldc % 8 == 0, 16-byte aligned C): each wave's 64 x 64 piece goes to LDS in
+// two halves of 32 rows (row pitch 72 elements, so the 16 rows one write
+// instruction covers land in distinct banks) and leaves as 16-byte row
+// pieces, eight rows x 128 bytes per store instruction, instead of the
+// 16 rows x 32 bytes of the register layout. `stage` is block LDS of at least
+// 4 x 32 x 72 elements that no wave still reads; ends with a barrier.
+template <class T>
+__device__ __forceinline__ bool store_c_staged(const GemmArgs& a, int64_t b, int64_t m0, int64_t n0,
+                                               int wm, int wn, int lane, int wave,
+                                               const f32x4 (&acc)[4][4], uint16_t* stage) {
+    uint16_t* Cb = reinterpret_cast<uint16_t*>(a.C) + b * a.sc;
+    const bool fits = m0 + GBM <= a.m && n0 + GBN <= a.n && (a.ldc & 7) == 0 &&
+                      (reinterpret_cast<uintptr_t>(Cb) & 15) == 0;
+    if (!fits) return false;  // block-uniform
+    uint16_t* stg = stage + wave * (32 * 72);
+    uint16_t* C = Cb + (m0 + wm * 64) * a.ldc + n0 + wn * 64;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x4& v4 = acc[2 * h + ii][j];
+                u32x2 v;
+                v[0] = (uint32_t)narrow(T{}, v4[0]) | ((uint32_t)narrow(T{}, v4[1]) << 16);
+                v[1] = (uint32_t)narrow(T{}, v4[2]) | ((uint32_t)narrow(T{}, v4[3]) << 16);
+                *reinterpret_cast<u32x2*>(stg + (ii * 16 + (lane & 15)) * 72 + j * 16 + 4 * (lane >> 4)) = v;
+            }
+        }
+        // LDS instructions of one wave complete in order: the reads below see
+        // the writes above, and the next half's writes follow these reads.
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int r = p * 8 + (lane >> 3), c = (lane & 7) * 8;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * 72 + c);
+            *reinterpret_cast<u32x4*>(C + (int64_t)(h * 32 + r) * a.ldc + c) = v;
+        }
+    }
+    __syncthreads();  // the stage is free for the next item's tiles
+    return true;
+}
+
 // Block = 4 waves (2 x 2), tile 128 x 128 x 32, each wave 64 x 64 with
 // v_mfma_f32_16x16x32. Double-buffered LDS: k-tile kt+1 is fetched into
 // registers before tile kt is multiplied and stored to the other LDS buffer
@@ -248,7 +291,8 @@ __global__ __launch_bounds__(GThreads) void gemm_mfma_generic(GemmArgs a) {
             __syncthreads();
         }
 
-        store_c<T>(a, b, m0, n0, wm, wn, lane, acc);
+        if (!store_c_staged<T>(a, b, m0, n0, wm, wn, lane, wave, acc, &As[0][0]))
+            store_c<T>(a, b, m0, n0, wm, wn, lane, acc);
     }
 }
 
@@ -308,7 +352,9 @@ __global__ __launch_bounds__(GThreads) void gemm_mfma_shortk(GemmArgs a) {
                     for (int j = 0; j < 4; ++j) acc[i][j] = mfma16<T>(bf[j], af[i], acc[i][j]);
             }
         }
-        store_c<T>(a, b, m0, n0, wm, wn, lane, acc);
+        __syncthreads();  // every wave is done reading As before it holds the epilogue stage
+        if (!store_c_staged<T>(a, b, m0, n0, wm, wn, lane, wave, acc, &As[0][0]))
+            store_c<T>(a, b, m0, n0, wm, wn, lane, acc);
     }
 }
 
