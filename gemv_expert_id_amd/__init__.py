@@ -39,7 +39,7 @@ STATUS_NAMES = {
 
 # Every symbol include/mm.h declares.
 EXPORTS = [
-    "mm_gemm", "mm_gemv", "mm_id_query", "mm_id_route_hint", "mm_id_direct", "mm_id_map",
+    "mm_gemm", "mm_gemm_ex", "mm_gemv", "mm_id_query", "mm_id_route_hint", "mm_id_direct", "mm_id_map",
     "mm_id_grouped",
     "mm_id", "mm_capabilities", "mm_status_string", "mm_last_error",
     "mm_test_inject_resolve_failure", "mm_test_launch_count",
@@ -114,6 +114,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     vp = ctypes.c_void_p
     lib.mm_gemm.argtypes = [P(GemmDesc), Buf, Buf, Buf, vp, P(Receipt)]
     lib.mm_gemm.restype = st
+    lib.mm_gemm_ex.argtypes = [P(GemmDesc), ctypes.c_float, ctypes.c_float, Buf, Buf, Buf, vp,
+                               P(Receipt)]
+    lib.mm_gemm_ex.restype = st
     lib.mm_gemv.argtypes = [P(GemmDesc), Buf, Buf, Buf, vp, P(Receipt)]
     lib.mm_gemv.restype = st
     lib.mm_id_query.argtypes = [ctypes.c_int, P(IdParams), P(IdCapability)]
@@ -182,6 +185,15 @@ def id_params(m: int, n: int, k: int, top_k: int, n_experts: int, expert_stride_
 def mm_gemm(desc: GemmDesc, a: Buf, b: Buf, c: Buf, stream=None) -> Receipt:
     r = Receipt()
     _raise(load().mm_gemm(ctypes.byref(desc), a, b, c, _stream(stream), ctypes.byref(r)))
+    return r
+
+
+def mm_gemm_ex(desc: GemmDesc, alpha: float, beta: float, a: Buf, b: Buf, c: Buf,
+               stream=None) -> Receipt:
+    """C = alpha * op(A) op(B) + beta * C (beta == 0: old C unread)."""
+    r = Receipt()
+    _raise(load().mm_gemm_ex(ctypes.byref(desc), ctypes.c_float(alpha), ctypes.c_float(beta),
+                             a, b, c, _stream(stream), ctypes.byref(r)))
     return r
 
 

@@ -129,6 +129,7 @@ struct GemmPlan {
     const char* a;
     const char* b;
     char* c;
+    float alpha = 1.f, beta = 0.f;  // C = alpha * op(A) op(B) + beta * C_old
 };
 
 // Elements spanned by `nb` matrices of `rows` x `cols` with leading dimension
@@ -213,6 +214,8 @@ mm_status plan_gemm(const mm_gemm_desc* d, mm_buf a, mm_buf b, mm_buf c, GemmPla
 mmk::GemvArgs gemv_args(const GemmPlan& p) {
     mmk::GemvArgs g{};
     g.dtype = p.dt;
+    g.alpha = p.alpha;
+    g.beta = p.beta;
     g.k = p.k;
     g.batch = p.batch;
     g.out = p.c;
@@ -267,6 +270,8 @@ bool skinny_args(const GemmPlan& p, mmk::SkinnyArgs* g) {
         return false;
     *g = mmk::SkinnyArgs{};
     g->dtype = p.dt;
+    g->alpha = p.alpha;
+    g->beta = p.beta;
     g->k = p.k;
     g->batch = p.batch;
     g->out = p.c;
@@ -305,7 +310,7 @@ mm_status run_gemm(const GemmPlan& p, hipStream_t s, mm_receipt* r) {
     mm_status st = resolve("gemm");
     if (st != MM_OK) return st;
     mmk::GemmArgs g{p.a, p.b, p.c, p.m, p.n, p.k, p.lda, p.ldb, p.ldc, p.sa, p.sb, p.sc,
-                    p.batch, p.dt, p.ta, p.tb};
+                    p.batch, p.dt, p.ta, p.tb, p.alpha, p.beta};
     ++g_launches;
     int kernel = -1;
     st = finish(mmk::launch_gemm(g, s, &kernel), s, "gemm");
@@ -465,6 +470,15 @@ mmk::IdArgs fill_ptrs(mmk::IdArgs a, mm_buf weights, mm_buf input, mm_buf ids, m
     return a;
 }
 
+// Route choice: skinny, else GEMV, else tiled GEMM (see mm.h).
+mm_status dispatch_gemm(const GemmPlan& p, void* stream, mm_receipt* receipt) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    mmk::SkinnyArgs g;
+    if (skinny_args(p, &g)) return run_skinny(g, p.dt, s, receipt);
+    if (p.m == 1 || p.n == 1) return run_gemv(p, s, receipt);
+    return run_gemm(p, s, receipt);
+}
+
 }  // namespace
 
 extern "C" {
@@ -474,11 +488,17 @@ mm_status mm_gemm(const mm_gemm_desc* desc, mm_buf a, mm_buf b, mm_buf c, void* 
     GemmPlan p;
     mm_status st = plan_gemm(desc, a, b, c, &p);
     if (st != MM_OK) return st;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    mmk::SkinnyArgs g;
-    if (skinny_args(p, &g)) return run_skinny(g, p.dt, s, receipt);
-    if (p.m == 1 || p.n == 1) return run_gemv(p, s, receipt);
-    return run_gemm(p, s, receipt);
+    return dispatch_gemm(p, stream, receipt);
+}
+
+mm_status mm_gemm_ex(const mm_gemm_desc* desc, float alpha, float beta, mm_buf a, mm_buf b,
+                     mm_buf c, void* stream, mm_receipt* receipt) {
+    GemmPlan p;
+    mm_status st = plan_gemm(desc, a, b, c, &p);
+    if (st != MM_OK) return st;
+    p.alpha = alpha;
+    p.beta = beta;
+    return dispatch_gemm(p, stream, receipt);
 }
 
 mm_status mm_gemv(const mm_gemm_desc* desc, mm_buf a, mm_buf b, mm_buf c, void* stream,

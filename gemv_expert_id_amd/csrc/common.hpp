@@ -55,6 +55,16 @@ __device__ __forceinline__ uint16_t narrow(TBF16, float x) {
     return (uint16_t)(u >> 16);
 }
 
+// ---- output epilogue: alpha * acc + beta * C_old, rounded once ---------------
+// beta == 0 never reads the old value (its contents, NaN included, do not
+// matter); alpha == 1, beta == 0 returns exactly narrow(acc).
+template <class T>
+__device__ __forceinline__ typename T::store_t axpby(float acc, float alpha, float beta,
+                                                     const typename T::store_t* old) {
+    const float v = beta != 0.f ? __builtin_fmaf(alpha, acc, beta * widen(T{}, *old)) : alpha * acc;
+    return narrow(T{}, v);
+}
+
 // ---- unpack a 16-byte chunk into f32 ---------------------------------------
 // 8 x 16-bit elements -> 8 floats (exact).
 __device__ __forceinline__ void unpack8(TF16, u32x4 v, float* f) {

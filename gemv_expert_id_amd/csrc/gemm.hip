@@ -177,22 +177,23 @@ __device__ __forceinline__ void store_c(const GemmArgs& a, int64_t b, int64_t m0
         for (int j = 0; j < 4; ++j) {
             const int64_t gn = n0 + wn * 64 + j * 16 + 4 * (lane >> 4);
             uint16_t* dst = C + gm * a.ldc + gn;
-            if (gn + 4 <= a.n && (a.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(dst) & 7) == 0) {
+            if (a.beta == 0.f && gn + 4 <= a.n && (a.ldc & 3) == 0 &&
+                (reinterpret_cast<uintptr_t>(dst) & 7) == 0) {
                 u32x2 v;
-                v[0] = (uint32_t)narrow(T{}, acc[i][j][0]) | ((uint32_t)narrow(T{}, acc[i][j][1]) << 16);
-                v[1] = (uint32_t)narrow(T{}, acc[i][j][2]) | ((uint32_t)narrow(T{}, acc[i][j][3]) << 16);
+                v[0] = (uint32_t)narrow(T{}, a.alpha * acc[i][j][0]) | ((uint32_t)narrow(T{}, a.alpha * acc[i][j][1]) << 16);
+                v[1] = (uint32_t)narrow(T{}, a.alpha * acc[i][j][2]) | ((uint32_t)narrow(T{}, a.alpha * acc[i][j][3]) << 16);
                 *reinterpret_cast<u32x2*>(dst) = v;
             } else {
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    if (gn + q < a.n) dst[q] = narrow(T{}, acc[i][j][q]);
+                    if (gn + q < a.n) dst[q] = axpby<T>(acc[i][j][q], a.alpha, a.beta, dst + q);
             }
         }
     }
 }
 
 // Epilogue through LDS for interior tiles (the whole 128 x 128 tile inside C,
-// ldc % 8 == 0, 16-byte aligned C): each wave's 64 x 64 piece goes to LDS in
+// ldc % 8 == 0, 16-byte aligned C, beta == 0): each wave's 64 x 64 piece goes to LDS in
 // two halves of 32 rows (row pitch 72 elements, so the 16 rows one write
 // instruction covers land in distinct banks) and leaves as 16-byte row
 // pieces, eight rows x 128 bytes per store instruction, instead of the
@@ -203,7 +204,7 @@ __device__ __forceinline__ bool store_c_staged(const GemmArgs& a, int64_t b, int
                                                int wm, int wn, int lane, int wave,
                                                const f32x4 (&acc)[4][4], uint16_t* stage) {
     uint16_t* Cb = reinterpret_cast<uint16_t*>(a.C) + b * a.sc;
-    const bool fits = m0 + GBM <= a.m && n0 + GBN <= a.n && (a.ldc & 7) == 0 &&
+    const bool fits = a.beta == 0.f && m0 + GBM <= a.m && n0 + GBN <= a.n && (a.ldc & 7) == 0 &&
                       (reinterpret_cast<uintptr_t>(Cb) & 15) == 0;
     if (!fits) return false;  // block-uniform
     uint16_t* stg = stage + wave * (32 * 72);
@@ -216,8 +217,8 @@ __device__ __forceinline__ bool store_c_staged(const GemmArgs& a, int64_t b, int
             for (int j = 0; j < 4; ++j) {
                 const f32x4& v4 = acc[2 * h + ii][j];
                 u32x2 v;
-                v[0] = (uint32_t)narrow(T{}, v4[0]) | ((uint32_t)narrow(T{}, v4[1]) << 16);
-                v[1] = (uint32_t)narrow(T{}, v4[2]) | ((uint32_t)narrow(T{}, v4[3]) << 16);
+                v[0] = (uint32_t)narrow(T{}, a.alpha * v4[0]) | ((uint32_t)narrow(T{}, a.alpha * v4[1]) << 16);
+                v[1] = (uint32_t)narrow(T{}, a.alpha * v4[2]) | ((uint32_t)narrow(T{}, a.alpha * v4[3]) << 16);
                 *reinterpret_cast<u32x2*>(stg + (ii * 16 + (lane & 15)) * 72 + j * 16 + 4 * (lane >> 4)) = v;
             }
         }
@@ -568,10 +569,19 @@ __global__ __launch_bounds__(LThreads, 1) void gemm_mfma_large(GemmArgs a) {
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const int64_t gn = n0 + wn * 128 + j * 32 + g * 8 + lh * 4;
-                    u32x2 v;
-                    v[0] = (uint32_t)narrow(T{}, acc[i][j][4 * g]) | ((uint32_t)narrow(T{}, acc[i][j][4 * g + 1]) << 16);
-                    v[1] = (uint32_t)narrow(T{}, acc[i][j][4 * g + 2]) | ((uint32_t)narrow(T{}, acc[i][j][4 * g + 3]) << 16);
-                    *reinterpret_cast<u32x2*>(C + gm * a.ldc + gn) = v;
+                    uint16_t* dst = C + gm * a.ldc + gn;
+                    if (a.beta == 0.f) {
+                        u32x2 v;
+                        v[0] = (uint32_t)narrow(T{}, a.alpha * acc[i][j][4 * g]) |
+                               ((uint32_t)narrow(T{}, a.alpha * acc[i][j][4 * g + 1]) << 16);
+                        v[1] = (uint32_t)narrow(T{}, a.alpha * acc[i][j][4 * g + 2]) |
+                               ((uint32_t)narrow(T{}, a.alpha * acc[i][j][4 * g + 3]) << 16);
+                        *reinterpret_cast<u32x2*>(dst) = v;
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            dst[q] = axpby<T>(acc[i][j][4 * g + q], a.alpha, a.beta, dst + q);
+                    }
                 }
             }
         }
@@ -666,7 +676,7 @@ __global__ __launch_bounds__(256) void gemm_f32_fma(GemmArgs a) {
 #pragma unroll
             for (int c = 0; c < R; ++c) {
                 const int64_t gj = n0 + tx * R + c;
-                if (gj < a.n) C[gi * a.ldc + gj] = acc[r][c];
+                if (gj < a.n) C[gi * a.ldc + gj] = axpby<TF32>(acc[r][c], a.alpha, a.beta, &C[gi * a.ldc + gj]);
             }
         }
     }

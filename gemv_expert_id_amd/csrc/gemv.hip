@@ -29,9 +29,10 @@ __device__ __forceinline__ void unpack(u32x4 v, float* f) {
 }
 
 template <class T>
-__device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
+__device__ __forceinline__ void store_out(const GemvArgs& a, int64_t idx, float v) {
     using S = typename T::store_t;
-    reinterpret_cast<S*>(out)[idx] = narrow(T{}, v);
+    S* o = reinterpret_cast<S*>(a.out) + idx;
+    *o = axpby<T>(v, a.alpha, a.beta, o);
 }
 
 // Row form with 16-byte loads. Requires k % Elems16 == 0, ld and the batch
@@ -102,7 +103,7 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_vec(GemvArgs a) {
 #pragma unroll
         for (int r = 0; r < R; ++r)
             if (lane == r && o0 + r < a.rows)
-                store_out<T>(a.out, b * a.out_bstride + (o0 + r) * a.out_inc, acc[r]);
+                store_out<T>(a, b * a.out_bstride + (o0 + r) * a.out_inc, acc[r]);
     }
 }
 
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_scalar(GemvArgs a) {
 #pragma unroll
         for (int r = 0; r < R; ++r)
             if (lane == r && o0 + r < a.rows)
-                store_out<T>(a.out, b * a.out_bstride + (o0 + r) * a.out_inc, acc[r]);
+                store_out<T>(a, b * a.out_bstride + (o0 + r) * a.out_inc, acc[r]);
     }
 }
 
@@ -189,7 +190,7 @@ __global__ __launch_bounds__(kThreads) void gemv_cols(GemvArgs a) {
                 float s = part[0][idx];
 #pragma unroll
                 for (int w = 1; w < kWaves; ++w) s += part[w][idx];
-                if (o0 + q < a.rows) store_out<T>(a.out, b * a.out_bstride + (o0 + q) * a.out_inc, s);
+                if (o0 + q < a.rows) store_out<T>(a, b * a.out_bstride + (o0 + q) * a.out_inc, s);
             }
         }
         __syncthreads();

@@ -27,6 +27,7 @@ struct GemvArgs {
     int64_t batch;
     int32_t dtype;       // 0 f32, 1 f16, 2 bf16
     int32_t col_form;    // 1: M(o, p) = mat[p * ld + o]
+    float alpha, beta;   // out = alpha * sum + beta * out_old (beta == 0: out_old unread)
 };
 // Launchers enqueue one kernel on `s`; `kernel` receives its mm_kernel code.
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t s, int* kernel);
@@ -44,6 +45,7 @@ struct SkinnyArgs {
     int64_t batch;
     int64_t w_bytes, x_bytes;  // extent of one batch's W and X (each below 2^31)
     int32_t dtype;
+    float alpha, beta;   // out = alpha * sum + beta * out_old (beta == 0: out_old unread)
 };
 hipError_t launch_gemv_wide(const SkinnyArgs& a, hipStream_t s, int* kernel);
 
@@ -58,6 +60,7 @@ struct GemmArgs {
     int64_t batch;
     int32_t dtype;
     int32_t ta, tb;
+    float alpha, beta;   // C = alpha * op(A) op(B) + beta * C_old (beta == 0: C_old unread)
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, int* kernel);
 

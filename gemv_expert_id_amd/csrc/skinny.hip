@@ -184,7 +184,7 @@ __global__ __launch_bounds__(SThreads) void gemv_wide(SkinnyArgs a) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int64_t ow = w0 + 4 * g + q;
-                    if (ow < a.nw) o[ow * a.out_sw] = narrow(T{}, acc[q]);
+                    if (ow < a.nw) o[ow * a.out_sw] = axpby<T>(acc[q], a.alpha, a.beta, o + ow * a.out_sw);
                 }
             }
         }

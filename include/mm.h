@@ -156,6 +156,19 @@ typedef struct {
 mm_status mm_gemm(const mm_gemm_desc *desc, mm_buf a, mm_buf b, mm_buf c, void *stream,
                   mm_receipt *receipt);
 
+/*
+ * Same dispatch with an output epilogue (tract-metal `dispatch_metal_mlx_gemm`
+ * function constants `do_axpby` and `use_out_source`, present but switched off
+ * there; rlx-metal `encode_mps_sgemm_t` passes alpha = 1, beta = 0):
+ *   C[b][i][j] = alpha * sum_p op(A)[b][i][p] * op(B)[b][p][j] + beta * C_old[b][i][j]
+ * computed in f32 from the f32 accumulator and the old value as stored,
+ * rounded once to the dtype. With beta == 0 the old C is never read (its
+ * contents, NaN included, do not matter); mm_gemm is alpha = 1, beta = 0.
+ * Same routes, validation and errors as mm_gemm.
+ */
+mm_status mm_gemm_ex(const mm_gemm_desc *desc, float alpha, float beta, mm_buf a, mm_buf b,
+                     mm_buf c, void *stream, mm_receipt *receipt);
+
 /* The GEMV route only; INVALID_ARGUMENT unless m == 1 or n == 1
  * (tract-metal `dispatch_metal_mlx_gemv`). Same validation as mm_gemm. */
 mm_status mm_gemv(const mm_gemm_desc *desc, mm_buf a, mm_buf b, mm_buf c, void *stream,

@@ -6,8 +6,10 @@ code with the GPU library (``gemv_expert_id_amd``) and neither imports the
 other; the seeded input generators in ``workloads`` serve both.
 
 The arithmetic lives in ``mm_oracle.c`` (plain C, fp64 accumulation, triple
-loops in ascending contraction order). This module only builds that file
-with gcc, loads it with ctypes and marshals numpy arrays.
+loops in ascending contraction order). This module builds that file with gcc,
+loads it with ctypes and marshals numpy arrays; the one exception is the
+output epilogue ``gemm_axpby`` (alpha * product + beta * C_old), two float64
+numpy operations written out here.
 
 Parity of every function here is pinned by the CPU tests in
 ``tests/test_oracle_pins.py`` (worked examples printed on the pages, closed
@@ -115,6 +117,18 @@ def gemm(dtype: int, batch: int, m: int, n: int, k: int, trans_a: bool, trans_b:
                           stride_a, stride_b, off_a, off_b, _ptr(A), _ptr(B), _ptr(C), nthreads)
     _check(rc, "gemm")
     return C
+
+
+def gemm_axpby(alpha: float, beta: float, product, c_old) -> np.ndarray:
+    """Output epilogue (tract-metal mlx_gemm/mod.rs, `dispatch_metal_mlx_gemm`:
+    function constants `do_axpby` and `use_out_source`): alpha * product +
+    beta * C_old in float64, unrounded. `product` is a result of gemm() or
+    gemm_at(); `c_old` the decoded old outputs at the same positions. With
+    beta == 0 the old values take no part (a NaN there does not propagate)."""
+    out = float(alpha) * np.asarray(product, dtype=np.float64)
+    if beta != 0:
+        out = out + float(beta) * np.asarray(c_old, dtype=np.float64)
+    return out
 
 
 def gemm_at(dtype: int, k: int, trans_a: bool, trans_b: bool, lda: int, ldb: int,

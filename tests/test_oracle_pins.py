@@ -131,6 +131,37 @@ def test_rank1_closed_form(dt, k):
     np.testing.assert_array_equal(c[0], k * np.outer(u, v))
 
 
+# ----------------------------------------------------------------------------
+# Output epilogue alpha * A.B + beta * C_old (tract-metal `dispatch_metal_mlx_gemm`
+# do_axpby / use_out_source): identity and rank-1 products give closed forms.
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("alpha,beta", [(2.0, -0.5), (-1.25, 3.0), (0.0, 1.0), (1.0, 0.0)])
+def test_axpby_closed_forms(alpha, beta):
+    """I.B scaled by alpha plus C_old scaled by beta, elementwise, and a rank-1
+    product k u v^T: catches a swapped alpha/beta, a dropped term or a sign."""
+    rng = np.random.default_rng(13)
+    m, n = 5, 7
+    b_log = np.round(rng.uniform(-4, 4, (1, m, n)) * 8) / 8
+    c_old = np.round(rng.uniform(-4, 4, (1, m, n)) * 8) / 8
+    prod = _gemm(wl.make_gemm_case(wl.F32, np.eye(m)[None], b_log, False, False))
+    np.testing.assert_array_equal(oracle.gemm_axpby(alpha, beta, prod, c_old),
+                                  alpha * b_log + beta * c_old)
+    u = rng.integers(-8, 9, m) / 4.0
+    v = rng.integers(-8, 9, n) / 8.0
+    k = 9
+    prod = _gemm(wl.make_gemm_case(wl.F32, np.repeat(u[:, None], k, 1)[None],
+                                   np.repeat(v[None, :], k, 0)[None], False, False))
+    np.testing.assert_array_equal(oracle.gemm_axpby(alpha, beta, prod, c_old),
+                                  alpha * k * np.outer(u, v)[None] + beta * c_old)
+
+
+def test_axpby_beta_zero_ignores_old_values():
+    prod = np.arange(6.0).reshape(1, 2, 3)
+    got = oracle.gemm_axpby(1.5, 0.0, prod, np.full((1, 2, 3), np.nan))
+    np.testing.assert_array_equal(got, 1.5 * prod)
+
+
 @pytest.mark.parametrize("dt,k", [(wl.F32, 1000), (wl.F16, 300), (wl.BF16, 200)])
 def test_arithmetic_series(dt, k):
     """A = 1, B[p, j] = p (B stored [n, k]): every output is k(k-1)/2."""
