@@ -83,7 +83,8 @@ class Timer:
         self.stream = stream
         self.use_graph = use_graph
 
-    def time(self, step, n_rot, steps, warmup):
+    def time(self, step, n_rot, steps, warmup, repeats=5):
+        """ms per step: the median over `repeats` timed runs of `steps` calls."""
         torch = self.torch
         with torch.cuda.stream(self.stream):
             for i in range(warmup):
@@ -97,14 +98,19 @@ class Timer:
                         step(i)
                 g.replay()
                 torch.cuda.synchronize()
-                t0 = torch.cuda.Event(enable_timing=True)
-                t1 = torch.cuda.Event(enable_timing=True)
-                t0.record(self.stream)
-                for _ in range(reps):
-                    g.replay()
-                t1.record(self.stream)
-                torch.cuda.synchronize()
                 n = reps * n_rot
+                runs = []
+                for _ in range(repeats):
+                    t0 = torch.cuda.Event(enable_timing=True)
+                    t1 = torch.cuda.Event(enable_timing=True)
+                    t0.record(self.stream)
+                    for _ in range(reps):
+                        g.replay()
+                    t1.record(self.stream)
+                    torch.cuda.synchronize()
+                    runs.append(t0.elapsed_time(t1) / n)
+                runs.sort()
+                return runs[len(runs) // 2], n
             else:
                 t0 = torch.cuda.Event(enable_timing=True)
                 t1 = torch.cuda.Event(enable_timing=True)
