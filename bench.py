@@ -15,7 +15,8 @@ rotates through enough copies of its operands that a buffer is reused only
 after >= 1 GiB of other traffic (more than the 256 MB Infinity Cache). The
 rotated calls are captured once in a HIP graph and the graph is replayed;
 the time per step comes from HIP events recorded on the stream the kernels
-run on, bracketed by device synchronisation.
+run on, bracketed by device synchronisation, and is the median of five such
+timed runs.
 
 cpu_baseline: the CPU oracle (test infrastructure, fp64 triple loops) timed
 on this host on the same decode GEMV, repeated to about ten seconds of work.
