@@ -702,6 +702,68 @@ const void* pick_mfma(bool ta, bool tb, bool vec, bool shortk) {
     return nullptr;
 }
 
+// ---------------------------------------------------------------------------
+// Small f32 products (k <= 128, at most 1024 tiles of 16 x 16 per batch
+// item): one wave per 16 x 16 tile on f32 MFMA 16x16x4. Latency, not
+// throughput, bounds these: every operand element of the tile is requested
+// at once (one memory round trip; contraction indices past k read through an
+// offset beyond the buffer resource's range and come back as zero), then
+// k / 4 MFMAs run in four independent chains that are summed in a fixed
+// order. Lane l supplies A(m0 + l % 16, 4t + l / 16) and B(4t + l / 16,
+// n0 + l % 16) to MFMA t and ends with C rows m0 + 4 (l / 16) + q of column
+// n0 + l % 16.
+// ---------------------------------------------------------------------------
+constexpr int SFK = 128;
+
+template <bool TA, bool TB>
+__global__ __launch_bounds__(kWave) void gemm_f32_mfma_small(GemmArgs a) {
+    constexpr uint32_t kOff = 0x80000000u;
+    const int lane = threadIdx.x;
+    const int r = lane & 15, g = lane >> 4;
+    const int64_t tiles_n = (a.n + 15) / 16;
+    const int64_t m0 = (int64_t)(blockIdx.x / tiles_n) * 16, n0 = (int64_t)(blockIdx.x % tiles_n) * 16;
+    const int64_t i = m0 + r < a.m ? m0 + r : a.m - 1;
+    const int64_t j = n0 + r < a.n ? n0 + r : a.n - 1;
+    const int64_t span_a = TA ? (a.k - 1) * a.lda + a.m : (a.m - 1) * a.lda + a.k;
+    const int64_t span_b = TB ? (a.n - 1) * a.ldb + a.k : (a.k - 1) * a.ldb + a.n;
+    for (int64_t b = blockIdx.y; b < a.batch; b += gridDim.y) {
+        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(reinterpret_cast<const float*>(a.A) + b * a.sa), (short)0,
+            (int)(span_a * 4), 0x00020000);
+        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(reinterpret_cast<const float*>(a.B) + b * a.sb), (short)0,
+            (int)(span_b * 4), 0x00020000);
+        float av[SFK / 4], bv[SFK / 4];
+#pragma unroll
+        for (int t = 0; t < SFK / 4; ++t) {
+            const int64_t p = 4 * t + g;
+            const bool live = p < a.k;
+            const int64_t ea = TA ? p * a.lda + i : i * a.lda + p;
+            const int64_t eb = TB ? j * a.ldb + p : p * a.ldb + j;
+            av[t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                        ra, live ? (uint32_t)(ea * 4) : kOff, 0, 0));
+            bv[t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                        rb, live ? (uint32_t)(eb * 4) : kOff, 0, 0));
+        }
+        f32x4 acc[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < SFK / 4; ++t)
+            acc[t & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[t], bv[t], acc[t & 3], 0, 0, 0);
+        const f32x4 sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        float* C = reinterpret_cast<float*>(a.C) + b * a.sc;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t row = m0 + 4 * g + q, col = n0 + r;
+            if (row < a.m && col < a.n) {
+                float* dst = C + row * a.ldc + col;
+                *dst = axpby<TF32>(sum[q], a.alpha, a.beta, dst);
+            }
+        }
+    }
+}
+
 template <int TILE>
 const void* pick_f32(bool ta, bool tb) {
     if (!ta && !tb) return reinterpret_cast<const void*>(&gemm_f32_fma<false, false, TILE>);
@@ -716,6 +778,17 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, int* kernel) {
     void* args[] = {const_cast<GemmArgs*>(&a)};
     const unsigned gy = (unsigned)(a.batch < 65535 ? a.batch : 65535);
     if (a.dtype == 0) {
+        const int64_t t16 = ((a.m + 15) / 16) * ((a.n + 15) / 16);
+        const int64_t span_a = a.ta ? (a.k - 1) * a.lda + a.m : (a.m - 1) * a.lda + a.k;
+        const int64_t span_b = a.tb ? (a.n - 1) * a.ldb + a.k : (a.k - 1) * a.ldb + a.n;
+        if (a.k <= SFK && t16 <= 1024 && span_a < (1ll << 29) && span_b < (1ll << 29)) {
+            const void* fn = !a.ta && !a.tb ? (const void*)&gemm_f32_mfma_small<false, false>
+                             : !a.ta        ? (const void*)&gemm_f32_mfma_small<false, true>
+                             : !a.tb        ? (const void*)&gemm_f32_mfma_small<true, false>
+                                            : (const void*)&gemm_f32_mfma_small<true, true>;
+            *kernel = MM_KERNEL_GEMM_F32_SMALL;
+            return hipLaunchKernel(fn, dim3((unsigned)t16, gy), dim3(kWave), args, 0, s);
+        }
         // 64 x 64 tiles, or 32 x 32 when that leaves fewer blocks than CUs.
         const int64_t t64 = ((a.m + 63) / 64) * ((a.n + 63) / 64);
         const bool small = t64 * a.batch < 256;

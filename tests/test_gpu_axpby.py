@@ -101,7 +101,8 @@ def test_axpby_every_route(dt, shape, alpha, beta):
     if kernel is not None:
         assert rec.kernel == kernel, rec.kernel
     if dt == wl.F32 and route == mm.MM_ROUTE_GEMM:
-        assert rec.kernel == mm.MM_KERNEL_GEMM_F32
+        small = k <= 128 and ((m + 15) // 16) * ((n + 15) // 16) <= 1024
+        assert rec.kernel == (mm.MM_KERNEL_GEMM_F32_SMALL if small else mm.MM_KERNEL_GEMM_F32)
 
 
 @pytest.mark.parametrize("dt", [wl.F16, wl.BF16])

@@ -70,6 +70,26 @@ def test_lm_head_shape_f32():
 
 
 @pytest.mark.parametrize("ta,tb", LAYOUTS)
+@pytest.mark.parametrize("shape", [(1, 17, 33, 1), (3, 100, 70, 77), (1, 128, 128, 128),
+                                   (2, 5, 513, 3), (1, 512, 512, 4)])
+def test_f32_small_kernel(ta, tb, shape):
+    """f32 with k <= 128 and at most 1024 tiles of 16 x 16: one wave per tile on
+    f32 MFMA; ragged m, n, k (including k = 1 and k % 4 != 0), padded leading
+    dimensions and offsets; random operands to the tolerance, ramp bit for bit."""
+    b, m, n, k = shape
+    _say(f"f32 small kernel ta={ta} tb={tb} shape={shape}")
+    case = wl.random_gemm_case(90, wl.F32, b, m, n, k, ta, tb, dist="uniform",
+                               lda=(m if ta else k) + 3, ldb=(k if tb else n) + 5, off_a=2, off_b=1)
+    rec = check_gemm(case, what=f"{shape}")
+    assert rec.kernel == mm.MM_KERNEL_GEMM_F32_SMALL, rec.kernel
+    a_shape = (b, k, m) if ta else (b, m, k)
+    b_shape = (b, n, k) if tb else (b, k, n)
+    ramp = wl.make_gemm_case(wl.F32, wl.ramp(int(np.prod(a_shape)), 1).reshape(a_shape),
+                             wl.ramp(int(np.prod(b_shape)), 2).reshape(b_shape), ta, tb)
+    check_gemm(ramp, exact=True, what=f"ramp {shape}")
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
 def test_f32_wide_tiles_ragged(ta, tb):
     """Enough 64 x 64 tiles for the wide f32 form (smaller problems use 32 x 32),
     ragged in m, n and k."""
