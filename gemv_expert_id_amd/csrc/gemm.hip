@@ -363,26 +363,31 @@ __global__ __launch_bounds__(GThreads) void gemm_mfma_shortk(GemmArgs a) {
 // Large f16 / bf16 kernel: C = A . B^T with A [m,k] and B [n,k] both
 // K-contiguous, m % 256 == n % 256 == 0, k % 128 == 0, k >= 256, 16-byte aligned.
 //
-// Block = 4 waves (one per SIMD), tile 256 x 256, each wave 128 x 128 with
-// v_mfma_f32_32x32x16 (16 accumulators of 16 f32, held in AGPRs). A 128 x 128
-// wave tile halves the LDS fragment reads per MFMA compared with 128 x 64.
+// Block = 4 waves (one per SIMD), tile 256 x 256, each wave 128 x 128 as 8 x 8
+// fragments of 16 x 16 (v_mfma_f32_16x16x32, 64 accumulators of 4 f32 in
+// AGPRs). A 128 x 128 wave tile halves the LDS fragment reads per MFMA
+// compared with 128 x 64.
 //
 // Operands go from global memory straight into LDS (buffer_load ... lds, no
 // VGPR staging) in k-tiles of 32: four LDS stages of 32 KiB (A 16 KiB, B 16 KiB).
 // One DMA instruction fills 1 KiB = 16 tile rows x 64 bytes; lane i fetches
 // the global chunk that belongs at LDS slot i, so the XOR swizzle (chunk c of
 // row r at slot c ^ ((r >> 2) & 3)) costs nothing on the write side and the
-// fragment reads of 8 or 16 consecutive rows hit distinct banks.
+// fragment reads of 16 consecutive rows hit distinct banks.
 //
-// Per k-tile kt (stage kt % 4), each wave runs two groups of 16 MFMAs (k 0-15
-// and 16-31). Fragments for the next group are read from LDS while the
-// current group runs. Between the two groups sits the only barrier of the
-// k-tile: after it tile kt+1 is resident and stage kt % 4 is free, so the DMA
-// of tile kt+4 into it starts there. Its eight instructions are spread one
-// per four MFMAs over the next two groups (a burst would fill the address
-// queue and stall MFMA issue behind it); tile kt+4 is needed three barriers
-// later. Loops are unrolled by the stage count so every LDS offset, stage and
-// wait count is a compile-time constant.
+// Per k-tile kt (stage kt % 4), each wave runs two groups of 32 MFMAs: A rows
+// 0-63 of its wave tile, then rows 64-127, each against all eight B
+// fragments. The second half's A fragments are read while the first group
+// runs. Between the two groups sits the only barrier of the k-tile: after it
+// tile kt+1 is resident and stage kt % 4 is free, so the next tile's first A
+// half and its B fragments (into the other B register set) are read, and
+// the DMA of tile kt+4 into the freed stage starts. Its eight instructions
+// are spread one per eight MFMAs over the next two groups (a burst would
+// fill the address queue and stall MFMA issue behind it); tile kt+4 is
+// needed three barriers later. Loops are unrolled by the stage count so every
+// LDS offset, stage and wait count is a compile-time constant. In same-run
+// comparisons the 16x16x32 form beat the 32x32x16 form of the same pipeline
+// by about 4% on 8192^3.
 //
 // Tile order: groups of 4 tile-rows, column-major inside a group, each XCD
 // (blockIdx % 8) taking a contiguous run, so resident blocks on one XCD share
@@ -409,16 +414,6 @@ template <bool V> using bc = std::integral_constant<bool, V>;
 constexpr int wait_vm_lgkm0(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4); }
 
 __device__ __forceinline__ int lswz(int r) { return (r >> 2) & 3; }
-
-template <class T>
-__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
-    if constexpr (T::code == 1)
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-    else
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
 
 #define MM_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
@@ -451,7 +446,9 @@ __global__ __launch_bounds__(LThreads, 1) void gemm_mfma_large(GemmArgs a) {
     const int chunk = (lane % LCPR) ^ lswz(lane / LCPR);
     const int voa = ((w * 64 + lane / LCPR) * lda + chunk * 8) * 2;
     const int vob = ((w * 64 + lane / LCPR) * ldb + chunk * 8) * 2;
-    const int lr = lane & 31, lh = lane >> 5;
+    // Fragment reads: lane -> row lane%16 of a 16-row slab, chunk lane/16.
+    const int lr = lane & 15, lq = lane >> 4;
+    const int foff = lr * LBK + ((lq ^ lswz(lr)) << 3);
 
     for (int64_t b = blockIdx.y; b < a.batch; b += gridDim.y) {
         const uint16_t* A = reinterpret_cast<const uint16_t*>(a.A) + b * a.sa + m0 * a.lda;
@@ -474,60 +471,62 @@ __global__ __launch_bounds__(LThreads, 1) void gemm_mfma_large(GemmArgs a) {
                                                          (j * LRPI * ldb + kt * LBK) * 2, 0, 0);
             }
         };
-        f32x16 acc[4][4];
+        f32x4 acc[8][8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // A fragments of half hh (wave rows hh*64 + 16i) / all 8 B fragments of a stage.
+        auto rda = [&](int stage, int hh, u32x4 (&fa)[4]) {
+            const uint16_t* sa = lds + stage * LSTAGE_H + (wm * 128 + hh * 64) * LBK;
 #pragma unroll
-                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-        // Fragments of group ks (k 16*ks .. +16) of a stage: lane -> row lane%32
-        // of each 32-row slab, chunk 2*ks + lane/32.
-        auto rd = [&](int stage, int ks, u32x4 (&fa)[4], u32x4 (&fb)[4]) {
-            const uint16_t* sa = lds + stage * LSTAGE_H + wm * 128 * LBK;
+            for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const u32x4*>(sa + i * 16 * LBK + foff);
+        };
+        auto rdb = [&](int stage, u32x4 (&fb)[8]) {
             const uint16_t* sb = lds + stage * LSTAGE_H + LBM * LBK + wn * 128 * LBK;
-            const int off = lr * LBK + (((2 * ks + lh) ^ lswz(lr)) << 3);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const u32x4*>(sa + i * 32 * LBK + off);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) fb[j] = *reinterpret_cast<const u32x4*>(sb + j * 32 * LBK + off);
+            for (int j = 0; j < 8; ++j) fb[j] = *reinterpret_cast<const u32x4*>(sb + j * 16 * LBK + foff);
         };
         // D[n][m] = sum_k B(n,k) A(m,k): the lane's four consecutive values run along n.
-        auto mm = [&](const u32x4 (&fa)[4], const u32x4 (&fb)[4]) {
+        auto mm = [&](int hh, const u32x4 (&fa)[4], const u32x4 (&fb)[8]) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = mfma32<T>(fb[j], fa[i], acc[i][j]);
+                for (int j = 0; j < 8; ++j) acc[hh * 4 + i][j] = mfma16<T>(fb[j], fa[i], acc[hh * 4 + i][j]);
         };
-        // Scheduling of one group: its 8 fragment reads first, then 16 MFMAs
-        // with a DMA instruction after every fourth when ndma == 4.
-        auto weave = [&](int ndma) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        // Scheduling of one group: its NDS fragment reads first, then 32 MFMAs
+        // with a DMA instruction after every eighth when ndma == 4.
+        auto weave = [&](auto NDS, int ndma) {
+            __builtin_amdgcn_sched_group_barrier(0x100, decltype(NDS)::value, 0);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
                 if (q < ndma) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
             }
         };
-        u32x4 fa0[4], fb0[4], fa1[4], fb1[4];
-        // One k-tile. S_: stage (kt % 4); P1: finish tile kt+3 (second half);
-        // NEXT: tile kt+1 exists; DMA0: start tile kt+4; VM: DMA instructions
-        // allowed in flight after tile kt+1's at the barrier.
+        u32x4 fa0[4], fa1[4], fb0[8], fb1[8];
+        // One k-tile. S_: stage (kt % 4), whose B fragments sit in fb0 (even
+        // stage) or fb1; P1: finish tile kt+3 (second half); NEXT: tile kt+1
+        // exists; DMA0: start tile kt+4; VM: DMA instructions allowed in
+        // flight after tile kt+1's at the barrier.
         auto ktile = [&](auto S_, auto P1, auto NEXT, auto DMA0, auto VM, int kt) {
             constexpr int s = decltype(S_)::value;
-            rd(s, 1, fa1, fb1);
+            auto& fb = (s % 2 == 0) ? fb0 : fb1;
+            auto& fbn = (s % 2 == 0) ? fb1 : fb0;
+            rda(s, 1, fa1);
             if constexpr (decltype(P1)::value) dma_half((s + 3) % LSTAGES, kt + 3, 1);
-            mm(fa0, fb0);
-            weave(decltype(P1)::value ? 4 : 0);
+            mm(0, fa0, fb);
+            weave(ic<4>{}, decltype(P1)::value ? 4 : 0);
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (decltype(NEXT)::value) {
                 __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(decltype(VM)::value));
                 __builtin_amdgcn_s_barrier();
-                rd((s + 1) % LSTAGES, 0, fa0, fb0);
+                rda((s + 1) % LSTAGES, 0, fa0);
+                rdb((s + 1) % LSTAGES, fbn);
                 if constexpr (decltype(DMA0)::value) dma_half(s, kt + LSTAGES, 0);
             }
-            mm(fa1, fb1);
-            weave(decltype(DMA0)::value ? 4 : 0);
+            mm(1, fa1, fb);
+            weave(ic<decltype(NEXT)::value ? 12 : 0>{}, decltype(DMA0)::value ? 4 : 0);
             __builtin_amdgcn_sched_barrier(0);
         };
 
@@ -539,7 +538,8 @@ __global__ __launch_bounds__(LThreads, 1) void gemm_mfma_large(GemmArgs a) {
         }
         __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(LLPS * (LSTAGES - 1)));
         __builtin_amdgcn_s_barrier();
-        rd(0, 0, fa0, fb0);
+        rda(0, 0, fa0);
+        rdb(0, fb0);
         constexpr int VMS = LLPS * (LSTAGES - 2);  // steady state: tiles kt+2, kt+3 in flight
         // First round: tile 3 went out whole, so no second half at kt = 0.
         ktile(ic<0>{}, bc<false>{}, bc<true>{}, bc<true>{}, ic<VMS>{}, 0);
@@ -559,29 +559,25 @@ __global__ __launch_bounds__(LThreads, 1) void gemm_mfma_large(GemmArgs a) {
                   ic<LLPS * (LSTAGES - 2 - s < 0 ? 0 : LSTAGES - 2 - s)>{}, kt0 + s);
         });
 
-        // Lane holds C[m = mfrag base + lane%32][n = nfrag base + (v/4)*8 + (lane/32)*4 + v%4].
+        // Lane holds C[m = 16i-slab base + lane%16][n = 16j-slab base + 4 (lane/16) + q].
         uint16_t* C = reinterpret_cast<uint16_t*>(a.C) + b * a.sc;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t gm = m0 + wm * 128 + i * 32 + lr;
+        for (int i = 0; i < 8; ++i) {
+            const int64_t gm = m0 + wm * 128 + i * 16 + lr;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < 8; ++j) {
+                const int64_t gn = n0 + wn * 128 + j * 16 + lq * 4;
+                uint16_t* dst = C + gm * a.ldc + gn;
+                if (a.beta == 0.f) {
+                    u32x2 v;
+                    v[0] = (uint32_t)narrow(T{}, a.alpha * acc[i][j][0]) |
+                           ((uint32_t)narrow(T{}, a.alpha * acc[i][j][1]) << 16);
+                    v[1] = (uint32_t)narrow(T{}, a.alpha * acc[i][j][2]) |
+                           ((uint32_t)narrow(T{}, a.alpha * acc[i][j][3]) << 16);
+                    *reinterpret_cast<u32x2*>(dst) = v;
+                } else {
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int64_t gn = n0 + wn * 128 + j * 32 + g * 8 + lh * 4;
-                    uint16_t* dst = C + gm * a.ldc + gn;
-                    if (a.beta == 0.f) {
-                        u32x2 v;
-                        v[0] = (uint32_t)narrow(T{}, a.alpha * acc[i][j][4 * g]) |
-                               ((uint32_t)narrow(T{}, a.alpha * acc[i][j][4 * g + 1]) << 16);
-                        v[1] = (uint32_t)narrow(T{}, a.alpha * acc[i][j][4 * g + 2]) |
-                               ((uint32_t)narrow(T{}, a.alpha * acc[i][j][4 * g + 3]) << 16);
-                        *reinterpret_cast<u32x2*>(dst) = v;
-                    } else {
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            dst[q] = axpby<T>(acc[i][j][4 * g + q], a.alpha, a.beta, dst + q);
-                    }
+                    for (int q = 0; q < 4; ++q) dst[q] = axpby<T>(acc[i][j][q], a.alpha, a.beta, dst + q);
                 }
             }
         }
