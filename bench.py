@@ -20,6 +20,10 @@ timed runs.
 
 cpu_baseline: the CPU oracle (test infrastructure, fp64 triple loops) timed
 on this host on the same decode GEMV, repeated to about ten seconds of work.
+
+vendor (GEMM workloads, context only): torch's own matmul (rocBLAS /
+hipBLASLt) on the same operand copies, timed the same way right after this
+library's kernel, so both see a similar power state; --no-vendor skips it.
 """
 from __future__ import annotations
 
@@ -55,6 +59,8 @@ def parse():
                     "gemm_f16_batched,gemm_f16_large,moe_prefill,moe_decode")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-graph", action="store_true", help="time direct launches, no HIP graph")
+    ap.add_argument("--no-vendor", action="store_true",
+                    help="skip timing torch's own matmul (rocBLAS / hipBLASLt) on the GEMM workloads")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
     ap.add_argument("--calibrate-id", action="store_true",
@@ -268,6 +274,53 @@ def main():
     def want(name):
         return not only or name in only
 
+    # ------------------------------------------------- vendor context (torch matmul)
+    def vendor_time(case, As, Bs, n_rot, steps):
+        """torch's own matmul (rocBLAS / hipBLASLt) on the same operand copies,
+        timed the same way right after this library's kernel: context only.
+        Tight layouts only. A batched product with a transposed right operand
+        gets a contiguous [k, n] copy of B first (torch's batched half-precision
+        products have faulted on transposed views), so it runs NN."""
+        tight = (case.lda in (0, case.k if not case.trans_a else case.m) and
+                 case.ldb in (0, case.k if case.trans_b else case.n) and
+                 case.ldc in (0, case.n) and not case.off_a and not case.off_b)
+        if not tight or case.trans_a:
+            return None
+        tdt = {wl.F32: torch.float32, wl.F16: torch.float16, wl.BF16: torch.bfloat16}[case.dtype]
+        bt, m, n, k = case.batch, case.m, case.n, case.k
+
+        def view_a(t):
+            return t.view(tdt)[: bt * m * k].view(bt, m, k)
+
+        def view_b(t):
+            v = t.view(tdt)[: bt * n * k]
+            return v.view(bt, n, k) if case.trans_b else v.view(bt, k, n)
+
+        A = [view_a(t) for t in As]
+        if bt > 1 and case.trans_b:
+            B = [view_b(t).transpose(1, 2).contiguous() for t in Bs]
+            note = "bmm NN (B pre-transposed)"
+        else:
+            B = [view_b(t) for t in Bs]
+            note = "mm " + ("NT" if case.trans_b else "NN")
+        C = torch.empty(bt, m, n, dtype=tdt, device=dev)
+
+        def vstep(i):
+            with torch.cuda.stream(stream):
+                if bt > 1:
+                    torch.bmm(A[i], B[i], out=C)
+                else:
+                    bb = B[i][0].t() if case.trans_b else B[i][0]
+                    torch.mm(A[i][0], bb, out=C[0])
+        try:
+            vms, _ = timer.time(vstep, n_rot, steps, args.warmup)
+        except Exception as e:  # context only: never fails the bench
+            log(f"vendor timing unavailable: {e}")
+            return None
+        finally:
+            del A, B, C
+        return vms, note
+
     # ---------------------------------------------------------------- GEMM family
     def gemm_workload(name, case, bound, alg_bytes):
         a = to_dev(case.A)
@@ -316,6 +369,13 @@ def main():
         log(f"{name}: {ms * 1e3:.2f} us/call  {tflops:.2f} TFLOP/s  {gbs:.1f} GB/s  "
             f"({achieved / peak * 100:.1f}% of {bound} peak)"
             + (f"  sclk {clock:.0f} MHz under load" if clock else ""))
+        if not args.no_vendor:
+            vend = vendor_time(case, As, Bs, n_rot, steps)
+            if vend is not None:
+                vms, vnote = vend
+                results[name]["vendor"] = {"what": vnote, "us_per_call": vms * 1e3,
+                                           "ours_over_vendor_time": ms / vms}
+                log(f"{name}: torch {vnote}: {vms * 1e3:.2f} us/call (ours / torch time {ms / vms:.3f})")
         del As, Bs, c
         torch.cuda.empty_cache()
 
