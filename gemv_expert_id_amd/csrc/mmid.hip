@@ -753,8 +753,10 @@ __global__ __launch_bounds__(GW * kWave, 1) void id_grouped_bf16(IdArgs a, uint3
 //   X  the gathered f32 activation rows go from global memory straight into
 //      LDS (buffer_load ... lds; each lane fetches the 16-byte chunk that
 //      belongs at its LDS slot: rows of 8 chunks, chunk c of row r at slot
-//      c ^ ((r >> 1) & 7), so the fragment reads of 16 rows hit distinct
-//      banks), three steps ahead;
+//      c ^ ((r ^ (r >> 3)) & 7), so the fragment reads of 16 rows, one chunk
+//      index, hit distinct 16-byte bank groups both per 8 consecutive lanes
+//      in a 128-byte window and over all 16 lanes in a 256-byte window),
+//      three steps ahead;
 //   W  each wave's fragments (16 rows x 64 bytes per 16-byte lane load) go
 //      to registers three steps ahead, four buffers rotating by name;
 //   MFMA per row group, two 16-byte LDS reads give 8 floats that are split
@@ -780,6 +782,9 @@ constexpr int DSTAGE = DQM * DBK;   // floats per stage
 constexpr int dwait_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
 #define MM_LDSP(p) ((__attribute__((address_space(3))) void*)(p))
+
+// LDS slot swizzle of an activation row (8 chunks of 16 bytes per row).
+__device__ __forceinline__ int xswz(int row) { return (row ^ (row >> 3)) & 7; }
 
 struct DTile {
     const uint32_t* rows;  // routed row of each tile row (0xffffffff: none)
@@ -844,7 +849,7 @@ __device__ __attribute__((always_inline)) void grouped_dma_body(const IdArgs& a,
         const int row = 8 * ins + lane / 8;
         const bool live = (uint32_t)row < t.cnt && t.rows[row] != 0xffffffffu;
         const uint64_t off = live ? t.xoff[row] : t.xoff[t.cnt - 1];
-        xvo[d] = (int)off + (((lane & 7) ^ ((row >> 1) & 7)) * 16);
+        xvo[d] = (int)off + (((lane & 7) ^ xswz(row)) * 16);
     }
     // Stages are separate LDS arrays picked by a compile-time index: when the
     // compiler cannot tell a DMA target from the stage being read, it waits
@@ -895,7 +900,7 @@ __device__ __attribute__((always_inline)) void grouped_dma_body(const IdArgs& a,
 #pragma unroll
                 for (int i = 0; i < mn; ++i) {
                     const int row = (m0 + i) * 16 + frow;
-                    const int sw = (row >> 1) & 7;
+                    const int sw = xswz(row);
                     x0[i] = *reinterpret_cast<const f32x4*>(st + row * DBK + (((2 * fq) ^ sw) << 2));
                     x1[i] = *reinterpret_cast<const f32x4*>(st + row * DBK + (((2 * fq + 1) ^ sw) << 2));
                 }
@@ -934,7 +939,7 @@ __device__ __attribute__((always_inline)) void grouped_dma_body(const IdArgs& a,
 #pragma unroll
             for (int i = 0; i < mn; ++i) {
                 const int row = (m0 + i) * 16 + frow;
-                const int sw = (row >> 1) & 7;
+                const int sw = xswz(row);
                 const f32x4 x0 = *reinterpret_cast<const f32x4*>(st + row * DBK + (((2 * fq) ^ sw) << 2));
                 const f32x4 x1 = *reinterpret_cast<const f32x4*>(st + row * DBK + (((2 * fq + 1) ^ sw) << 2));
                 xh[i][0] = cvt_pk_bf16(x0[0], x0[1]);
