@@ -225,7 +225,7 @@ def to_dev_bits(torch, dev, bits):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
 
