@@ -56,7 +56,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", default="", help="comma list: gemm_f32_128,gemv_f16_decode,"
-                    "gemm_f16_batched,gemm_f16_large,moe_prefill,moe_decode")
+                    "gemm_f16_batched,gemm_f16_large,moe_prefill,moe_decode,moe_decode_slotted")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-graph", action="store_true", help="time direct launches, no HIP graph")
     ap.add_argument("--no-vendor", action="store_true",
@@ -396,7 +396,7 @@ def main():
         gemm_workload("gemm_f16_large", case, "mfma", case.A.nbytes + case.B.nbytes + 8192 * 8192 * 2)
 
     # ---------------------------------------------------------------- expert-ID
-    if want("moe_prefill") or want("moe_decode"):
+    if want("moe_prefill") or want("moe_decode") or want("moe_decode_slotted"):
         moe = wl.moe_bf16()
         pre, dec = moe.prefill, moe.decode
         w = to_dev(pre.W)
@@ -429,12 +429,16 @@ def main():
             }
             log(f"moe_prefill: {ms * 1e3:.2f} us/call  {alg / sec / 1e9:.1f} GB/s  "
                 f"{pre.flops / sec / 1e12:.1f} TFLOP/s")
-        if want("moe_decode"):
+        for name, dcase in (("moe_decode", dec),
+                            ("moe_decode_slotted", wl.moe_bf16_slotted_decode(moe))):
+            if not want(name):
+                continue
+            dec = dcase
             x = to_dev(dec.X.reshape(-1))
             ids = to_dev(dec.ids.reshape(-1))
             out = torch.empty(dec.top_k * dec.n, dtype=torch.float32, device=dev)
             p = mm.id_params(dec.m, dec.n, dec.k, dec.top_k, dec.n_experts,
-                             dec.expert_stride_bytes, 0, 1, 0)
+                             dec.expert_stride_bytes, dec.layout, 1, 0)
             u = len(set(int(v) for v in dec.ids.reshape(-1)))
             per_call = u * dec.n * dec.k * 2
             n_rot_d = rotations(per_call)
@@ -449,14 +453,15 @@ def main():
             ms, n = timer.time(step, n_rot_d, max(n_rot_d, args.steps), args.warmup)
             alg = per_call + dec.X.nbytes + dec.ids.nbytes + out.numel() * 4
             sec = ms * 1e-3
-            results["moe_decode"] = {
-                "route": "direct", "distinct_experts": u, "us_per_call": ms * 1e3,
+            results[name] = {
+                "route": "direct", "layout": "slotted" if dec.layout else "shared",
+                "distinct_experts": u, "us_per_call": ms * 1e3,
                 "calls_timed": n, "rotations": n_rot_d, "tflops": dec.flops / sec / 1e12,
                 "alg_gbs": alg / sec / 1e9, "alg_bytes": alg, "flops": dec.flops, "bound": "hbm",
                 "achieved": alg / sec / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": alg / sec / 1e9 / HBM_PEAK_GBS,
             }
-            log(f"moe_decode: {ms * 1e3:.2f} us/call  {alg / sec / 1e9:.1f} GB/s (u={u})")
+            log(f"{name}: {ms * 1e3:.2f} us/call  {alg / sec / 1e9:.1f} GB/s (u={u})")
         del Ws
         torch.cuda.empty_cache()
 

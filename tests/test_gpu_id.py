@@ -61,7 +61,8 @@ def _with_bad_ids(case: wl.IdCase):
 @pytest.mark.parametrize("shape", [(9, 7, 35, 2, 4), (5, 130, 260, 3, 6), (3, 1408, 2048, 8, 64),
                                    (17, 33, 64, 4, 9),
                                    # many repeats per token on the one-group fast form
-                                   (3, 40, 2048, 16, 4),
+                                   # (k = 2048 for 2-byte weights, 1024 for f32)
+                                   (3, 40, 2048, 16, 4), (4, 24, 1024, 8, 3),
                                    # several K groups, and K past 8192
                                    (2, 24, 4096, 3, 5), (1, 8, 12288, 2, 3),
                                    # top_k above the wave width: element-loop form

@@ -131,3 +131,19 @@ def test_moe_decode(moe):
     err = assert_close(got, ref, case.wdtype, case.k, wmax, xmax, "decode")
     np.testing.assert_array_equal(got[0], got[7])
     _say(f"  max err {err:.3e}")
+
+
+def test_moe_decode_slotted(moe):
+    """The decode pass with one activation row per slot (slotted layout): the
+    repeated expert is computed for each of its slots with that slot's row."""
+    _say("workload: expert-ID decode, slotted activations [8,2048], direct route")
+    case = wl.moe_bf16_slotted_decode(moe)
+    run = IdRun(case, route=0, multiplicity=1)
+    rec = run.run()
+    assert rec.route == mm.MM_ROUTE_ID_DIRECT
+    got = run.out_f64()
+    ref = run.oracle()
+    wmax, xmax = finite_absmax(case.W, case.wdtype), float(np.abs(case.X).max())
+    err = assert_close(got, ref, case.wdtype, case.k, wmax, xmax, "decode slotted")
+    assert not np.array_equal(got[0], got[7])  # same expert, different activation rows
+    _say(f"  max err {err:.3e}")

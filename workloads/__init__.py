@@ -341,3 +341,14 @@ def moe_bf16() -> MoeWorkload:
     prefill = IdCase(BF16, m, n, k, top_k, E, stride, 0, W, X, ids)
     decode = IdCase(BF16, 1, n, k, top_k, E, stride, 0, W, xd, idd.reshape(1, top_k))
     return MoeWorkload(prefill, decode)
+
+
+def moe_bf16_slotted_decode(moe: MoeWorkload) -> IdCase:
+    """The decode pass of `moe_bf16` with the slotted activation layout: one
+    f32 row per (token, slot), x [8, 2048] ~ N(0,1) from seed 5, same weights
+    and ids (slot 7 repeats slot 0's expert with its own activations)."""
+    d = moe.decode
+    rng = np.random.default_rng(5)
+    xs = to_storage(rng.standard_normal((d.m * d.top_k, d.k)), F32)
+    return IdCase(d.wdtype, d.m, d.n, d.k, d.top_k, d.n_experts, d.expert_stride_bytes, 1,
+                  d.W, xs, d.ids)
