@@ -285,6 +285,20 @@ def test_large_tile_route_batched_padded():
     _sampled_check(case, 4096, 5, kernel=mm.MM_KERNEL_GEMM_LARGE)
 
 
+def test_large_tile_route_broadcast_b():
+    """Batch of two with one B for both (batch stride 0) and element offsets on
+    every operand, on the 256 x 256 kernel."""
+    _say("large-tile NT batched, B broadcast, offsets, f16 m=4096 n=4096 k=256 batch 2")
+    rng = np.random.default_rng(11)
+    b_, m, n, k = 2, 4096, 4096, 256
+    a = rng.uniform(-1, 1, (b_, m, k))
+    b1 = rng.uniform(-1, 1, (1, n, k)) / np.sqrt(k)
+    case = wl.make_gemm_case(wl.F16, a, np.broadcast_to(b1, (b_, n, k)), False, True,
+                             broadcast_b=True, off_a=8, off_b=16, off_c=4)
+    assert case.stride_b == 0
+    _sampled_check(case, 4096, 7, kernel=mm.MM_KERNEL_GEMM_LARGE)
+
+
 @pytest.mark.parametrize("k", [128, 192, 320])
 def test_large_shape_other_k_takes_tiled_kernel(k):
     """k below 256 or not a multiple of 128: the 128 x 128 kernel, same results."""
