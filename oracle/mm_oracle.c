@@ -64,6 +64,19 @@ double orc_bf16_to_double(uint16_t h)
     return (double)f;
 }
 
+/* Threads for one parallel loop: `requested` when positive, else the
+ * OpenMP default. Passed per loop, so a call never changes the thread count
+ * of later calls. */
+static int threads_for(int requested)
+{
+#ifdef _OPENMP
+    return requested > 0 ? requested : omp_get_max_threads();
+#else
+    (void)requested;
+    return 1;
+#endif
+}
+
 static size_t elt_size(int dtype)
 {
     return dtype == ORC_F32 ? 4 : 2;
@@ -215,13 +228,11 @@ int orc_gemm(int dtype, int64_t batch, int64_t m, int64_t n, int64_t k, int ta, 
     if (off_a % es || off_b % es)
         return -2;
     int64_t a_base = (int64_t)(off_a / es), b_base = (int64_t)(off_b / es);
-#ifdef _OPENMP
-    if (nthreads > 0)
-        omp_set_num_threads(nthreads);
-#else
-    (void)nthreads;
-#endif
-#pragma omp parallel for collapse(2) schedule(static)
+    int nt = threads_for(nthreads);
+    /* One work item per output element, so a single-row product (the GEMV
+     * route) spreads over every thread too; each element is still one
+     * ascending-p sum, so the bits do not depend on the thread count. */
+#pragma omp parallel for collapse(3) schedule(static) num_threads(nt)
     for (int64_t b = 0; b < batch; ++b)
         for (int64_t i = 0; i < m; ++i)
             for (int64_t j = 0; j < n; ++j)
@@ -243,13 +254,8 @@ int orc_gemm_at(int dtype, int64_t k, int ta, int tb, int64_t lda, int64_t ldb,
     if (off_a % es || off_b % es)
         return -2;
     int64_t a_base = (int64_t)(off_a / es), b_base = (int64_t)(off_b / es);
-#ifdef _OPENMP
-    if (nthreads > 0)
-        omp_set_num_threads(nthreads);
-#else
-    (void)nthreads;
-#endif
-#pragma omp parallel for schedule(static)
+    int nt = threads_for(nthreads);
+#pragma omp parallel for schedule(static) num_threads(nt)
     for (int64_t s = 0; s < ns; ++s)
         out[s] = gemm_entry(dtype, k, ta, tb, lda, ldb, A, a_base + bs[s] * stride_a, B,
                             b_base + bs[s] * stride_b, is[s], js[s]);
@@ -269,30 +275,23 @@ int orc_gemm_at(int dtype, int64_t k, int ta, int tb, int64_t lda, int64_t ldb,
  * (4k, 0) for the shared-per-token layout (layout 0) and (4k*top_k, 4k) for
  * the slotted layout (layout 1), as `dense_matmul_id` derives them.
  */
-static void id_row(int wdtype, uint32_t n, uint32_t k, uint32_t top_k, uint32_t n_experts,
-                   uint64_t expert_stride_bytes, int layout, const void *W, const float *X,
-                   const uint32_t *ids, int64_t r, double *out_row)
+static double id_entry(int wdtype, uint32_t k, uint32_t top_k, uint32_t n_experts,
+                       uint64_t expert_stride_bytes, int layout, const void *W, const float *X,
+                       const uint32_t *ids, int64_t r, int64_t j)
 {
     uint32_t e = ids[r];
-    if (e >= n_experts) {
-        for (uint32_t j = 0; j < n; ++j)
-            out_row[j] = 0.0;
-        return;
-    }
+    if (e >= n_experts)
+        return 0.0;
     int64_t t = r / top_k, s = r % top_k;
     int64_t x_row = layout == 0 ? t : t * (int64_t)top_k + s; /* in units of k floats */
     const float *x = X + x_row * (int64_t)k;
-    size_t es = elt_size(wdtype);
     const char *We = (const char *)W + (uint64_t)e * expert_stride_bytes;
-    for (uint32_t j = 0; j < n; ++j) {
-        double acc = 0.0;
-        for (uint32_t p = 0; p < k; ++p) {
-            double w = load_elem(We, wdtype, (int64_t)j * k + p);
-            acc += w * (double)x[p];
-        }
-        out_row[j] = acc;
+    double acc = 0.0;
+    for (uint32_t p = 0; p < k; ++p) {
+        double w = load_elem(We, wdtype, j * (int64_t)k + p);
+        acc += w * (double)x[p];
     }
-    (void)es;
+    return acc;
 }
 
 int orc_id(int wdtype, uint32_t m, uint32_t n, uint32_t k, uint32_t top_k, uint32_t n_experts,
@@ -305,17 +304,14 @@ int orc_id(int wdtype, uint32_t m, uint32_t n, uint32_t k, uint32_t top_k, uint3
         return -1;
     if (expert_stride_bytes % elt_size(wdtype))
         return -2;
-#ifdef _OPENMP
-    if (nthreads > 0)
-        omp_set_num_threads(nthreads);
-#else
-    (void)nthreads;
-#endif
+    int nt = threads_for(nthreads);
     int64_t rows = (int64_t)m * top_k;
-#pragma omp parallel for schedule(dynamic, 1)
+    /* One work item per output element (a decode has only top_k rows). */
+#pragma omp parallel for collapse(2) schedule(static) num_threads(nt)
     for (int64_t r = 0; r < rows; ++r)
-        id_row(wdtype, n, k, top_k, n_experts, expert_stride_bytes, layout, W, X, ids, r,
-               out + r * (int64_t)n);
+        for (int64_t j = 0; j < (int64_t)n; ++j)
+            out[r * (int64_t)n + j] = id_entry(wdtype, k, top_k, n_experts, expert_stride_bytes,
+                                               layout, W, X, ids, r, j);
     return 0;
 }
 
@@ -334,16 +330,12 @@ int orc_id_rows(int wdtype, uint32_t m, uint32_t n, uint32_t k, uint32_t top_k,
     for (int64_t q = 0; q < nr; ++q)
         if (rows[q] < 0 || rows[q] >= (int64_t)m * top_k)
             return -3;
-#ifdef _OPENMP
-    if (nthreads > 0)
-        omp_set_num_threads(nthreads);
-#else
-    (void)nthreads;
-#endif
-#pragma omp parallel for schedule(dynamic, 1)
+    int nt = threads_for(nthreads);
+#pragma omp parallel for collapse(2) schedule(static) num_threads(nt)
     for (int64_t q = 0; q < nr; ++q)
-        id_row(wdtype, n, k, top_k, n_experts, expert_stride_bytes, layout, W, X, ids, rows[q],
-               out + q * (int64_t)n);
+        for (int64_t j = 0; j < (int64_t)n; ++j)
+            out[q * (int64_t)n + j] = id_entry(wdtype, k, top_k, n_experts, expert_stride_bytes,
+                                               layout, W, X, ids, rows[q], j);
     return 0;
 }
 
