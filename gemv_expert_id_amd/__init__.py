@@ -28,7 +28,7 @@ MM_ROUTE_GEMV_WIDE = 6
  MM_KERNEL_GEMM_LARGE, MM_KERNEL_GEMM_F32, MM_KERNEL_ID_DIRECT_FAST, MM_KERNEL_ID_DIRECT,
  MM_KERNEL_ID_MAP, MM_KERNEL_ID_GROUPED_MFMA, MM_KERNEL_ID_GROUPED_FMA,
  MM_KERNEL_GEMV_WIDE, MM_KERNEL_GEMM_F32_SMALL) = range(13)
-MM_ID_SCHEMA_VERSION = 4
+MM_ID_SCHEMA_VERSION = 5
 MM_ID_GROUPED_MAX_EXPERTS = 1024
 
 STATUS_NAMES = {
@@ -60,7 +60,7 @@ class Buf(ctypes.Structure):
 class Receipt(ctypes.Structure):
     _fields_ = [("schema_version", ctypes.c_uint32), ("route", ctypes.c_uint32),
                 ("dtype", ctypes.c_uint32), ("dispatch_count", ctypes.c_uint32),
-                ("kernel", ctypes.c_uint32)]
+                ("kernel", ctypes.c_uint32), ("variant", ctypes.c_uint32)]
 
 
 class GemmDesc(ctypes.Structure):

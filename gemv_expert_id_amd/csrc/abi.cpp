@@ -110,13 +110,14 @@ mm_status finish(hipError_t err, hipStream_t s, const char* what) {
     return MM_OK;
 }
 
-void set_receipt(mm_receipt* r, uint32_t route, uint32_t dtype, uint32_t n, int kernel) {
+void set_receipt(mm_receipt* r, uint32_t route, uint32_t dtype, uint32_t n, const mmk::Launched& L) {
     if (!r) return;
     r->schema_version = MM_ID_SCHEMA_VERSION;
     r->route = route;
     r->dtype = dtype;
     r->dispatch_count = n;
-    r->kernel = (uint32_t)kernel;
+    r->kernel = (uint32_t)L.kernel;
+    r->variant = (uint32_t)L.variant;
 }
 
 // ---------------------------------------------------------------------------
@@ -248,10 +249,10 @@ mm_status run_gemv(const GemmPlan& p, hipStream_t s, mm_receipt* r) {
     mm_status st = resolve("gemv");
     if (st != MM_OK) return st;
     ++g_launches;
-    int kernel = -1;
-    st = finish(mmk::launch_gemv(gemv_args(p), s, &kernel), s, "gemv");
+    mmk::Launched L;
+    st = finish(mmk::launch_gemv(gemv_args(p), s, &L), s, "gemv");
     if (st != MM_OK) return st;
-    set_receipt(r, MM_ROUTE_GEMV, (uint32_t)p.dt, 1, kernel);
+    set_receipt(r, MM_ROUTE_GEMV, (uint32_t)p.dt, 1, L);
     return ok();
 }
 
@@ -299,10 +300,10 @@ mm_status run_skinny(const mmk::SkinnyArgs& g, int dt, hipStream_t s, mm_receipt
     mm_status st = resolve("gemv_wide");
     if (st != MM_OK) return st;
     ++g_launches;
-    int kernel = -1;
-    st = finish(mmk::launch_gemv_wide(g, s, &kernel), s, "gemv_wide");
+    mmk::Launched L;
+    st = finish(mmk::launch_gemv_wide(g, s, &L), s, "gemv_wide");
     if (st != MM_OK) return st;
-    set_receipt(r, MM_ROUTE_GEMV_WIDE, (uint32_t)dt, 1, kernel);
+    set_receipt(r, MM_ROUTE_GEMV_WIDE, (uint32_t)dt, 1, L);
     return ok();
 }
 
@@ -312,10 +313,10 @@ mm_status run_gemm(const GemmPlan& p, hipStream_t s, mm_receipt* r) {
     mmk::GemmArgs g{p.a, p.b, p.c, p.m, p.n, p.k, p.lda, p.ldb, p.ldc, p.sa, p.sb, p.sc,
                     p.batch, p.dt, p.ta, p.tb, p.alpha, p.beta};
     ++g_launches;
-    int kernel = -1;
-    st = finish(mmk::launch_gemm(g, s, &kernel), s, "gemm");
+    mmk::Launched L;
+    st = finish(mmk::launch_gemm(g, s, &L), s, "gemm");
     if (st != MM_OK) return st;
-    set_receipt(r, MM_ROUTE_GEMM, (uint32_t)p.dt, 1, kernel);
+    set_receipt(r, MM_ROUTE_GEMM, (uint32_t)p.dt, 1, L);
     return ok();
 }
 
@@ -553,9 +554,9 @@ mm_status mm_id_direct(const mm_id_params* params, mm_dtype weight_dtype, mm_buf
     mmk::IdArgs a = fill_ptrs(id_args(params, weight_dtype), weights, input, ids, out,
                               mm_buf{nullptr, 0}, mm_buf{nullptr, 0});
     ++g_launches;
-    int kernel = -1;
-    if ((st = finish(mmk::launch_id_direct(a, s, &kernel), s, "id_direct")) != MM_OK) return st;
-    set_receipt(receipt, MM_ROUTE_ID_DIRECT, (uint32_t)weight_dtype, 1, kernel);
+    mmk::Launched L;
+    if ((st = finish(mmk::launch_id_direct(a, s, &L), s, "id_direct")) != MM_OK) return st;
+    set_receipt(receipt, MM_ROUTE_ID_DIRECT, (uint32_t)weight_dtype, 1, L);
     return ok();
 }
 
@@ -571,9 +572,9 @@ mm_status mm_id_map(const mm_id_params* params, mm_buf ids, mm_buf counts, mm_bu
     mmk::IdArgs a = fill_ptrs(id_args(params, MM_F32), mm_buf{nullptr, 0}, mm_buf{nullptr, 0}, ids,
                               out, counts, routed_rows);
     ++g_launches;
-    int kernel = -1;
-    if ((st = finish(mmk::launch_id_map(a, s, &kernel), s, "id_map")) != MM_OK) return st;
-    set_receipt(receipt, MM_ROUTE_ID_MAP, (uint32_t)MM_F32, 1, kernel);
+    mmk::Launched L;
+    if ((st = finish(mmk::launch_id_map(a, s, &L), s, "id_map")) != MM_OK) return st;
+    set_receipt(receipt, MM_ROUTE_ID_MAP, (uint32_t)MM_F32, 1, L);
     return ok();
 }
 
@@ -589,9 +590,9 @@ mm_status mm_id_grouped(const mm_id_params* params, mm_dtype weight_dtype, mm_bu
     mmk::IdArgs a = fill_ptrs(id_args(params, weight_dtype), weights, input, mm_buf{nullptr, 0},
                               out, counts, routed_rows);
     ++g_launches;
-    int kernel = -1;
-    if ((st = finish(mmk::launch_id_grouped(a, s, &kernel), s, "id_grouped")) != MM_OK) return st;
-    set_receipt(receipt, MM_ROUTE_ID_GROUPED, (uint32_t)weight_dtype, 1, kernel);
+    mmk::Launched L;
+    if ((st = finish(mmk::launch_id_grouped(a, s, &L), s, "id_grouped")) != MM_OK) return st;
+    set_receipt(receipt, MM_ROUTE_ID_GROUPED, (uint32_t)weight_dtype, 1, L);
     return ok();
 }
 
@@ -610,12 +611,12 @@ mm_status mm_id(const mm_id_params* params, mm_dtype weight_dtype, mm_buf weight
     hipStream_t s = static_cast<hipStream_t>(stream);
     mmk::IdArgs a = fill_ptrs(id_args(params, weight_dtype), weights, input, ids, out, counts,
                               routed_rows);
-    int kernel = -1;
+    mmk::Launched L;
     ++g_launches;
-    if ((st = finish(mmk::launch_id_map(a, s, &kernel), s, "id_map")) != MM_OK) return st;
+    if ((st = finish(mmk::launch_id_map(a, s, &L), s, "id_map")) != MM_OK) return st;
     ++g_launches;
-    if ((st = finish(mmk::launch_id_grouped(a, s, &kernel), s, "id_grouped")) != MM_OK) return st;
-    set_receipt(receipt, MM_ROUTE_ID_PREFILL, (uint32_t)weight_dtype, 2, kernel);
+    if ((st = finish(mmk::launch_id_grouped(a, s, &L), s, "id_grouped")) != MM_OK) return st;
+    set_receipt(receipt, MM_ROUTE_ID_PREFILL, (uint32_t)weight_dtype, 2, L);
     return ok();
 }
 

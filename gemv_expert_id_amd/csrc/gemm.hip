@@ -770,7 +770,7 @@ const void* pick_f32(bool ta, bool tb) {
 
 }  // namespace
 
-hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, int* kernel) {
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, Launched* L) {
     void* args[] = {const_cast<GemmArgs*>(&a)};
     const unsigned gy = (unsigned)(a.batch < 65535 ? a.batch : 65535);
     if (a.dtype == 0) {
@@ -782,14 +782,14 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, int* kernel) {
                              : !a.ta        ? (const void*)&gemm_f32_mfma_small<false, true>
                              : !a.tb        ? (const void*)&gemm_f32_mfma_small<true, false>
                                             : (const void*)&gemm_f32_mfma_small<true, true>;
-            *kernel = MM_KERNEL_GEMM_F32_SMALL;
+            L->kernel = MM_KERNEL_GEMM_F32_SMALL;
             return hipLaunchKernel(fn, dim3((unsigned)t16, gy), dim3(kWave), args, 0, s);
         }
         // 64 x 64 tiles, or 32 x 32 when that leaves fewer blocks than CUs.
         const int64_t t64 = ((a.m + 63) / 64) * ((a.n + 63) / 64);
         const bool small = t64 * a.batch < 256;
         const int64_t tiles = small ? ((a.m + 31) / 32) * ((a.n + 31) / 32) : t64;
-        *kernel = MM_KERNEL_GEMM_F32;
+        L->kernel = MM_KERNEL_GEMM_F32;
         return hipLaunchKernel(small ? pick_f32<32>(a.ta, a.tb) : pick_f32<64>(a.ta, a.tb),
                                dim3((unsigned)tiles, gy), dim3(256), args, 0, s);
     }
@@ -807,7 +807,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, int* kernel) {
         const void* fn = a.dtype == 1 ? (const void*)&gemm_mfma_large<TF16>
                                       : (const void*)&gemm_mfma_large<TBF16>;
         const unsigned grid = (unsigned)(((big_tiles + 7) / 8) * 8);
-        *kernel = MM_KERNEL_GEMM_LARGE;
+        L->kernel = MM_KERNEL_GEMM_LARGE;
         return hipLaunchKernel(fn, dim3(grid, gy), dim3(LThreads), args, kLargeLds, s);
     }
     const int64_t total = ((a.m + GBM - 1) / GBM) * ((a.n + GBN - 1) / GBN) * a.batch;
@@ -816,7 +816,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, int* kernel) {
     const bool shortk = a.k <= GSK * GBK;
     const void* fn = a.dtype == 1 ? pick_mfma<TF16>(a.ta, a.tb, vec, shortk)
                                   : pick_mfma<TBF16>(a.ta, a.tb, vec, shortk);
-    *kernel = MM_KERNEL_GEMM_TILED;
+    L->kernel = MM_KERNEL_GEMM_TILED;
     return hipLaunchKernel(fn, dim3((unsigned)(8 * per_xcd)), dim3(GThreads), args, 0, s);
 }
 

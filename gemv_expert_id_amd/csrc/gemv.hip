@@ -200,7 +200,7 @@ __global__ __launch_bounds__(kThreads) void gemv_cols(GemvArgs a) {
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 template <class T>
-hipError_t launch_typed(const GemvArgs& a, hipStream_t s, int* kernel) {
+hipError_t launch_typed(const GemvArgs& a, hipStream_t s, Launched* L) {
     constexpr int CH = T::Elems16;
     const unsigned gy = (unsigned)(a.batch < 65535 ? a.batch : 65535);
     void* args[] = {const_cast<GemvArgs*>(&a)};
@@ -212,11 +212,11 @@ hipError_t launch_typed(const GemvArgs& a, hipStream_t s, int* kernel) {
         dim3 grid((unsigned)((a.rows + kWaves * R - 1) / (kWaves * R)), gy);
         const void* fn = vec ? reinterpret_cast<const void*>(&gemv_rows_vec<T, R, 8>)
                              : reinterpret_cast<const void*>(&gemv_rows_scalar<T, R>);
-        *kernel = vec ? MM_KERNEL_GEMV_ROWS : MM_KERNEL_GEMV_ROWS_ELEM;
+        L->kernel = vec ? MM_KERNEL_GEMV_ROWS : MM_KERNEL_GEMV_ROWS_ELEM;
         return hipLaunchKernel(fn, grid, dim3(kThreads), args, 0, s);
     }
     const bool vec = a.ld % CH == 0 && a.mat_bstride % CH == 0 && aligned16(a.mat);
-    *kernel = MM_KERNEL_GEMV_COLS;
+    L->kernel = MM_KERNEL_GEMV_COLS;
     if (vec) {
         dim3 grid((unsigned)((a.rows + kWave * CH - 1) / (kWave * CH)), gy);
         return hipLaunchKernel(reinterpret_cast<const void*>(&gemv_cols<T, CH>), grid,
@@ -229,11 +229,11 @@ hipError_t launch_typed(const GemvArgs& a, hipStream_t s, int* kernel) {
 
 }  // namespace
 
-hipError_t launch_gemv(const GemvArgs& a, hipStream_t s, int* kernel) {
+hipError_t launch_gemv(const GemvArgs& a, hipStream_t s, Launched* L) {
     switch (a.dtype) {
-        case 0: return launch_typed<TF32>(a, s, kernel);
-        case 1: return launch_typed<TF16>(a, s, kernel);
-        case 2: return launch_typed<TBF16>(a, s, kernel);
+        case 0: return launch_typed<TF32>(a, s, L);
+        case 1: return launch_typed<TF16>(a, s, L);
+        case 2: return launch_typed<TBF16>(a, s, L);
         default: return hipErrorInvalidValue;
     }
 }

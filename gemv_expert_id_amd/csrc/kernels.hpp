@@ -1,8 +1,8 @@
 // Kernel argument blocks and host-side launchers. The launchers (defined in
 // gemv.hip, gemm.hip, mmid.hip) pick a template instance, size the grid and
 // enqueue exactly one kernel; they never validate (the C ABI layer has done
-// that), report the kernel family they chose (an mm_kernel code) through
-// `kernel`, and return the hipError_t of the enqueue.
+// that), report the kernel family and instance they chose through a
+// `Launched` record, and return the hipError_t of the enqueue.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -14,6 +14,13 @@ namespace mmk {
 
 // Largest expert count of the grouped route (sizes the in-block tile table).
 constexpr int MM_GROUPED_MAX_E = 1024;
+
+// What a launcher enqueued: the mm_kernel family and a family-specific
+// instance number (mm_receipt.variant).
+struct Launched {
+    int kernel = -1;
+    int variant = 0;
+};
 
 // out[o * out_inc] = sum_p M(o, p) * vec[p * vec_inc] for o < rows, with
 // M(o, p) = mat[o * ld + p] (row form) or mat[p * ld + o] (column form).
@@ -29,8 +36,8 @@ struct GemvArgs {
     int32_t col_form;    // 1: M(o, p) = mat[p * ld + o]
     float alpha, beta;   // out = alpha * sum + beta * out_old (beta == 0: out_old unread)
 };
-// Launchers enqueue one kernel on `s`; `kernel` receives its mm_kernel code.
-hipError_t launch_gemv(const GemvArgs& a, hipStream_t s, int* kernel);
+// Launchers enqueue one kernel on `s` and describe it in *L.
+hipError_t launch_gemv(const GemvArgs& a, hipStream_t s, Launched* L);
 
 // Skinny product: out[b][x * out_sx + w * out_sw] = sum_p W[b](w, p) * X[b](x, p)
 // for w < nw, x < nx (nx <= 16); W(w, p) = W[w * ldw + p], X(x, p) = X[x * ldx + p].
@@ -47,7 +54,7 @@ struct SkinnyArgs {
     int32_t dtype;
     float alpha, beta;   // out = alpha * sum + beta * out_old (beta == 0: out_old unread)
 };
-hipError_t launch_gemv_wide(const SkinnyArgs& a, hipStream_t s, int* kernel);
+hipError_t launch_gemv_wide(const SkinnyArgs& a, hipStream_t s, Launched* L);
 
 // C[b] = op(A[b]) . op(B[b]); pointers already include the byte offsets.
 struct GemmArgs {
@@ -62,7 +69,7 @@ struct GemmArgs {
     int32_t ta, tb;
     float alpha, beta;   // C = alpha * op(A) op(B) + beta * C_old (beta == 0: C_old unread)
 };
-hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, int* kernel);
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, Launched* L);
 
 // Expert-ID matmul. Byte strides locate the activation row of (token, slot).
 struct IdArgs {
@@ -81,8 +88,8 @@ struct IdArgs {
     int32_t wdtype;
     int32_t dedup;                // direct: repeated ids of one token share one pass
 };
-hipError_t launch_id_direct(const IdArgs& a, hipStream_t s, int* kernel);
-hipError_t launch_id_map(const IdArgs& a, hipStream_t s, int* kernel);
-hipError_t launch_id_grouped(const IdArgs& a, hipStream_t s, int* kernel);
+hipError_t launch_id_direct(const IdArgs& a, hipStream_t s, Launched* L);
+hipError_t launch_id_map(const IdArgs& a, hipStream_t s, Launched* L);
+hipError_t launch_id_grouped(const IdArgs& a, hipStream_t s, Launched* L);
 
 }  // namespace mmk

@@ -455,12 +455,9 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
-// FAST: k % 256 == 0, 16-byte aligned operands, input and one expert below
-// 2 GiB. Every
-// global load is then issued unconditionally (dead columns read a clamped,
-// valid address and are never stored), so the compiler counts outstanding
-// loads exactly and the prefetches stay in flight across the barrier.
-template <bool VEC, bool FAST>
+// VEC: k % 8 == 0 and 16-byte aligned operands (16-byte weight and
+// activation loads); otherwise element loads with edge masks.
+template <bool VEC>
 __global__ __launch_bounds__(GW * kWave, 1) void id_grouped_bf16(IdArgs a, uint32_t bn) {
     constexpr int NT = GW * kWave;       // threads
     constexpr int XRP = NT / 16;         // activation rows per staging pass
@@ -521,33 +518,16 @@ __global__ __launch_bounds__(GW * kWave, 1) void id_grouped_bf16(IdArgs a, uint3
 
     // Activation staging: thread covers 4 consecutive k of rows p*XRP + tid/16.
     const int xr0 = tid >> 4, xk = (tid & 15) * 4;
-    const char* xrow[FAST ? 1 : XP];
-    uint32_t xoff[XP];  // FAST: byte offset of the row from X
+    const char* xrow[XP];
     bool xlive[XP];
 #pragma unroll
     for (int p = 0; p < XP; ++p) {
         const int row = p * XRP + xr0;
         xlive[p] = (uint32_t)row < cnt && s_rows[row] != 0xffffffffu;
         const uint64_t off = xlive[p] ? s_xoff[row] : s_xoff[cnt - 1];
-        xoff[p] = (uint32_t)off + (uint32_t)xk * 4u;
-        if constexpr (!FAST) xrow[p] = reinterpret_cast<const char*>(a.X) + off;
+        xrow[p] = reinterpret_cast<const char*>(a.X) + off;
     }
-    // FAST: buffer loads; the lane offsets stay fixed and the K step rides in
-    // the scalar offset, so no address register is rewritten while a load
-    // that targets it may still be in flight.
-    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(a.X), (short)0, 0x7fffffff, 0x00020000);
-    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(reinterpret_cast<const char*>(a.W) + (uint64_t)e * a.expert_stride_bytes),
-        (short)0, (int)(FAST ? a.n * a.k * 2 : 0), 0x00020000);
     auto load_x = [&](int64_t k0, f32x4 (&xv)[XP]) {
-        if constexpr (FAST) {
-#pragma unroll
-            for (int p = 0; p < XP; ++p)
-                xv[p] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                            xrs, (int)xoff[p], (int)(k0 * 4), 0));
-            return;
-        }
 #pragma unroll
         for (int p = 0; p < XP; ++p) {
             xv[p] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -579,29 +559,13 @@ __global__ __launch_bounds__(GW * kWave, 1) void id_grouped_bf16(IdArgs a, uint3
         }
     };
     // Weight fragments: lane -> column wcol[j], k offset kk*32 + (lane/16)*8.
-    int wvo[GF];
-#pragma unroll
-    for (int j = 0; j < GF; ++j) wvo[j] = (int)((wcol[j] * a.k + (lane >> 4) * 8) * 2);
     auto load_w = [&](int64_t k0, u32x4 (&w)[GF][2]) {
-        if constexpr (FAST) {
-#pragma unroll
-            for (int j = 0; j < GF; ++j)
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk)
-                    // Plain (cached) loads: with the non-temporal hint the two
-                    // 64-byte halves of a line, fetched by kk = 0 and 1, were
-                    // each served from HBM (streaming dropped from ~4.8 to
-                    // ~3.4 TB/s in isolation).
-                    w[j][kk] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                   wrs, wvo[j] + kk * 64, (int)(k0 * 2), 0));
-            return;
-        }
 #pragma unroll
         for (int j = 0; j < GF; ++j) {
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 const int64_t kb = k0 + kk * 32 + (lane >> 4) * 8;
-                if (FAST || (VEC && kb + 8 <= a.k)) {
+                if (VEC && kb + 8 <= a.k) {
                     w[j][kk] = ld16_stream(We + wcol[j] * a.k + kb);
                 } else {
                     uint32_t h[8];
@@ -661,43 +625,6 @@ __global__ __launch_bounds__(GW * kWave, 1) void id_grouped_bf16(IdArgs a, uint3
         __syncthreads();
     };
 
-    if constexpr (FAST) {
-        // nk % 4 == 0. W is loaded three K steps ahead into four buffers, X two
-        // steps ahead into two; a round of four steps closes both rotations, so
-        // the steady loop is straight-line code and the compiler's load
-        // counting is exact (a conditional load would make it wait for all).
-        // X (from L2) is fetched one step ahead into one register buffer.
-        u32x4 w3[GF][2];
-        auto fstep = [&](auto LW, auto LX, auto SX, int64_t it, const u32x4 (&wc)[GF][2],
-                         u32x4 (&wf)[GF][2]) {
-            if constexpr (decltype(LW)::value) load_w((it + 3) * QBK, wf);
-            compute(it, wc);
-            if constexpr (decltype(SX)::value) store_x(xA, (int)((it + 1) & 1));
-            if constexpr (decltype(LX)::value) load_x((it + 2) * QBK, xA);
-            __syncthreads();
-        };
-        using T_ = std::integral_constant<bool, true>;
-        using F_ = std::integral_constant<bool, false>;
-        load_w(0, w0);
-        load_w(QBK, w1);
-        load_w(2 * QBK, w2);
-        load_x(0, xA);
-        store_x(xA, 0);
-        load_x(QBK, xA);
-        __syncthreads();
-        int64_t it = 0;
-        for (; it + 4 < nk; it += 4) {
-            fstep(T_{}, T_{}, T_{}, it, w0, w3);
-            fstep(T_{}, T_{}, T_{}, it + 1, w1, w0);
-            fstep(T_{}, T_{}, T_{}, it + 2, w2, w1);
-            fstep(T_{}, T_{}, T_{}, it + 3, w3, w2);
-        }
-        // Last round: W of the final step and X of the last two remain.
-        fstep(T_{}, T_{}, T_{}, it, w0, w3);
-        fstep(F_{}, T_{}, T_{}, it + 1, w1, w0);
-        fstep(F_{}, F_{}, T_{}, it + 2, w2, w1);
-        fstep(F_{}, F_{}, F_{}, it + 3, w3, w2);
-    } else {
     load_w(0, w0);
     if (nk > 1) load_w(QBK, w1);
     load_x(0, xA);
@@ -712,7 +639,6 @@ __global__ __launch_bounds__(GW * kWave, 1) void id_grouped_bf16(IdArgs a, uint3
         if (it + 3 < nk) step(it + 3, w0, w2, xB);
         if (it + 4 < nk) step(it + 4, w1, w0, xA);
         if (it + 5 < nk) step(it + 5, w2, w1, xB);
-    }
     }
 
     // Lane holds out[row = mf*16 + lane%16][n = frag column base + 4*(lane/16) + q].
@@ -1208,7 +1134,7 @@ inline uint64_t grid_for(const IdArgs& a, int bm, int bn) {
 
 }  // namespace
 
-hipError_t launch_id_direct(const IdArgs& a, hipStream_t s, int* kernel) {
+hipError_t launch_id_direct(const IdArgs& a, hipStream_t s, Launched* L) {
     void* args[] = {const_cast<IdArgs*>(&a)};
     const int64_t es = a.wdtype == 0 ? 4 : 2;
     const int64_t ch = 16 / es;  // weights per 16-byte load
@@ -1222,10 +1148,10 @@ hipError_t launch_id_direct(const IdArgs& a, hipStream_t s, int* kernel) {
 #define MM_DF(T) (one ? (const void*)&id_direct_fast<T, true> : (const void*)&id_direct_fast<T, false>)
         const void* fn = a.wdtype == 0 ? MM_DF(TF32) : a.wdtype == 1 ? MM_DF(TF16) : MM_DF(TBF16);
 #undef MM_DF
-        *kernel = MM_KERNEL_ID_DIRECT_FAST;
+        L->kernel = MM_KERNEL_ID_DIRECT_FAST;
         return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
     }
-    *kernel = MM_KERNEL_ID_DIRECT;
+    L->kernel = MM_KERNEL_ID_DIRECT;
     constexpr int R = 2;
     const int64_t per_block = kWaves * R;
     const int64_t work = (int64_t)a.m * a.top_k * ((a.n + per_block - 1) / per_block);
@@ -1241,8 +1167,8 @@ hipError_t launch_id_direct(const IdArgs& a, hipStream_t s, int* kernel) {
     return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
 }
 
-hipError_t launch_id_map(const IdArgs& a, hipStream_t s, int* kernel) {
-    *kernel = MM_KERNEL_ID_MAP;
+hipError_t launch_id_map(const IdArgs& a, hipStream_t s, Launched* L) {
+    L->kernel = MM_KERNEL_ID_MAP;
     void* args[] = {const_cast<IdArgs*>(&a)};
     // 12 bytes of LDS per (wave, expert); keep the tables within 64 KiB.
     int waves = (int)(65536 / (12ull * a.n_experts));
@@ -1252,7 +1178,7 @@ hipError_t launch_id_map(const IdArgs& a, hipStream_t s, int* kernel) {
                            args, lds, s);
 }
 
-hipError_t launch_id_grouped(const IdArgs& a, hipStream_t s, int* kernel) {
+hipError_t launch_id_grouped(const IdArgs& a, hipStream_t s, Launched* L) {
     // Output tile width: as few tiles as cover n at the widest tile each,
     // raised until (experts that can be in use) x tiles reaches the CU count,
     // so every CU streams one W slab even when few tokens touch few experts.
@@ -1277,10 +1203,11 @@ hipError_t launch_id_grouped(const IdArgs& a, hipStream_t s, int* kernel) {
     const bool fast = vec && a.k % (DST * DBK) == 0 && in_rows * a.k * 4 < (1ull << 31) &&
                       (uint64_t)a.n * a.k * es < (1ull << 31);
     if (fast) {
-        *kernel = MM_KERNEL_ID_GROUPED_MFMA;
+        L->kernel = MM_KERNEL_ID_GROUPED_MFMA;
         // Fragment slots per wave: the fewest of 2, 4, 6 that cover the tile.
         const uint32_t per_wave = (bn / 16 + DW - 1) / DW;
         const int df = per_wave <= 2 ? 2 : per_wave <= 4 ? 4 : 6;
+        L->variant = df;
 #define MM_GD(T) (df == 2 ? (const void*)&id_grouped_dma<T, 2>   \
                   : df == 4 ? (const void*)&id_grouped_dma<T, 4> \
                             : (const void*)&id_grouped_dma<T, 6>)
@@ -1292,15 +1219,15 @@ hipError_t launch_id_grouped(const IdArgs& a, hipStream_t s, int* kernel) {
         return hipLaunchKernel(fn, dim3((unsigned)grid_for(a, DQM, bn)), dim3(DW * kWave), args, 0, s);
     }
     if (a.wdtype == 2) {
-        *kernel = MM_KERNEL_ID_GROUPED_MFMA;
+        L->kernel = MM_KERNEL_ID_GROUPED_MFMA;
         const uint64_t g = grid_for(a, QBM, bn);
-        const void* fn = vec ? (const void*)&id_grouped_bf16<true, false>
-                             : (const void*)&id_grouped_bf16<false, false>;
+        const void* fn = vec ? (const void*)&id_grouped_bf16<true>
+                             : (const void*)&id_grouped_bf16<false>;
         return hipLaunchKernel(fn, dim3((unsigned)g), dim3(GW * kWave), args, 0, s);
     }
     void* fargs[] = {const_cast<IdArgs*>(&a)};
     const uint64_t g = grid_for(a, FBM, FBN);
-    *kernel = MM_KERNEL_ID_GROUPED_FMA;
+    L->kernel = MM_KERNEL_ID_GROUPED_FMA;
     const void* fn = a.wdtype == 0 ? (const void*)&id_grouped_fma<TF32> : (const void*)&id_grouped_fma<TF16>;
     return hipLaunchKernel(fn, dim3((unsigned)g), dim3(kThreads), fargs, 0, s);
 }

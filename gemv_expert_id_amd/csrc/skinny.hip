@@ -195,13 +195,13 @@ __global__ __launch_bounds__(SThreads) void gemv_wide(SkinnyArgs a) {
 
 }  // namespace
 
-hipError_t launch_gemv_wide(const SkinnyArgs& a, hipStream_t s, int* kernel) {
+hipError_t launch_gemv_wide(const SkinnyArgs& a, hipStream_t s, Launched* L) {
     void* args[] = {const_cast<SkinnyArgs*>(&a)};
     const dim3 grid((unsigned)((a.nw + 15) / 16), (unsigned)(a.batch < 65535 ? a.batch : 65535));
     const void* fn = a.dtype == 0   ? reinterpret_cast<const void*>(&gemv_wide<TF32>)
                      : a.dtype == 1 ? reinterpret_cast<const void*>(&gemv_wide<TF16>)
                                     : reinterpret_cast<const void*>(&gemv_wide<TBF16>);
-    *kernel = MM_KERNEL_GEMV_WIDE;
+    L->kernel = MM_KERNEL_GEMV_WIDE;
     return hipLaunchKernel(fn, grid, dim3(SThreads), args, 0, s);
 }
 

@@ -17,7 +17,10 @@
  *   enqueues anything (mlx-native dense_matmul_id.rs, `dense_matmul_id`:
  *   every pipeline is resolved and every limit checked before encoding; test
  *   `grouped_pipeline_resolution_failure_does_not_mutate_encoder`). A call
- *   that returns an error has enqueued nothing.
+ *   that returns an error other than MM_ERR_DEVICE has enqueued nothing.
+ *   MM_ERR_DEVICE means the HIP runtime refused a launch after validation;
+ *   the one call that makes two launches (mm_id with the grouped route) may
+ *   then leave its first launch, the map pass, enqueued (see mm_id).
  * - Asynchrony: on MM_OK the work is enqueued on `stream` (a hipStream_t; 0 =
  *   the null stream) and results are valid once the stream has reached that
  *   point. Stream order is the only ordering: a map launch followed by a
@@ -45,7 +48,7 @@ extern "C" {
 #define MM_ABI_VERSION 1u
 /* Schema version of capability/receipt records (mlx-native
  * `DENSE_MATMUL_ID_SCHEMA_VERSION`). */
-#define MM_ID_SCHEMA_VERSION 4u
+#define MM_ID_SCHEMA_VERSION 5u
 /* Largest expert count the grouped route accepts (mlx-native
  * `GROUPED_MAX_EXPERTS`). */
 #define MM_ID_GROUPED_MAX_EXPERTS 1024u
@@ -102,6 +105,11 @@ typedef struct {
     uint32_t dtype;           /* mm_dtype of A/B/C or of the expert weights */
     uint32_t dispatch_count;  /* kernel launches enqueued by the call */
     uint32_t kernel;          /* mm_kernel of the last launch */
+    uint32_t variant;         /* instance of that kernel family: for
+                                 MM_KERNEL_ID_GROUPED_MFMA the 16-output
+                                 fragment slots per wave (2, 4 or 6) of the
+                                 pipelined form, 0 for its 8-wave LDS-split
+                                 bf16 form; 0 for every other family */
 } mm_receipt;
 
 /* ------------------------------------------------------------------------ */
@@ -277,8 +285,12 @@ mm_status mm_id_grouped(const mm_id_params *params, mm_dtype weight_dtype, mm_bu
 /*
  * The whole expert-ID matmul in one call, by params->route: the direct launch,
  * or the map launch followed by the grouped launch (mlx-native
- * `dense_matmul_id`). Everything for both launches is validated before the
- * first is enqueued. counts / routed_rows are ignored by the direct route.
+ * `dense_matmul_id`). Everything for both launches is validated and resolved
+ * before the first is enqueued. counts / routed_rows are ignored by the
+ * direct route. If the HIP runtime refuses the grouped launch after the map
+ * launch was accepted, the call returns MM_ERR_DEVICE with the map pass still
+ * enqueued: it then writes only the scratch (counts, routed_rows) and the
+ * +0.0 rows of invalid ids, and the rest of the output is unspecified.
  */
 mm_status mm_id(const mm_id_params *params, mm_dtype weight_dtype, mm_buf weights, mm_buf input,
                 mm_buf ids, mm_buf out, mm_buf counts, mm_buf routed_rows, void *stream,
@@ -302,13 +314,21 @@ typedef struct {
 } mm_device_caps;
 
 /* Fills `out` for HIP device `device`; UNSUPPORTED when it is not a gfx950
- * (the only architecture the kernels are built for), DEVICE on a HIP error. */
+ * (the only architecture the kernels are built for), DEVICE on a HIP error.
+ * The counterpart of tract-metal mlx_gemm/mod.rs `device_arch_gen`, which
+ * reads the GPU architecture generation once and gates kernels on it; here
+ * the gate is the architecture name. */
 mm_status mm_capabilities(int device, mm_device_caps *out);
 
-/* Static description of a status code. */
+/* Static description of a status code. The codes are the error classes of
+ * mlx-native dense_matmul_id.rs (`MlxError::InvalidArgument` and friends
+ * returned by `dense_matmul_id_capability` / `dense_matmul_id`), split by
+ * cause. */
 const char *mm_status_string(mm_status status);
 
-/* Message for the last failing call on the calling thread ("" if none). */
+/* Message for the last failing call on the calling thread ("" if none): the
+ * detail text that mlx-native dense_matmul_id.rs puts inside each
+ * `MlxError::InvalidArgument` (which dimension, extent or buffer failed). */
 const char *mm_last_error(void);
 
 /* ------------------------------------------------------------------------ */

@@ -125,7 +125,7 @@ MOE = dict(m=512, n=1408, k=2048, top_k=8, n_experts=64, expert_stride_bytes=140
 def test_id_query_extents_moe():
     p = mm.id_params(**MOE, input_layout=0, multiplicity=0, route=1)
     cap = mm.mm_id_query(mm.MM_BF16, p)
-    assert cap.schema_version == mm.MM_ID_SCHEMA_VERSION == 4
+    assert cap.schema_version == mm.MM_ID_SCHEMA_VERSION == 5
     assert cap.weight_bytes == 64 * 1408 * 2048 * 2 == 369_098_752
     assert cap.input_bytes == 512 * 2048 * 4 == 4_194_304
     assert cap.ids_bytes == 512 * 8 * 4 == 16_384
@@ -256,5 +256,5 @@ def test_struct_layouts_match_header():
     assert ctypes.sizeof(mm.GemmDesc) == 4 * 3 + 4 + 8 * 13
     assert ctypes.sizeof(mm.IdParams) == 48
     assert ctypes.sizeof(mm.IdCapability) == 16 + 48
-    assert ctypes.sizeof(mm.Receipt) == 20
+    assert ctypes.sizeof(mm.Receipt) == 24
     assert ctypes.sizeof(mm.DeviceCaps) == 64 + 16 + 8 + 16
