@@ -53,8 +53,6 @@ PAGE_SHAPES = [
 def test_page_shapes_f32(shape, ta, tb, order):
     b, m, x, y = shape
     k, n = (x, y) if order == "bmkn" else (y, x)
-    if m * n * k * b > 2e8:
-        pytest.skip("too large for the CPU oracle in a test")
     _say(f"page shape {shape} order={order} -> b={b} m={m} n={n} k={k} ta={ta} tb={tb}")
     case = wl.random_gemm_case(7, wl.F32, b, m, n, k, ta, tb)
     rec = check_gemm(case, what=f"{shape}")
@@ -297,6 +295,24 @@ def test_large_tile_route_broadcast_b():
                              broadcast_b=True, off_a=8, off_b=16, off_c=4)
     assert case.stride_b == 0
     _sampled_check(case, 4096, 7, kernel=mm.MM_KERNEL_GEMM_LARGE)
+
+
+@pytest.mark.parametrize("dt,seed", [(wl.F16, 44), (wl.BF16, 45)])
+def test_large_tile_route_full_compare(dt, seed):
+    """The 256 x 256 kernel at its smallest admissible size (512 tiles,
+    k = 256) with every output compared against the oracle."""
+    from gpu_util import GemmRun, assert_close
+    _say(f"large-tile NT full compare dt={wl.DTYPE_NAMES[dt]} m=4096 n=8192 k=256")
+    case = wl.random_gemm_case(seed, dt, 1, 4096, 8192, 256, False, True, dist="uniform")
+    run = GemmRun(case)
+    rec = run.run()
+    assert rec.kernel == mm.MM_KERNEL_GEMM_LARGE, rec.kernel
+    bits = run.c_bits()
+    got, mask = run.logical_c(bits)
+    run.check_untouched(bits, mask)
+    amax, bmax = run.operand_absmax()
+    err = assert_close(got, run.oracle_full(), case.dtype, case.k, amax, bmax, "large full")
+    _say(f"  max err {err:.3e}")
 
 
 @pytest.mark.parametrize("k", [128, 192, 320])

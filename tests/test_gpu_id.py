@@ -156,6 +156,67 @@ def test_ramp_bit_exact_pipelined_grouped(wdt):
     np.testing.assert_array_equal(got, ref)
 
 
+# Fragment slots per wave of the pipelined grouped kernel. The host sizes the
+# output tile so that (experts in use) x (output tiles) reaches the CU count,
+# then takes the fewest of 2, 4 or 6 slots of 16 outputs per wave that cover
+# the tile (f32 weights: at most 4). With 64 experts in use:
+#   n = 120  -> 64-wide tiles            -> 2 slots
+#   n = 1000 -> 256-wide tiles           -> 4 slots
+#   n = 1408 -> 352-wide tiles (2-byte)  -> 6 slots; f32: 240-wide -> 4 slots
+#   n = 1040 -> 272-wide tiles (2-byte)  -> 6 slots; f32: 208-wide -> 4 slots
+# (wdt, (m, n, k, top_k, E), slots)
+FRAG_CASES = [
+    (wl.BF16, (64, 120, 256, 4, 64), 2), (wl.F16, (64, 120, 256, 4, 64), 2),
+    (wl.F32, (64, 120, 256, 4, 64), 2),
+    (wl.BF16, (64, 1000, 256, 4, 64), 4), (wl.F16, (64, 1000, 256, 4, 64), 4),
+    (wl.F32, (64, 1000, 256, 4, 64), 4),
+    (wl.BF16, (64, 1408, 256, 4, 64), 6), (wl.F16, (64, 1408, 256, 4, 64), 6),
+    (wl.F32, (64, 1408, 256, 4, 64), 4),
+]
+
+
+@pytest.mark.parametrize("layout", [0, 1])
+@pytest.mark.parametrize("wdt,shape,slots", FRAG_CASES)
+def test_grouped_fragment_slots(wdt, shape, slots, layout):
+    """Every fragment-slot instance of the pipelined grouped kernel, every
+    weight dtype, both activation layouts, ragged tile edges (n not a
+    multiple of the tile width), out-of-range ids: all routed rows against
+    the oracle; the receipt names the instance that ran."""
+    m, n, k, top_k, E = shape
+    _say(f"grouped slots={slots} wdt={wl.DTYPE_NAMES[wdt]} layout={layout} shape={shape}")
+    case = _with_bad_ids(wl.random_id_case(100 + n, wdt, m, n, k, top_k, E, layout=layout))
+    run = IdRun(case, route=1)
+    rec = run.run()
+    assert rec.kernel == mm.MM_KERNEL_ID_GROUPED_MFMA, rec.kernel
+    assert rec.variant == slots, f"fragment slots {rec.variant}, expected {slots}"
+    _check_map(run)
+    _check_all_rows(run, f"grouped slots={slots}")
+
+
+@pytest.mark.parametrize("wdt,slots", [(wl.BF16, 6), (wl.F16, 6), (wl.F32, 4)])
+def test_grouped_wide_tiles_full_row_tiles_ramp_exact(wdt, slots):
+    """The widest tile of each weight dtype with more than 128 routed rows per
+    expert (full 128-row tiles, several row tiles per expert, a ragged last
+    one): ramp inputs make every partial sum exact, so the output equals the
+    rounded oracle bit for bit."""
+    m, n, k, top_k, E = 1024, 1040, 256, 8, 64
+    _say(f"grouped ramp exact slots={slots} wdt={wl.DTYPE_NAMES[wdt]} m={m} n={n} k={k}")
+    rng = np.random.default_rng(72)
+    w = wl.ramp(E * n * k, 5).reshape(E, n, k)
+    x = wl.ramp(m * k, 6).reshape(m, k)
+    ids = wl.distinct_ids(rng, m, top_k, E)
+    case = wl.make_id_case(wdt, w, x, ids)
+    run = IdRun(case, route=1)
+    rec = run.run()
+    assert rec.kernel == mm.MM_KERNEL_ID_GROUPED_MFMA and rec.variant == slots, \
+        (rec.kernel, rec.variant)
+    counts, _ = run.scratch()
+    assert counts.max() > 128
+    got = from_dev(run.out, np.float32).reshape(m * top_k, n)
+    ref = oracle.round_to(wl.F32, run.oracle())
+    np.testing.assert_array_equal(got, ref)
+
+
 def test_direct_repeats_and_dedup_rows_identical():
     m, n, k, top_k, E = 2, 300, 512, 8, 5
     _say("direct repeats")
