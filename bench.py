@@ -11,15 +11,18 @@ GEMM, f16 GEMM 8192^3, 64-expert bf16 expert-ID prefill + decode) are timed
 the same way and reported under "workloads".
 
 Timing: inputs are resident in HBM before the timed region. Each workload
-rotates through enough copies of its operands that a buffer is reused only
-after >= 1 GiB of other traffic (more than the 256 MB Infinity Cache). The
-rotated calls are captured once in a HIP graph and the graph is replayed;
-the time per step comes from HIP events recorded on the stream the kernels
-run on, bracketed by device synchronisation, and is the median of five such
-timed runs.
+rotates through copies of its operands (call i uses copy i % copies) so that
+a buffer is reused only after >= 1 GiB of other traffic (more than the
+256 MB Infinity Cache) when --steps reaches the copy count. Exactly --steps
+calls are captured in one HIP graph; the time per step comes from HIP events
+recorded around one replay on the stream the kernels run on, bracketed by
+device synchronisation, and is the median of five such timed replays.
 
-cpu_baseline: the CPU oracle (test infrastructure, fp64 triple loops) timed
-on this host on the same decode GEMV, repeated to about ten seconds of work.
+cpu_baseline: the CPU oracle (test infrastructure, fp64 triple loops,
+untuned) timed on this host's cores for every workload, on a bounded sample
+scaled to the whole workload (single-thread times too for the three small
+GEMM workloads); the headline line carries the decode GEMV's, each workload
+entry its own. Baseline only.
 
 vendor (GEMM workloads, context only): torch's own matmul (rocBLAS /
 hipBLASLt) on the same operand copies, timed the same way right after this
@@ -91,43 +94,39 @@ class Timer:
         self.use_graph = use_graph
 
     def time(self, step, n_rot, steps, warmup, repeats=5):
-        """ms per step: the median over `repeats` timed runs of `steps` calls."""
+        """ms per step: the median over `repeats` timed runs of exactly `steps`
+        calls, call i using rotation i % n_rot."""
         torch = self.torch
         with torch.cuda.stream(self.stream):
             for i in range(warmup):
                 step(i % n_rot)
             torch.cuda.synchronize()
             if self.use_graph:
-                reps = max(1, steps // n_rot)
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=self.stream):
-                    for i in range(n_rot):
-                        step(i)
+                    for i in range(steps):
+                        step(i % n_rot)
                 g.replay()
                 torch.cuda.synchronize()
-                n = reps * n_rot
                 runs = []
                 for _ in range(repeats):
                     t0 = torch.cuda.Event(enable_timing=True)
                     t1 = torch.cuda.Event(enable_timing=True)
                     t0.record(self.stream)
-                    for _ in range(reps):
-                        g.replay()
+                    g.replay()
                     t1.record(self.stream)
                     torch.cuda.synchronize()
-                    runs.append(t0.elapsed_time(t1) / n)
+                    runs.append(t0.elapsed_time(t1) / steps)
                 runs.sort()
-                return runs[len(runs) // 2], n
-            else:
-                t0 = torch.cuda.Event(enable_timing=True)
-                t1 = torch.cuda.Event(enable_timing=True)
-                t0.record(self.stream)
-                for i in range(steps):
-                    step(i % n_rot)
-                t1.record(self.stream)
-                torch.cuda.synchronize()
-                n = steps
-        return t0.elapsed_time(t1) / n, n  # ms per step
+                return runs[len(runs) // 2], steps
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            t0.record(self.stream)
+            for i in range(steps):
+                step(i % n_rot)
+            t1.record(self.stream)
+            torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps, steps  # ms per step
 
 
 def sample_clock(torch, dev, stream, step, n_rot, seconds=1.5):
@@ -220,6 +219,125 @@ def to_dev_bits(torch, dev, bits):
     view = {np.dtype(np.float32): None, np.dtype(np.uint16): np.int16,
             np.dtype(np.uint32): np.int32}[bits.dtype]
     return torch.from_numpy(bits if view is None else bits.view(view)).to(dev)
+
+
+def cpu_info():
+    """(model string, logical CPUs this process may use, OpenMP default threads)."""
+    import oracle
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except AttributeError:
+        nproc = os.cpu_count() or 1
+    return model, nproc, oracle.max_threads()
+
+
+def cpu_baselines(wl, want):
+    """The CPU oracle (test infrastructure, fp64 triple loops, untuned) timed
+    on this host, per workload: a bounded sample of the workload's outputs,
+    its time scaled to the whole workload, on every OpenMP thread and, for the
+    three small GEMM workloads, on one thread. Baseline only."""
+    import oracle
+    model, nproc, threads = cpu_info()
+    out = {"cpu_model": model, "nproc": nproc, "threads": threads, "workloads": {}}
+
+    def timed(fn, min_s):
+        reps, total = 0, 0.0
+        while total < min_s:
+            t0 = time.perf_counter()
+            fn()
+            total += time.perf_counter() - t0
+            reps += 1
+        return total / reps, reps
+
+    def entry(name, sec_full, unit, per_call, what, reps, threads_used, single=None):
+        val = per_call / sec_full
+        e = {"value": val, "unit": unit, "cores": threads_used, "sample": what,
+             "seconds_per_call": sec_full, "repetitions": reps}
+        if single is not None:
+            e["single_thread_value"] = per_call / single
+            e["single_thread_seconds_per_call"] = single
+        out["workloads"][name] = e
+        log(f"cpu oracle {name}: {val:.4g} {unit} on {threads_used} threads"
+            + (f", {per_call / single:.4g} {unit} on 1 thread" if single else "") + f" ({what})")
+
+    def gemm_full(case, nt):
+        return lambda: oracle.gemm(case.dtype, case.batch, case.m, case.n, case.k, case.trans_a,
+                                   case.trans_b, case.lda, case.ldb, case.stride_a,
+                                   case.stride_b, case.off_a, case.off_b, case.A, case.B, nt)
+
+    if want("gemm_f32_128"):
+        case = wl.gemm_f32_128()
+        t, r = timed(gemm_full(case, threads), 0.5)
+        t1, _ = timed(gemm_full(case, 1), 0.5)
+        entry("gemm_f32_128", t, "TFLOP/s", case.flops / 1e12,
+              "the full 128^3 f32 product, repeated", r, threads, t1)
+    if want("gemv_f16_decode"):
+        case = wl.gemv_f16_decode()
+        alg = case.B.nbytes + case.A.nbytes + 11008 * 2
+        t, r = timed(gemm_full(case, threads), 2.0)
+        t1, _ = timed(gemm_full(case, 1), 0.5)
+        entry("gemv_f16_decode", t, "GB/s", alg / 1e9,
+              "the full f16 decode GEMV (1 x 4096 by 11008 x 4096), repeated", r, threads, t1)
+    if want("gemm_f16_batched"):
+        case = wl.gemm_f16_batched()
+        alg = case.A.nbytes + case.B.nbytes + 32 * 512 * 512 * 2
+        t, r = timed(gemm_full(case, threads), 0.5)
+        # one thread: batch item 0 of 32, scaled by 32
+        one = wl.gemm_f16_batched()
+        t1, _ = timed(lambda: oracle.gemm(one.dtype, 1, one.m, one.n, one.k, one.trans_a,
+                                          one.trans_b, one.lda, one.ldb, one.stride_a,
+                                          one.stride_b, 0, 0, one.A, one.B, 1), 0.1)
+        entry("gemm_f16_batched", t, "GB/s", alg / 1e9,
+              "the full batched product on all threads; one thread: batch item 0 of 32, x32",
+              r, threads, t1 * 32)
+    if want("gemm_f16_large"):
+        case = wl.gemm_f16_large()
+        rows = 16
+        rng = np.random.default_rng(0)
+        is_ = np.repeat(rng.choice(case.m, rows, replace=False), case.n)
+        js = np.tile(np.arange(case.n), rows)
+        bs = np.zeros_like(is_)
+        t, r = timed(lambda: oracle.gemm_at(case.dtype, case.k, case.trans_a, case.trans_b,
+                                            case.lda, case.ldb, 0, 0, 0, 0, case.A, case.B,
+                                            bs, is_, js, threads), 0.5)
+        entry("gemm_f16_large", t * case.m / rows, "TFLOP/s", case.flops / 1e12,
+              f"{rows} random output rows of 8192 (all 8192 columns each), time x{case.m // rows}",
+              r, threads)
+    if want("moe_prefill") or want("moe_decode"):
+        moe = wl.moe_bf16()
+        pre, dec = moe.prefill, moe.decode
+        if want("moe_prefill"):
+            nr = 128
+            rows = np.random.default_rng(0).choice(pre.m * pre.top_k, nr, replace=False)
+            alg = pre.W.nbytes + pre.X.nbytes + pre.ids.nbytes + pre.m * pre.top_k * pre.n * 4
+            t, r = timed(lambda: oracle.matmul_id_rows(pre.wdtype, pre.m, pre.n, pre.k,
+                                                       pre.top_k, pre.n_experts,
+                                                       pre.expert_stride_bytes, 0, pre.W,
+                                                       pre.X, pre.ids, rows, threads), 0.5)
+            tot = pre.m * pre.top_k
+            entry("moe_prefill", t * tot / nr, "GB/s", alg / 1e9,
+                  f"{nr} random routed rows of {tot} (every output of each), time x{tot // nr}",
+                  r, threads)
+        if want("moe_decode"):
+            u = len(set(int(v) for v in dec.ids.reshape(-1)))
+            alg = u * dec.n * dec.k * 2 + dec.X.nbytes + dec.ids.nbytes + dec.top_k * dec.n * 4
+            t, r = timed(lambda: oracle.matmul_id(dec.wdtype, dec.m, dec.n, dec.k, dec.top_k,
+                                                  dec.n_experts, dec.expert_stride_bytes,
+                                                  dec.layout, dec.W, dec.X, dec.ids, threads),
+                         1.0)
+            entry("moe_decode", t, "GB/s", alg / 1e9,
+                  "the full decode (8 routed rows, repeated expert computed per slot), repeated",
+                  r, threads)
+    return out
 
 
 def main():
@@ -341,7 +459,7 @@ def main():
         def step(i):
             mm.mm_gemm(d, bufs[i][0], bufs[i][1], cbuf, stream=stream)
 
-        steps = args.steps if case.flops < 1e11 else max(n_rot, args.steps // 10)
+        steps = args.steps
         ms, n = timer.time(step, n_rot, steps, args.warmup)
         sec = ms * 1e-3
         tflops = case.flops / sec / 1e12
@@ -417,7 +535,7 @@ def main():
             def step(i):
                 mm.mm_id(p, wl.BF16, wb[i], xb, ib, ob, cb, rb, stream=stream)
 
-            ms, n = timer.time(step, n_rot, max(n_rot, args.steps // 4), args.warmup)
+            ms, n = timer.time(step, n_rot, args.steps, args.warmup)
             alg = wbytes + pre.X.nbytes + pre.ids.nbytes + out.numel() * 4
             sec = ms * 1e-3
             results["moe_prefill"] = {
@@ -450,7 +568,7 @@ def main():
             def step(i):
                 mm.mm_id_direct(p, wl.BF16, wb[i], xb, ib, ob, stream=stream)
 
-            ms, n = timer.time(step, n_rot_d, max(n_rot_d, args.steps), args.warmup)
+            ms, n = timer.time(step, n_rot_d, args.steps, args.warmup)
             alg = per_call + dec.X.nbytes + dec.ids.nbytes + out.numel() * 4
             sec = ms * 1e-3
             results[name] = {
@@ -467,22 +585,17 @@ def main():
 
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
-    if not args.no_cpu and want("gemv_f16_decode"):
-        import oracle
-        case = wl.gemv_f16_decode()
-        alg = case.B.nbytes + case.A.nbytes + 11008 * 2
-        reps, t_total = 0, 0.0
-        while t_total < 10.0 and reps < 1000:
-            t0 = time.perf_counter()
-            oracle.gemm(case.dtype, 1, 1, case.n, case.k, False, True, case.lda, case.ldb, 0, 0,
-                        0, 0, case.A, case.B)
-            t_total += time.perf_counter() - t0
-            reps += 1
-        cpu = {"value": alg * reps / t_total / 1e9, "unit": "GB/s",
-               "cores": oracle.max_threads(), "kind": "oracle",
-               "sample": f"the full f16 decode GEMV (1 x 4096 by 11008 x 4096), "
-                         f"{reps} repetitions, {t_total:.1f} s of fp64 oracle work"}
-        log(f"cpu oracle: {cpu['value']:.3f} GB/s on {cpu['cores']} threads ({reps} reps)")
+    if not args.no_cpu:
+        cpu_all = cpu_baselines(wl, want)
+        for name, ent in cpu_all["workloads"].items():
+            if name in results:
+                results[name]["cpu_baseline"] = ent
+        head_cpu = cpu_all["workloads"].get("gemv_f16_decode")
+        if head_cpu is not None:
+            cpu = dict(head_cpu)
+            cpu["kind"] = "oracle"
+            cpu["cpu_model"] = cpu_all["cpu_model"]
+            cpu["nproc"] = cpu_all["nproc"]
 
     head = results.get("gemv_f16_decode")
     traffic = None
