@@ -42,8 +42,9 @@ EXPORTS = [
     "mm_gemm", "mm_gemm_ex", "mm_gemv", "mm_id_query", "mm_id_route_hint", "mm_id_direct", "mm_id_map",
     "mm_id_grouped",
     "mm_id", "mm_capabilities", "mm_status_string", "mm_last_error",
-    "mm_test_inject_resolve_failure", "mm_test_launch_count",
+    "mm_test_inject_resolve_failure", "mm_test_launch_count", "mm_id_prefill_noalloc",
 ]
+MM_ID_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 
 class MmError(RuntimeError):
@@ -133,6 +134,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.mm_id.argtypes = [P(IdParams), ctypes.c_int, Buf, Buf, Buf, Buf, Buf, Buf, vp,
                           P(Receipt)]
     lib.mm_id.restype = st
+    lib.mm_id_prefill_noalloc.argtypes = [P(IdParams), ctypes.c_int, Buf, Buf, Buf, Buf, vp,
+                                          P(Receipt)]
+    lib.mm_id_prefill_noalloc.restype = st
     lib.mm_capabilities.argtypes = [ctypes.c_int, P(DeviceCaps)]
     lib.mm_capabilities.restype = st
     lib.mm_status_string.argtypes = [ctypes.c_int]
@@ -247,6 +251,15 @@ def mm_id(params: IdParams, weight_dtype: int, weights: Buf, inp: Buf, ids: Buf,
     _raise(load().mm_id(ctypes.byref(params), weight_dtype, weights, inp, ids, out,
                         counts or Buf(None, 0), routed_rows or Buf(None, 0), _stream(stream),
                         ctypes.byref(r)))
+    return r
+
+
+def mm_id_prefill_noalloc(params: IdParams, weight_dtype: int, weights: Buf, inp: Buf, ids: Buf,
+                          out: Buf, stream=None) -> Receipt:
+    """Map + grouped prefill with the library's own scratch (no allocation)."""
+    r = Receipt()
+    _raise(load().mm_id_prefill_noalloc(ctypes.byref(params), weight_dtype, weights, inp, ids,
+                                        out, _stream(stream), ctypes.byref(r)))
     return r
 
 

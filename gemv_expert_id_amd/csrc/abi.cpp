@@ -407,7 +407,7 @@ mmk::IdArgs id_args(const mm_id_params* p, mm_dtype wdt) {
     return a;
 }
 
-enum IdUse { USE_DIRECT, USE_MAP, USE_GROUPED, USE_PREFILL };
+enum IdUse { USE_DIRECT, USE_MAP, USE_GROUPED, USE_PREFILL, USE_PREFILL_NOALLOC };
 
 // Validates buffers for one use of the params (mlx-native
 // `validate_dense_matmul_id_call`).
@@ -421,7 +421,9 @@ mm_status id_validate(IdUse use, const mm_id_params* p, mm_dtype wdt, mm_buf wei
         return fail(MM_ERR_INVALID_ARGUMENT, "matmul_id: params.route = %u does not match this entry point (%s)",
                     p->route, want_route ? "grouped prefill" : "direct");
     const bool need_w = use != USE_MAP, need_in = use != USE_MAP;
-    const bool need_ids = use != USE_GROUPED, need_scr = use != USE_DIRECT;
+    // The allocation-free prefill keeps its scratch in the library's own array.
+    const bool need_ids = use != USE_GROUPED;
+    const bool need_scr = use != USE_DIRECT && use != USE_PREFILL_NOALLOC;
     Range rw{0, 0}, ri{0, 0}, rids{0, 0}, ro{0, 0}, rc{0, 0}, rr{0, 0};
     if (need_w && (st = check_buf("matmul_id weights", weights, 0, cap->weight_bytes,
                                   elt_size(wdt), &rw)) != MM_OK)
@@ -611,6 +613,41 @@ mm_status mm_id(const mm_id_params* params, mm_dtype weight_dtype, mm_buf weight
     hipStream_t s = static_cast<hipStream_t>(stream);
     mmk::IdArgs a = fill_ptrs(id_args(params, weight_dtype), weights, input, ids, out, counts,
                               routed_rows);
+    mmk::Launched L;
+    ++g_launches;
+    if ((st = finish(mmk::launch_id_map(a, s, &L), s, "id_map")) != MM_OK) return st;
+    ++g_launches;
+    if ((st = finish(mmk::launch_id_grouped(a, s, &L), s, "id_grouped")) != MM_OK) return st;
+    set_receipt(receipt, MM_ROUTE_ID_PREFILL, (uint32_t)weight_dtype, 2, L);
+    return ok();
+}
+
+mm_status mm_id_prefill_noalloc(const mm_id_params* params, mm_dtype weight_dtype, mm_buf weights,
+                                mm_buf input, mm_buf ids, mm_buf out, void* stream,
+                                mm_receipt* receipt) {
+    mm_id_capability cap;
+    mm_status st = id_validate(USE_PREFILL_NOALLOC, params, weight_dtype, weights, input, ids, out,
+                               mm_buf{nullptr, 0}, mm_buf{nullptr, 0}, &cap);
+    if (st != MM_OK) return st;
+    const uint64_t counts_span = (cap.counts_bytes + 255) / 256 * 256;
+    if (counts_span + cap.routed_rows_bytes > mmk::kStaticScratchBytes)
+        return fail(MM_ERR_SCRATCH,
+                    "matmul_id no-alloc prefill: scratch needs %llu + %llu bytes, the library's "
+                    "array holds %llu",
+                    (unsigned long long)counts_span, (unsigned long long)cap.routed_rows_bytes,
+                    (unsigned long long)mmk::kStaticScratchBytes);
+    if ((st = resolve("id_map")) != MM_OK) return st;
+    if ((st = resolve("id_grouped")) != MM_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* base = nullptr;
+    hipError_t err = mmk::static_scratch(s, &base);
+    if (err != hipSuccess)
+        return fail(MM_ERR_DEVICE, "matmul_id no-alloc prefill: scratch address lookup failed: %s",
+                    hipGetErrorString(err));
+    mm_buf counts{base, cap.counts_bytes};
+    mm_buf routed{static_cast<char*>(base) + counts_span, cap.routed_rows_bytes};
+    mmk::IdArgs a = fill_ptrs(id_args(params, weight_dtype), weights, input, ids, out, counts,
+                              routed);
     mmk::Launched L;
     ++g_launches;
     if ((st = finish(mmk::launch_id_map(a, s, &L), s, "id_map")) != MM_OK) return st;

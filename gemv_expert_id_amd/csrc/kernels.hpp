@@ -92,4 +92,9 @@ hipError_t launch_id_direct(const IdArgs& a, hipStream_t s, Launched* L);
 hipError_t launch_id_map(const IdArgs& a, hipStream_t s, Launched* L);
 hipError_t launch_id_grouped(const IdArgs& a, hipStream_t s, Launched* L);
 
+// Library-held scratch for the allocation-free prefill call: its size, and
+// its device address on the GPU of stream `s` (looked up once per GPU).
+constexpr uint64_t kStaticScratchBytes = MM_ID_NOALLOC_SCRATCH_BYTES;
+hipError_t static_scratch(hipStream_t s, void** out);
+
 }  // namespace mmk

@@ -14,6 +14,7 @@
 //              into bf16 hi + lo parts (two MFMAs, f32 accumulate); f32/f16
 //              weights run an LDS-tiled FMA kernel. The tile list is rebuilt
 //              from the counts inside every block, so the host never waits.
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -1230,6 +1231,49 @@ hipError_t launch_id_grouped(const IdArgs& a, hipStream_t s, Launched* L) {
     L->kernel = MM_KERNEL_ID_GROUPED_FMA;
     const void* fn = a.wdtype == 0 ? (const void*)&id_grouped_fma<TF32> : (const void*)&id_grouped_fma<TF16>;
     return hipLaunchKernel(fn, dim3((unsigned)g), dim3(kThreads), fargs, 0, s);
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free prefill entry point: counts[E] followed (at
+// the next 256-byte boundary) by routed_rows[E * m], u32. Each GPU holds its
+// own copy of the array until the process ends; every call on one GPU shares
+// it, so calls that overlap on one GPU race. Nothing in it needs clearing:
+// the map pass writes every count and every list entry the grouped pass reads.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint32_t scratch[kStaticScratchBytes / 4];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+// Device address of `scratch` on the GPU that runs `s` (the current device
+// for the null stream). The first call for a GPU looks the address up with
+// that GPU current and keeps it; host code never passes the array's own name
+// (a host-side stand-in) to a kernel or a copy.
+hipError_t static_scratch(hipStream_t s, void** out) {
+    int dev = -1;
+    hipError_t err = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = -1;
+        if ((err = hipGetDevice(&cur)) != hipSuccess) return err;
+        if (cur != dev && (err = hipSetDevice(dev)) != hipSuccess) return err;
+        void* p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t back = hipSetDevice(cur);
+            if (err == hipSuccess) err = back;
+        }
+        if (err != hipSuccess) return err;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 }  // namespace mmk

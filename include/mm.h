@@ -296,6 +296,27 @@ mm_status mm_id(const mm_id_params *params, mm_dtype weight_dtype, mm_buf weight
                 mm_buf ids, mm_buf out, mm_buf counts, mm_buf routed_rows, void *stream,
                 mm_receipt *receipt);
 
+/*
+ * The grouped prefill (map launch, then grouped launch) without caller
+ * scratch and without any allocation: for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Same results, validation and errors as
+ * mm_id with params->route == 1, except that counts and routed_rows live in
+ * an array the library holds on each GPU (MM_ID_NOALLOC_SCRATCH_BYTES, kept
+ * until the process ends): counts at its start, routed rows at the next
+ * 256-byte boundary. A problem whose scratch does not fit
+ * (round_up(4 * n_experts, 256) + 4 * n_experts * m bytes above the limit)
+ * fails with MM_ERR_SCRATCH before anything is enqueued. The call makes no
+ * hipMalloc / hipFree and calls no allocating routine; its first call on a
+ * GPU looks up that GPU's array address once. Every call on one GPU shares
+ * the array: calls that overlap on one GPU (two streams at once) race and
+ * give unspecified results. The caller still passes inputs and outputs.
+ */
+#define MM_ID_NOALLOC_SCRATCH_BYTES (4u << 20)
+mm_status mm_id_prefill_noalloc(const mm_id_params *params, mm_dtype weight_dtype,
+                                mm_buf weights, mm_buf input, mm_buf ids, mm_buf out,
+                                void *stream, mm_receipt *receipt);
+
 /* ------------------------------------------------------------------------ */
 /* Device and library information                                            */
 /* ------------------------------------------------------------------------ */

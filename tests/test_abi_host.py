@@ -242,6 +242,29 @@ def test_prefill_fails_closed_on_grouped_resolution():
     lib.mm_test_inject_resolve_failure(None)
 
 
+def test_noalloc_prefill_rejects_before_enqueue():
+    """The allocation-free prefill: a problem whose scratch exceeds the
+    library's array, a direct-route params block and an unresolvable grouped
+    kernel all fail before anything is enqueued."""
+    lib = mm.load()
+    E, m, top_k = 1024, 1024, 1
+    pg = mm.id_params(m, 1, 1, top_k, E, 4, 0, 0, 1)
+    cap = mm.mm_id_query(mm.MM_F32, pg)
+    need = -(-cap.counts_bytes // 256) * 256 + cap.routed_rows_bytes
+    assert need > mm.MM_ID_NOALLOC_SCRATCH_BYTES
+    w, x, ids, out, _, _ = _id_bufs(cap)
+    msg = _fails(6, mm.mm_id_prefill_noalloc, pg, mm.MM_F32, w, x, ids, out)
+    assert "holds" in msg
+    pd = mm.id_params(9, 7, 35, 2, 4, 7 * 35 * 4, 0, 1, 0)
+    capd = mm.mm_id_query(mm.MM_F32, pd)
+    w, x, ids, out, _, _ = _id_bufs(capd)
+    _fails(1, mm.mm_id_prefill_noalloc, pd, mm.MM_F32, w, x, ids, out)
+    pg = mm.id_params(9, 7, 35, 2, 4, 7 * 35 * 4, 0, 0, 1)
+    lib.mm_test_inject_resolve_failure(b"id_grouped")
+    _fails(2, mm.mm_id_prefill_noalloc, pg, mm.MM_F32, w, x, ids, out)
+    lib.mm_test_inject_resolve_failure(None)
+
+
 def test_capabilities_without_gpu():
     import torch
     if torch.cuda.is_available():
