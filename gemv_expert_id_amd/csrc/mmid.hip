@@ -251,6 +251,150 @@ __global__ __launch_bounds__(kThreads) void id_direct_fast(IdArgs a) {
     }
 }
 
+// Direct route, staged form: the same block shape and weight stream as
+// id_direct_fast, with the activation row of the block's (token, slot) staged
+// in LDS once per block (k * 4 bytes, k = 1024 * XPT with XPT in {1, 2, 4, 8}).
+// Its loads are issued next to the id load, before the expert is known, and
+// each wave then reads its activation chunks from LDS instead of from L2.
+//   REUSE (slotted layout, one weight group per row): the first slot of a
+//   token naming expert e keeps its weight chunks in registers and also
+//   computes every later slot naming e, staging that slot's activation row
+//   in turn, so a repeated expert is streamed once.
+template <class T, bool ONE, bool REUSE, int XPT>  // XPT = k / 4 / kThreads exactly
+__global__ __launch_bounds__(kThreads) void id_direct_staged(IdArgs a) {
+    using S = typename T::store_t;
+    constexpr int CH = T::Elems16;
+    constexpr int G = kWave * DU;  // chunks per group
+    extern __shared__ __attribute__((aligned(16))) float xs[];  // k floats
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int64_t per_block = (int64_t)kWaves * DR;
+    const int64_t nchunks = (a.n + per_block - 1) / per_block;
+    const int64_t rows = (int64_t)a.m * a.top_k;
+    const int64_t ngroups = (int64_t)a.k / CH / G;
+    for (int64_t work = blockIdx.x; work < rows * nchunks; work += gridDim.x) {
+        // Everything up to the barriers below is uniform across the block
+        // (r, t, s, e depend on the work item only), so every wave reaches
+        // the same barriers.
+        const int64_t r = work / nchunks;
+        const int64_t j0 = (work % nchunks) * per_block + (int64_t)wave * DR;
+        const int64_t t = r / a.top_k;
+        const int s = (int)(r % a.top_k);
+        const uint32_t v = lane < a.top_k ? a.ids[t * a.top_k + lane] : 0xffffffffu;
+        auto xrow = [&](int slot) {
+            return reinterpret_cast<const float*>(reinterpret_cast<const char*>(a.X) +
+                                                  t * a.x_tok_stride_bytes +
+                                                  slot * a.x_slot_stride_bytes);
+        };
+        // Activation chunks of this slot (XPT per thread), in flight beside
+        // the id load.
+        u32x4 xv[XPT];
+        {
+            const float* x = xrow(s);
+#pragma unroll
+            for (int i = 0; i < XPT; ++i) xv[i] = ld16(x + 4 * (tid + i * kThreads));
+        }
+        const uint32_t e = __builtin_amdgcn_readlane(v, s);
+        float* out_r = a.out + r * a.n;
+        if (e >= a.n_experts) {  // no weight address is formed
+            if (lane < DR && j0 + lane < a.n) out_r[j0 + lane] = 0.f;
+            continue;
+        }
+        // Slots of this token naming expert e: the shared layout writes one
+        // result to all of them; REUSE computes each with its own row.
+        const uint64_t same = (a.dedup || REUSE) ? (uint64_t)__ballot(v == e) : (1ull << s);
+        if (same & ((1ull << s) - 1)) continue;  // an earlier slot owns this expert
+        const S* We = reinterpret_cast<const S*>(reinterpret_cast<const char*>(a.W) +
+                                                 (uint64_t)e * a.expert_stride_bytes);
+        const S* rowp[DR];
+#pragma unroll
+        for (int q = 0; q < DR; ++q) {
+            const int64_t j = j0 + q < a.n ? j0 + q : a.n - 1;
+            rowp[q] = We + j * a.k;
+        }
+        u32x4 wv[DR][DU];
+#pragma unroll
+        for (int q = 0; q < DR; ++q)
+#pragma unroll
+            for (int u = 0; u < DU; ++u) wv[q][u] = ld16_stream(rowp[q] + (lane + kWave * u) * CH);
+        __syncthreads();  // the previous work item's readers are done with xs
+#pragma unroll
+        for (int i = 0; i < XPT; ++i) *reinterpret_cast<u32x4*>(&xs[4 * (tid + i * kThreads)]) = xv[i];
+        __syncthreads();
+
+        // acc[q] = W rows . staged activation row
+        auto dot = [&](float (&acc)[DR]) {
+#pragma unroll
+            for (int q = 0; q < DR; ++q) acc[q] = 0.f;
+            for (int64_t g = 0; g < (ONE ? 1 : ngroups); ++g) {
+                u32x4 nv[ONE ? 1 : DR][DU];
+                const bool more = !ONE && g + 1 < ngroups;
+                if constexpr (!ONE) if (more) {
+#pragma unroll
+                    for (int q = 0; q < DR; ++q)
+#pragma unroll
+                        for (int u = 0; u < DU; ++u)
+                            nv[q][u] = ld16_stream(rowp[q] + ((g + 1) * G + lane + kWave * u) * CH);
+                }
+#pragma unroll
+                for (int u = 0; u < DU; ++u) {
+                    const float* xl = &xs[(g * G + lane + kWave * u) * CH];
+                    float xf[CH];
+#pragma unroll
+                    for (int h = 0; h < CH / 4; ++h)
+                        unpack4(*reinterpret_cast<const u32x4*>(xl + 4 * h), &xf[4 * h]);
+#pragma unroll
+                    for (int q = 0; q < DR; ++q) {
+                        float wf[CH];
+                        unpack_w<T>(wv[q][u], wf);
+#pragma unroll
+                        for (int c = 0; c < CH; ++c) acc[q] = __builtin_fmaf(wf[c], xf[c], acc[q]);
+                    }
+                }
+                if constexpr (!ONE) if (more) {
+#pragma unroll
+                    for (int q = 0; q < DR; ++q)
+#pragma unroll
+                        for (int u = 0; u < DU; ++u) wv[q][u] = nv[q][u];
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < DR; ++q) acc[q] = wave_sum(acc[q]);
+        };
+        float acc[DR];
+        dot(acc);
+        const uint64_t later = same & ~((2ull << s) - 1);  // s < 64
+#pragma unroll
+        for (int q = 0; q < DR; ++q) {
+            if (lane == q && j0 + q < a.n) {
+                out_r[j0 + q] = acc[q];
+                if constexpr (!REUSE)
+                    for (uint64_t mk = later; mk; mk &= mk - 1) {
+                        const int64_t s3 = __builtin_ctzll(mk);
+                        a.out[(t * a.top_k + s3) * a.n + j0 + q] = acc[q];
+                    }
+            }
+        }
+        if constexpr (REUSE) {
+            static_assert(ONE, "slot reuse keeps one weight group in registers");
+            for (uint64_t mk = later; mk; mk &= mk - 1) {
+                const int s3 = __builtin_ctzll(mk);
+                const float* x3 = xrow(s3);
+#pragma unroll
+                for (int i = 0; i < XPT; ++i) xv[i] = ld16(x3 + 4 * (tid + i * kThreads));
+                __syncthreads();  // every wave is done reading the previous row
+#pragma unroll
+                for (int i = 0; i < XPT; ++i)
+                    *reinterpret_cast<u32x4*>(&xs[4 * (tid + i * kThreads)]) = xv[i];
+                __syncthreads();
+                dot(acc);
+#pragma unroll
+                for (int q = 0; q < DR; ++q)
+                    if (lane == q && j0 + q < a.n) a.out[(t * a.top_k + s3) * a.n + j0 + q] = acc[q];
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Map pass: one workgroup of W waves (W chosen by the host so the LDS tables
 // fit). Wave w owns a contiguous segment of routed rows; LDS holds its
@@ -1146,10 +1290,39 @@ hipError_t launch_id_direct(const IdArgs& a, hipStream_t s, Launched* L) {
         const int64_t work = (int64_t)a.m * a.top_k * ((a.n + per_block - 1) / per_block);
         const unsigned grid = (unsigned)(work < (1ll << 30) ? work : (1ll << 30));
         const bool one = a.k == ch * kWave * DU;
+        L->kernel = MM_KERNEL_ID_DIRECT_FAST;
+        const int64_t xpt = a.k / 4 / kThreads;  // k is a multiple of 1024 here
+        if (xpt == 1 || xpt == 2 || xpt == 4 || xpt == 8) {
+            // Activation row staged in LDS; the slotted layout with one weight
+            // group per row reuses a repeated expert's weights across slots.
+            // One weight group is k = 2048 (2-byte weights, XPT 2) or k = 1024
+            // (f32, XPT 1).
+            const bool reuse = a.layout == 1 && one;
+            L->variant = reuse ? 2 : 1;
+            const void* fn = nullptr;
+            if (one) {
+                if (a.wdtype == 0)
+                    fn = reuse ? (const void*)&id_direct_staged<TF32, true, true, 1>
+                               : (const void*)&id_direct_staged<TF32, true, false, 1>;
+                else if (a.wdtype == 1)
+                    fn = reuse ? (const void*)&id_direct_staged<TF16, true, true, 2>
+                               : (const void*)&id_direct_staged<TF16, true, false, 2>;
+                else
+                    fn = reuse ? (const void*)&id_direct_staged<TBF16, true, true, 2>
+                               : (const void*)&id_direct_staged<TBF16, true, false, 2>;
+            } else {
+#define MM_DS(T) (xpt == 1 ? (const void*)&id_direct_staged<T, false, false, 1>   \
+                  : xpt == 2 ? (const void*)&id_direct_staged<T, false, false, 2> \
+                  : xpt == 4 ? (const void*)&id_direct_staged<T, false, false, 4> \
+                             : (const void*)&id_direct_staged<T, false, false, 8>)
+                fn = a.wdtype == 0 ? MM_DS(TF32) : a.wdtype == 1 ? MM_DS(TF16) : MM_DS(TBF16);
+#undef MM_DS
+            }
+            return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, (size_t)a.k * 4, s);
+        }
 #define MM_DF(T) (one ? (const void*)&id_direct_fast<T, true> : (const void*)&id_direct_fast<T, false>)
         const void* fn = a.wdtype == 0 ? MM_DF(TF32) : a.wdtype == 1 ? MM_DF(TF16) : MM_DF(TBF16);
 #undef MM_DF
-        L->kernel = MM_KERNEL_ID_DIRECT_FAST;
         return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
     }
     L->kernel = MM_KERNEL_ID_DIRECT;

@@ -109,7 +109,12 @@ typedef struct {
                                  MM_KERNEL_ID_GROUPED_MFMA the 16-output
                                  fragment slots per wave (2, 4 or 6) of the
                                  pipelined form, 0 for its 8-wave LDS-split
-                                 bf16 form; 0 for every other family */
+                                 bf16 form; for MM_KERNEL_ID_DIRECT_FAST 0
+                                 when activations come from L2, 1 when the
+                                 block stages its activation row in LDS, 2
+                                 when it also reuses a repeated expert's
+                                 weights across slots (slotted layout); 0 for
+                                 every other family */
 } mm_receipt;
 
 /* ------------------------------------------------------------------------ */

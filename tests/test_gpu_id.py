@@ -217,6 +217,33 @@ def test_grouped_wide_tiles_full_row_tiles_ramp_exact(wdt, slots):
     np.testing.assert_array_equal(got, ref)
 
 
+@pytest.mark.parametrize("wdt", DTYPES)
+@pytest.mark.parametrize("layout", [0, 1])
+def test_direct_staged_instances_ramp_exact(wdt, layout):
+    """The direct route's staged kernel: activation row in LDS (variant 1), and
+    with the slotted layout and one weight group per row (k = 2048 for 2-byte
+    weights, 1024 for f32) the first slot naming an expert also computes the
+    later slots naming it (variant 2). Many repeats per token, an
+    out-of-range id; ramp inputs make the output exact, compared bit for bit."""
+    m, n, top_k, E = 3, 40, 12, 3
+    k = 1024 if wdt == wl.F32 else 2048
+    rng = np.random.default_rng(73)
+    w = wl.ramp(E * n * k, 7).reshape(E, n, k)
+    rows = m if layout == 0 else m * top_k
+    x = wl.ramp(rows * k, 8).reshape(rows, k)
+    ids = rng.integers(0, E, (m, top_k)).astype(np.uint32)
+    ids[1, 5] = E + 1
+    case = wl.make_id_case(wdt, w, x, ids, layout=layout)
+    _say(f"direct staged wdt={wl.DTYPE_NAMES[wdt]} layout={layout}")
+    run = IdRun(case, route=0)
+    rec = run.run()
+    assert rec.kernel == mm.MM_KERNEL_ID_DIRECT_FAST, rec.kernel
+    assert rec.variant == (2 if layout == 1 else 1), rec.variant
+    got = from_dev(run.out, np.float32).reshape(m * top_k, n)
+    ref = oracle.round_to(wl.F32, run.oracle())
+    np.testing.assert_array_equal(got, ref)
+
+
 def test_direct_repeats_and_dedup_rows_identical():
     m, n, k, top_k, E = 2, 300, 512, 8, 5
     _say("direct repeats")

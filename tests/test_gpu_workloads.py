@@ -147,6 +147,7 @@ def test_moe_decode_slotted(moe):
     run = IdRun(case, route=0, multiplicity=1)
     rec = run.run()
     assert rec.route == mm.MM_ROUTE_ID_DIRECT
+    assert rec.kernel == mm.MM_KERNEL_ID_DIRECT_FAST and rec.variant == 2, (rec.kernel, rec.variant)
     got = run.out_f64()
     ref = run.oracle()
     wmax, xmax = finite_absmax(case.W, case.wdtype), float(np.abs(case.X).max())
