@@ -27,7 +27,7 @@ MM_ROUTE_GEMV_WIDE = 6
 (MM_KERNEL_GEMV_ROWS, MM_KERNEL_GEMV_ROWS_ELEM, MM_KERNEL_GEMV_COLS, MM_KERNEL_GEMM_TILED,
  MM_KERNEL_GEMM_LARGE, MM_KERNEL_GEMM_F32, MM_KERNEL_ID_DIRECT_FAST, MM_KERNEL_ID_DIRECT,
  MM_KERNEL_ID_MAP, MM_KERNEL_ID_GROUPED_MFMA, MM_KERNEL_ID_GROUPED_FMA,
- MM_KERNEL_GEMV_WIDE, MM_KERNEL_GEMM_F32_SMALL) = range(13)
+ MM_KERNEL_GEMV_WIDE, MM_KERNEL_GEMM_F32_SMALL, MM_KERNEL_GEMM_PANEL) = range(14)
 MM_ID_SCHEMA_VERSION = 5
 MM_ID_GROUPED_MAX_EXPERTS = 1024
 

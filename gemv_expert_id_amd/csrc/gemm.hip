@@ -417,6 +417,195 @@ __device__ __forceinline__ int lswz(int r) { return (r >> 2) & 3; }
 
 #define MM_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
+// ---------------------------------------------------------------------------
+// Batched short-K NT kernel: C[b] = A[b] . B[b]^T with A [m,k] and B [n,k]
+// both K-contiguous, k in {32, 64, 128}, m % 64 == 0, n % 128 == 0, 16-byte
+// aligned operands and C, beta == 0.
+//
+// With k this short the product is bound by memory (the batched 32 x 512 x
+// 512 x 128 workload does 85 FLOP per byte, below the MFMA ridge), and the
+// 128 x 128 kernels run fetch, MFMA and stores in lockstep across the whole
+// grid. Here a block owns one 64-row panel of A (kept in LDS for the whole
+// block) and walks the batch's B in tiles of 128 rows through three LDS
+// stages: B tile t+2 is in flight by DMA (buffer_load ... lds, 1 KiB per
+// instruction) while tile t is multiplied and its 64 x 128 output leaves
+// through a per-wave LDS stage as 16-byte row pieces, so the output stores
+// of one tile overlap the fetch of the next ones. Each wave computes 32 x 64
+// (2 x 4 fragments of v_mfma_f32_16x16x32). Rows of S = k / 8 16-byte chunks
+// are stored with chunk c of row r at slot c ^ ((r / (16 / S)) & (S - 1)), so
+// the fragment reads of 16 consecutive rows at one chunk index hit 16
+// distinct 16-byte bank groups; each DMA lane fetches the chunk that belongs
+// at its slot. Blocks are ordered so that the panels of one batch item run
+// on one XCD and share its B in L2.
+// ---------------------------------------------------------------------------
+constexpr int PM = 64, PThreads = 256, PStages = 3;
+
+template <int S>
+__device__ __forceinline__ int pswz(int r) {
+    return (r / (16 / S)) & (S - 1);
+}
+
+// Epilogue staging row pitch (halves) for a wave tile PN / 2 wide: 8 halves
+// of padding put the 16 rows one staging write covers in distinct banks.
+__host__ __device__ constexpr int panel_pitch(int PN) { return PN / 2 + 8; }
+
+// LDS of one block: A panel, PStages B stages of PN rows, four 32-row
+// epilogue stages.
+__host__ __device__ constexpr size_t panel_lds_bytes(int S, int PN) {
+    return ((size_t)(PM + PStages * PN) * S * 8 + 4 * 32 * panel_pitch(PN)) * sizeof(uint16_t);
+}
+
+// Block = one (batch item, 64-row panel of A, group of B tiles); `nsplit`
+// groups split the batch item's n / PN tiles (more blocks when there are few
+// panels), and the groups of one panel follow each other in the block order.
+template <class T, int S, int PN>
+__global__ __launch_bounds__(PThreads, 1) void gemm_nt_panel(GemmArgs a, int nsplit) {
+    constexpr int K = S * 8;          // contraction length
+    constexpr int RPI = 64 / S;       // tile rows per 1 KiB DMA instruction
+    constexpr int NA = PM / RPI / 4;  // A instructions per wave (= S / 4)
+    constexpr int NB = PN / RPI / 4;  // B instructions per wave per tile
+    constexpr int NV = S / 4;         // lane offset patterns (the swizzle repeats every 16 rows)
+    constexpr int WN = PN / 2;        // wave tile: 32 rows x WN columns
+    constexpr int FN = WN / 16;       // 16-column fragments per wave
+    constexpr int NST = PN / 32;      // store instructions per wave per tile (1 KiB each)
+    constexpr int SRW = 1024 / PN;    // rows per store instruction
+    constexpr int SLN = PN / 16;      // lanes per stored row (16 bytes each)
+    constexpr int AH = PM * K, BH = PN * K;  // halves per A panel / B stage
+    constexpr int PSP = panel_pitch(PN);
+    extern __shared__ __attribute__((aligned(1024))) uint16_t lds[];
+    uint16_t* const As = lds;
+    uint16_t* const Bs = lds + AH;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = w >> 1, wn = w & 1;
+    uint16_t* const stg = lds + AH + PStages * BH + w * 32 * PSP;
+
+    const int64_t panels = a.m / PM;
+    const int64_t items = panels * a.batch * nsplit;
+    const int64_t per_xcd = (items + 7) / 8;
+    const int64_t item = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (item >= items) return;
+    const int64_t pi = item / nsplit;
+    const int h = (int)(item % nsplit);
+    const int64_t b = pi / panels, m0 = (pi % panels) * PM;
+    const int all_tiles = (int)(a.n / PN);
+    const int t_begin = (int)((int64_t)all_tiles * h / nsplit);
+    const int ntiles = (int)((int64_t)all_tiles * (h + 1) / nsplit) - t_begin;
+    const int lda = (int)a.lda, ldb = (int)a.ldb;
+
+    const uint16_t* Ab = reinterpret_cast<const uint16_t*>(a.A) + b * a.sa;
+    const uint16_t* Bb = reinterpret_cast<const uint16_t*>(a.B) + b * a.sb;
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(Ab), (short)0, (int)(((a.m - 1) * a.lda + K) * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(Bb), (short)0, (int)(((a.n - 1) * a.ldb + K) * 2), 0x00020000);
+    // DMA lane offsets (bytes): the lane covers row lane / S of an
+    // instruction and fetches the chunk that the swizzle puts at slot
+    // lane % S. The swizzle depends on the row modulo 16 and every wave's
+    // first instruction starts at a multiple of 16 rows, so instruction jj
+    // uses pattern jj % NV (NV <= 4); named scalars, one per pattern.
+    const int lrow = lane / S, lslot = lane % S;
+    const int c0 = lslot ^ pswz<S>(lrow), c1 = lslot ^ pswz<S>(RPI + lrow);
+    const int c2 = lslot ^ pswz<S>(2 * RPI + lrow), c3 = lslot ^ pswz<S>(3 * RPI + lrow);
+    const int voa0 = (lrow * lda + c0 * 8) * 2, voa1 = (lrow * lda + c1 * 8) * 2;
+    const int voa2 = (lrow * lda + c2 * 8) * 2, voa3 = (lrow * lda + c3 * 8) * 2;
+    const int vob0 = (lrow * ldb + c0 * 8) * 2, vob1 = (lrow * ldb + c1 * 8) * 2;
+    const int vob2 = (lrow * ldb + c2 * 8) * 2, vob3 = (lrow * ldb + c3 * 8) * 2;
+    auto dma_a = [&]() {
+#pragma unroll
+        for (int jj = 0; jj < NA; ++jj) {
+            const int j = w * NA + jj;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, MM_LDS(As + j * RPI * K), 16,
+                                                     jj % NV == 0 ? voa0 : jj % NV == 1 ? voa1 : jj % NV == 2 ? voa2 : voa3,
+                                                     (int)((m0 + j * RPI) * lda * 2), 0, 0);
+        }
+    };
+    auto dma_b = [&](int t, int st) {  // t: tile index within the batch item
+#pragma unroll
+        for (int jj = 0; jj < NB; ++jj) {
+            const int j = w * NB + jj;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, MM_LDS(Bs + st * BH + j * RPI * K), 16,
+                                                     jj % NV == 0 ? vob0 : jj % NV == 1 ? vob1 : jj % NV == 2 ? vob2 : vob3,
+                                                     (t * PN + j * RPI) * ldb * 2, 0, 0);
+        }
+    };
+    // Fragment reads: lane -> row lane % 16 of a 16-row slab, chunk 4 * ks + lane / 16.
+    const int lr = lane & 15, lq = lane >> 4;
+    auto frag = [&](const uint16_t* base, int row0, int ks) {
+        return *reinterpret_cast<const u32x4*>(base + (row0 + lr) * K +
+                                               (((4 * ks + lq) ^ pswz<S>(lr)) << 3));
+    };
+    auto wait_vm = [](int n) {  // vmcnt <= n, lgkmcnt <= 0
+        if (n == NST) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(NST));
+        else if (n == 2 * NST) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(2 * NST));
+        else if (n == NB + NST) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(NB + NST));
+        else __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(NB + 2 * NST));
+    };
+
+    // Prologue: the A panel and the first two B tiles; wait for A and tile 0.
+    dma_a();
+    dma_b(t_begin, 0);
+    if (ntiles > 1) {
+        dma_b(t_begin + 1, 1);
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(NB));
+    } else {
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+    }
+    __builtin_amdgcn_s_barrier();
+
+    uint16_t* const Cb = reinterpret_cast<uint16_t*>(a.C) + b * a.sc + (m0 + wm * 32) * a.ldc + wn * WN;
+    for (int t = 0; t < ntiles; ++t) {
+        const int st = t % PStages;
+        // Stage (t + 2) % 3 held tile t - 1, which every wave finished before the barrier.
+        if (t + 2 < ntiles) dma_b(t_begin + t + 2, (t + 2) % PStages);
+        const uint16_t* Bt = Bs + st * BH;
+        f32x4 acc[2][FN];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < K / 32; ++ks) {
+            u32x4 fa[2], fb[FN];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) fa[i] = frag(As, wm * 32 + i * 16, ks);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) fb[j] = frag(Bt, wn * WN + j * 16, ks);
+            // D[n][m] = sum_k B(n,k) A(m,k): lane holds C[m = lane%16][n = 4*(lane/16) + q].
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] = mfma16<T>(fb[j], fa[i], acc[i][j]);
+        }
+        // Epilogue: the wave's 32 x WN piece through its LDS stage (LDS
+        // instructions of one wave complete in order), then 16-byte row
+        // pieces, 1 KiB per store instruction.
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const f32x4& v4 = acc[i][j];
+                u32x2 v;
+                v[0] = (uint32_t)narrow(T{}, a.alpha * v4[0]) | ((uint32_t)narrow(T{}, a.alpha * v4[1]) << 16);
+                v[1] = (uint32_t)narrow(T{}, a.alpha * v4[2]) | ((uint32_t)narrow(T{}, a.alpha * v4[3]) << 16);
+                *reinterpret_cast<u32x2*>(stg + (i * 16 + lr) * PSP + j * 16 + 4 * lq) = v;
+            }
+        const int64_t col0 = (int64_t)(t_begin + t) * PN;
+#pragma unroll
+        for (int p = 0; p < NST; ++p) {
+            const int r = p * SRW + lane / SLN, c = (lane % SLN) * 8;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * PSP + c);
+            *reinterpret_cast<u32x4*>(Cb + (int64_t)r * a.ldc + col0 + c) = v;
+        }
+        if (t + 1 < ntiles) {
+            // Tile t + 1 has landed once at most these remain: tile t + 2's DMA
+            // (if issued), this tile's stores and the previous tile's.
+            wait_vm((t + 2 < ntiles ? NB : 0) + NST + (t > 0 ? NST : 0));
+            __builtin_amdgcn_s_barrier();
+        }
+    }
+}
+
 template <class T>
 __global__ __launch_bounds__(LThreads, 1) void gemm_mfma_large(GemmArgs a) {
     extern __shared__ __attribute__((aligned(1024))) uint16_t lds[];  // [stage][A | B][row][32]
@@ -809,6 +998,35 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, Launched* L) {
         const unsigned grid = (unsigned)(((big_tiles + 7) / 8) * 8);
         L->kernel = MM_KERNEL_GEMM_LARGE;
         return hipLaunchKernel(fn, dim3(grid, gy), dim3(LThreads), args, kLargeLds, s);
+    }
+    const int64_t panel_items = (a.m / PM) * a.batch;
+    constexpr int PNW = 64;  // B tile rows of the panel kernel
+    if (vec && !a.ta && a.tb && (a.k == 32 || a.k == 64 || a.k == 128) && a.m % PM == 0 &&
+        a.n % PNW == 0 && a.beta == 0.f && a.ldc % 8 == 0 && aligned16(a.C) && a.sc % 8 == 0 &&
+        panel_items >= 128 && panel_items < (1ll << 28)) {
+        // Batched short-K NT products: A panel resident, B tiles streamed. Two
+        // blocks fit per CU (74 KiB of LDS each at k = 128); the tiles of a
+        // panel are split over up to four blocks so that at least 512 blocks
+        // run.
+        static_assert(2 * panel_lds_bytes(16, PNW) <= 160 * 1024, "two blocks per CU");
+        const int S = (int)(a.k / 8);
+        const int64_t tiles = a.n / PNW;
+        int nsplit = (int)((512 + panel_items - 1) / panel_items);
+        if (nsplit > 4) nsplit = 4;
+        if (nsplit > tiles) nsplit = (int)tiles;
+        const void* fn = nullptr;
+        if (a.dtype == 1)
+            fn = S == 4 ? (const void*)&gemm_nt_panel<TF16, 4, PNW>
+               : S == 8 ? (const void*)&gemm_nt_panel<TF16, 8, PNW> : (const void*)&gemm_nt_panel<TF16, 16, PNW>;
+        else
+            fn = S == 4 ? (const void*)&gemm_nt_panel<TBF16, 4, PNW>
+               : S == 8 ? (const void*)&gemm_nt_panel<TBF16, 8, PNW> : (const void*)&gemm_nt_panel<TBF16, 16, PNW>;
+        const int64_t items = panel_items * nsplit;
+        const unsigned grid = (unsigned)(((items + 7) / 8) * 8);
+        void* pargs[] = {const_cast<GemmArgs*>(&a), &nsplit};
+        L->kernel = MM_KERNEL_GEMM_PANEL;
+        L->variant = nsplit;
+        return hipLaunchKernel(fn, dim3(grid), dim3(PThreads), pargs, panel_lds_bytes(S, PNW), s);
     }
     const int64_t total = ((a.m + GBM - 1) / GBM) * ((a.n + GBN - 1) / GBN) * a.batch;
     int64_t per_xcd = (total + 7) / 8;

@@ -96,7 +96,8 @@ typedef enum {
     MM_KERNEL_ID_GROUPED_MFMA = 9,   /* grouped pass on MFMA (bf16 weights; f16/f32 when k % 128 == 0 and aligned) */
     MM_KERNEL_ID_GROUPED_FMA = 10,   /* grouped pass, FMA tiles (other f16/f32 layouts) */
     MM_KERNEL_GEMV_WIDE = 11,        /* skinny route, one 16 x 16 MFMA fragment per block */
-    MM_KERNEL_GEMM_F32_SMALL = 12    /* f32, k <= 128, few tiles: one wave per 16 x 16 f32 MFMA tile */
+    MM_KERNEL_GEMM_F32_SMALL = 12,   /* f32, k <= 128, few tiles: one wave per 16 x 16 f32 MFMA tile */
+    MM_KERNEL_GEMM_PANEL = 13        /* NT, k in {32, 64, 128}: 64-row A panel in LDS, B tiles streamed */
 } mm_kernel;
 
 typedef struct {

@@ -84,6 +84,8 @@ ROUTE_CASES = [
     (2, 5, 300, 256, False, True, mm.MM_ROUTE_GEMV_WIDE, mm.MM_KERNEL_GEMV_WIDE),
     (1, 300, 200, 300, False, False, mm.MM_ROUTE_GEMM, None),
     (2, 256, 256, 96, False, True, mm.MM_ROUTE_GEMM, None),
+    # batched short-K NT: the panel kernel when beta == 0, else the tiled one
+    (128, 64, 256, 64, False, True, mm.MM_ROUTE_GEMM, None),
 ]
 
 
@@ -103,6 +105,8 @@ def test_axpby_every_route(dt, shape, alpha, beta):
     if dt == wl.F32 and route == mm.MM_ROUTE_GEMM:
         small = k <= 128 and ((m + 15) // 16) * ((n + 15) // 16) <= 1024
         assert rec.kernel == (mm.MM_KERNEL_GEMM_F32_SMALL if small else mm.MM_KERNEL_GEMM_F32)
+    if dt != wl.F32 and (b, m, n, k) == (128, 64, 256, 64):
+        assert rec.kernel == (mm.MM_KERNEL_GEMM_PANEL if beta == 0 else mm.MM_KERNEL_GEMM_TILED)
 
 
 @pytest.mark.parametrize("dt", [wl.F16, wl.BF16])

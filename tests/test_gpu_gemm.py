@@ -315,6 +315,47 @@ def test_large_tile_route_full_compare(dt, seed):
     _say(f"  max err {err:.3e}")
 
 
+@pytest.mark.parametrize("dt", [wl.F16, wl.BF16])
+@pytest.mark.parametrize("k", [32, 64, 128])
+@pytest.mark.parametrize("n,nsplit", [(64, 1), (128, 2), (384, 4), (640, 4), (1536, 4)])
+def test_panel_kernel(dt, k, n, nsplit):
+    """Batched short-K NT products on the panel kernel (A panel resident in
+    LDS, B tiles of 64 rows streamed through three stages, a panel's tiles
+    split over up to four blocks): every admissible k, 1 to 6 tiles per
+    block (every pipeline depth), all outputs against the oracle; the
+    receipt names the split."""
+    b, m = 16, 512
+    _say(f"panel NT dt={wl.DTYPE_NAMES[dt]} b={b} m={m} n={n} k={k}")
+    case = wl.random_gemm_case(47 + k + n, dt, b, m, n, k, False, True)
+    rec = check_gemm(case, what=f"panel k={k} n={n}")
+    assert rec.kernel == mm.MM_KERNEL_GEMM_PANEL, rec.kernel
+    assert rec.variant == nsplit, rec.variant
+
+
+def test_panel_kernel_unsplit_long_rows():
+    """Enough panels that no split is needed: each block walks all 8 B tiles."""
+    b, m, n, k = 64, 512, 512, 128
+    _say("panel NT unsplit bf16 b=64 m=512 n=512 k=128")
+    case = wl.random_gemm_case(48, wl.BF16, b, m, n, k, False, True)
+    rec = check_gemm(case, what="panel unsplit")
+    assert rec.kernel == mm.MM_KERNEL_GEMM_PANEL and rec.variant == 1, (rec.kernel, rec.variant)
+
+
+@pytest.mark.parametrize("dt", [wl.F16, wl.BF16])
+def test_panel_kernel_padded_offsets_ramp_exact(dt):
+    """The panel kernel with padded leading dimensions, batch strides with gaps
+    and 16-byte element offsets on every operand; ramp inputs, bit for bit."""
+    b, m, n, k = 4, 2048, 384, 128
+    _say(f"panel NT padded ramp dt={wl.DTYPE_NAMES[dt]}")
+    a = wl.ramp(b * m * k, 1).reshape(b, m, k)
+    bb = wl.ramp(b * n * k, 2).reshape(b, n, k)
+    case = wl.make_gemm_case(dt, a, bb, False, True, lda=k + 8, ldb=k + 24, ldc=n + 8,
+                             off_a=8, off_b=16, off_c=8, stride_a=m * (k + 8) + 64,
+                             stride_b=n * (k + 24) + 8, stride_c=m * (n + 8) + 16)
+    rec = check_gemm(case, exact=True, what="panel padded ramp")
+    assert rec.kernel == mm.MM_KERNEL_GEMM_PANEL, rec.kernel
+
+
 @pytest.mark.parametrize("k", [128, 192, 320])
 def test_large_shape_other_k_takes_tiled_kernel(k):
     """k below 256 or not a multiple of 128: the 128 x 128 kernel, same results."""

@@ -55,7 +55,7 @@ def test_gemm_f16_batched():
     case = wl.gemm_f16_batched()
     run = GemmRun(case)
     rec = run.run()
-    assert rec.route == mm.MM_ROUTE_GEMM
+    assert rec.route == mm.MM_ROUTE_GEMM and rec.kernel == mm.MM_KERNEL_GEMM_PANEL, rec.kernel
     bits = run.c_bits()
     got, mask = run.logical_c(bits)
     run.check_untouched(bits, mask)
