@@ -68,7 +68,11 @@ def parse():
                     help="only run a plain device copy of this many bytes (counter calibration)")
     ap.add_argument("--calibrate-id", action="store_true",
                     help="only time the expert-ID direct route against map + grouped over a "
-                         "range of token counts (route crossover) and print one JSON line")
+                         "range of token counts and hot-expert set sizes (route crossover) and "
+                         "print one JSON line")
+    ap.add_argument("--calibrate-gemm", action="store_true",
+                    help="only time the skinny, tiled-GEMM and GEMV routes of x[m,k] . W[n,k]^T "
+                         "for m = 2..64 at three (n, k) (route crossover) and print one JSON line")
     return ap.parse_args()
 
 
@@ -160,58 +164,107 @@ def sample_clock(torch, dev, stream, step, n_rot, seconds=1.5):
 
 def calibrate_id(torch, mm, wl, dev, stream, args):
     """Direct route vs map + grouped route for expert-ID layers of a few shapes,
-    over token counts m: bf16 weights, distinct ids per token (a prefix of a
-    fresh permutation of the experts), shared activations. Weights rotate
-    through enough stacks to defeat the caches, as in the main benchmark."""
+    over token counts m: distinct ids per token (a prefix of a fresh
+    permutation of a hot set of H experts: H = E spreads the routing over
+    every expert, a small H repeats the same experts across tokens), shared
+    activations. Weights rotate through enough stacks to defeat the caches,
+    as in the main benchmark."""
     timer = Timer(torch, stream, True)
-    # (experts, top_k, n, k, weight dtype)
-    layers = [(64, 8, 1408, 2048, wl.BF16), (16, 4, 2048, 2048, wl.BF16),
-              (64, 8, 1408, 2048, wl.F16), (16, 4, 2048, 2048, wl.F32)]
+    # (experts, top_k, n, k, weight dtype, hot-set sizes)
+    layers = [(64, 8, 1408, 2048, wl.BF16, (64, 32, 16, 8)), (16, 4, 2048, 2048, wl.BF16, (16, 8)),
+              (64, 8, 1408, 2048, wl.F16, (64, 16)), (16, 4, 2048, 2048, wl.F32, (16, 8))]
     table = []
-    for (E, top_k, n, k, wdt) in layers:
+    for (E, top_k, n, k, wdt, hots) in layers:
         rng = np.random.default_rng(11)
         w = to_dev_bits(torch, dev, wl.to_storage(0.02 * rng.standard_normal(E * n * k), wdt))
         wbytes = E * n * k * wl.ELT[wdt]
         n_rot = max(2, math.ceil(ROTATE_BYTES / wbytes))
         Ws = [w] + [w.clone() for _ in range(n_rot - 1)]
         wb = [mm.buf(t) for t in Ws]
-        for m in [1, 2, 4, 8, 16, 32, 64, 128, 256, 512]:
-            ids_np = wl.distinct_ids(np.random.default_rng(m), m, top_k, E)
-            x = torch.from_numpy(rng.standard_normal((m, k)).astype(np.float32)).to(dev)
-            ids = torch.from_numpy(ids_np.reshape(-1).view(np.int32)).to(dev)
-            out = torch.empty(m * top_k * n, dtype=torch.float32, device=dev)
-            cnt = torch.empty(E, dtype=torch.int32, device=dev)
-            rr = torch.empty(E * m, dtype=torch.int32, device=dev)
-            es = wl.ELT[wdt]
-            pd = mm.id_params(m, n, k, top_k, E, n * k * es, 0, 0, 0)
-            pg = mm.id_params(m, n, k, top_k, E, n * k * es, 0, 0, 1)
-            xb, ib, ob, cb, rb = mm.buf(x), mm.buf(ids), mm.buf(out), mm.buf(cnt), mm.buf(rr)
+        for hot in hots:
+            for m in [1, 2, 4, 8, 16, 32, 64, 128, 256, 512]:
+                prng = np.random.default_rng(1000 * hot + m)
+                hot_set = prng.permutation(E)[:hot]
+                ids_np = hot_set[wl.distinct_ids(prng, m, top_k, hot)].astype(np.uint32)
+                x = torch.from_numpy(rng.standard_normal((m, k)).astype(np.float32)).to(dev)
+                ids = torch.from_numpy(ids_np.reshape(-1).view(np.int32)).to(dev)
+                out = torch.empty(m * top_k * n, dtype=torch.float32, device=dev)
+                cnt = torch.empty(E, dtype=torch.int32, device=dev)
+                rr = torch.empty(E * m, dtype=torch.int32, device=dev)
+                es = wl.ELT[wdt]
+                pd = mm.id_params(m, n, k, top_k, E, n * k * es, 0, 0, 0)
+                pg = mm.id_params(m, n, k, top_k, E, n * k * es, 0, 0, 1)
+                xb, ib, ob, cb, rb = mm.buf(x), mm.buf(ids), mm.buf(out), mm.buf(cnt), mm.buf(rr)
 
-            def direct(i):
-                mm.mm_id_direct(pd, wdt, wb[i], xb, ib, ob, stream=stream)
+                def direct(i):
+                    mm.mm_id_direct(pd, wdt, wb[i], xb, ib, ob, stream=stream)
 
-            def grouped(i):
-                mm.mm_id(pg, wdt, wb[i], xb, ib, ob, cb, rb, stream=stream)
+                def grouped(i):
+                    mm.mm_id(pg, wdt, wb[i], xb, ib, ob, cb, rb, stream=stream)
 
-            steps = max(n_rot, 2 * n_rot * max(1, 64 // m))
-            td, _ = timer.time(direct, n_rot, steps, 3)
-            tg, _ = timer.time(grouped, n_rot, steps, 3)
-            used = len(set(int(v) for v in ids_np.reshape(-1)))
-            hint = mm.mm_id_route_hint(wdt, pd)
-            row = {"experts": E, "top_k": top_k, "n": n, "k": k, "m": m,
-                   "weights": wl.DTYPE_NAMES[wdt], "hint": "grouped" if hint else "direct",
-                   "rows_per_expert": m * top_k / E, "experts_used": used,
-                   "direct_us": td * 1e3, "grouped_us": tg * 1e3,
-                   "faster": "direct" if td <= tg else "grouped"}
-            table.append(row)
-            log(f"{wl.DTYPE_NAMES[wdt]} E={E:3d} top_k={top_k} n={n} k={k} m={m:4d} "
-                f"rows/expert={m * top_k / E:7.3f} "
-                f"used={used:3d}  direct {td * 1e3:8.2f} us  grouped {tg * 1e3:8.2f} us  "
-                f"-> {row['faster']} (hint {row['hint']})")
-            del x, ids, out, cnt, rr
+                steps = max(n_rot, 2 * n_rot * max(1, 64 // m))
+                td, _ = timer.time(direct, n_rot, steps, 3)
+                tg, _ = timer.time(grouped, n_rot, steps, 3)
+                used = len(set(int(v) for v in ids_np.reshape(-1)))
+                hint = mm.mm_id_route_hint(wdt, pd)
+                row = {"experts": E, "top_k": top_k, "n": n, "k": k, "m": m, "hot": hot,
+                       "weights": wl.DTYPE_NAMES[wdt], "hint": "grouped" if hint else "direct",
+                       "rows_per_expert": m * top_k / E, "experts_used": used,
+                       "rows_per_used_expert": m * top_k / used,
+                       "direct_us": td * 1e3, "grouped_us": tg * 1e3,
+                       "faster": "direct" if td <= tg else "grouped"}
+                table.append(row)
+                log(f"{wl.DTYPE_NAMES[wdt]} E={E:3d} top_k={top_k} n={n} k={k} hot={hot:3d} m={m:4d} "
+                    f"used={used:3d} rows/used={m * top_k / used:7.3f}  direct {td * 1e3:8.2f} us  "
+                    f"grouped {tg * 1e3:8.2f} us  -> {row['faster']} (hint {row['hint']})")
+                del x, ids, out, cnt, rr
         del Ws, wb, w
         torch.cuda.empty_cache()
     print(json.dumps({"calibration": "matmul_id direct vs map+grouped", "rows": table}))
+
+
+def calibrate_gemm(torch, mm, wl, dev, stream, args):
+    """Routes of the skinny product x[m,k] . W[n,k]^T (f16, both stored with
+    rows along k): the skinny route (m <= 64), the tiled GEMM route, and the
+    GEMV route as m GEMVs in one batched launch that shares W, for m = 2..64
+    at three (n, k). W rotates through copies to defeat the caches."""
+    timer = Timer(torch, stream, True)
+    table = []
+    for (n, k) in [(11008, 4096), (4096, 4096), (4096, 11008)]:
+        rng = np.random.default_rng(21)
+        w = to_dev_bits(torch, dev, wl.to_storage(0.02 * rng.standard_normal(n * k), wl.F16))
+        n_rot = max(2, math.ceil(ROTATE_BYTES / (n * k * 2)))
+        Ws = [w] + [w.clone() for _ in range(n_rot - 1)]
+        wb = [mm.buf(t) for t in Ws]
+        for m in [2, 3, 4, 6, 8, 12, 16, 20, 24, 28, 32, 40, 48, 56, 64]:
+            x = to_dev_bits(torch, dev, wl.to_storage(rng.standard_normal(m * k), wl.F16))
+            c = torch.empty(m * n, dtype=torch.float16, device=dev)
+            xb, cbuf = mm.buf(x), mm.buf(c)
+            d = mm.gemm_desc(wl.F16, m, n, k, trans_b=True)
+            dv = mm.gemm_desc(wl.F16, 1, n, k, batch=m, trans_b=True, stride_a=k, stride_b=0,
+                              stride_c=n)
+            routes = {"gemm": (d, mm.MM_ROUTE_GEMM), "gemv": (dv, mm.MM_ROUTE_GEMV)}
+            if m <= 64:
+                routes["skinny"] = (d, mm.MM_ROUTE_GEMV_WIDE)
+            times = {}
+            for name, (desc, route) in routes.items():
+                def step(i, desc=desc, route=route):
+                    mm.mm_gemm_route(desc, route, xb, wb[i], cbuf, stream=stream)
+                t, _ = timer.time(step, n_rot, 4 * n_rot, 3)
+                times[name] = t * 1e3
+            picked = mm.mm_gemm(d, xb, wb[0], cbuf, stream=stream).route
+            picked = {mm.MM_ROUTE_GEMV_WIDE: "skinny", mm.MM_ROUTE_GEMM: "gemm",
+                      mm.MM_ROUTE_GEMV: "gemv"}[picked]
+            fastest = min(times, key=times.get)
+            row = {"n": n, "k": k, "m": m, "us": times, "fastest": fastest, "dispatch": picked,
+                   "weight_gbs": {r: n * k * 2 / (t * 1e3) for r, t in times.items()}}
+            table.append(row)
+            log(f"n={n:5d} k={k:5d} m={m:2d}  " + "  ".join(f"{r} {t:7.2f} us" for r, t in times.items())
+                + f"  -> fastest {fastest}, dispatch picks {picked}")
+            del x, c
+        del Ws, wb, w
+        torch.cuda.empty_cache()
+    print(json.dumps({"calibration": "skinny vs tiled GEMM vs GEMV routes", "rows": table}))
 
 
 def to_dev_bits(torch, dev, bits):
@@ -373,6 +426,9 @@ def main():
 
     if args.calibrate_id:
         calibrate_id(torch, mm, wl, dev, stream, args)
+        return
+    if args.calibrate_gemm:
+        calibrate_gemm(torch, mm, wl, dev, stream, args)
         return
 
     def to_dev(bits):

@@ -39,7 +39,7 @@ STATUS_NAMES = {
 
 # Every symbol include/mm.h declares.
 EXPORTS = [
-    "mm_gemm", "mm_gemm_ex", "mm_gemv", "mm_id_query", "mm_id_route_hint", "mm_id_direct", "mm_id_map",
+    "mm_gemm", "mm_gemm_ex", "mm_gemm_route", "mm_gemv", "mm_id_query", "mm_id_route_hint", "mm_id_direct", "mm_id_map",
     "mm_id_grouped",
     "mm_id", "mm_capabilities", "mm_status_string", "mm_last_error",
     "mm_test_inject_resolve_failure", "mm_test_launch_count", "mm_id_prefill_noalloc",
@@ -118,6 +118,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.mm_gemm_ex.argtypes = [P(GemmDesc), ctypes.c_float, ctypes.c_float, Buf, Buf, Buf, vp,
                                P(Receipt)]
     lib.mm_gemm_ex.restype = st
+    lib.mm_gemm_route.argtypes = [P(GemmDesc), ctypes.c_uint32, ctypes.c_float, ctypes.c_float,
+                                  Buf, Buf, Buf, vp, P(Receipt)]
+    lib.mm_gemm_route.restype = st
     lib.mm_gemv.argtypes = [P(GemmDesc), Buf, Buf, Buf, vp, P(Receipt)]
     lib.mm_gemv.restype = st
     lib.mm_id_query.argtypes = [ctypes.c_int, P(IdParams), P(IdCapability)]
@@ -198,6 +201,15 @@ def mm_gemm_ex(desc: GemmDesc, alpha: float, beta: float, a: Buf, b: Buf, c: Buf
     r = Receipt()
     _raise(load().mm_gemm_ex(ctypes.byref(desc), ctypes.c_float(alpha), ctypes.c_float(beta),
                              a, b, c, _stream(stream), ctypes.byref(r)))
+    return r
+
+
+def mm_gemm_route(desc: GemmDesc, route: int, a: Buf, b: Buf, c: Buf, alpha: float = 1.0,
+                  beta: float = 0.0, stream=None) -> Receipt:
+    """The product on the route the caller names (GEMV, skinny or tiled GEMM)."""
+    r = Receipt()
+    _raise(load().mm_gemm_route(ctypes.byref(desc), route, ctypes.c_float(alpha),
+                                ctypes.c_float(beta), a, b, c, _stream(stream), ctypes.byref(r)))
     return r
 
 

@@ -256,14 +256,14 @@ mm_status run_gemv(const GemmPlan& p, hipStream_t s, mm_receipt* r) {
     return ok();
 }
 
-// tract-metal `gemv_wide_config`: a skinny product (2..16 rows on one side)
+// tract-metal `gemv_wide_config`: a skinny product (2..64 rows on one side)
 // against a matrix with rows along k streams that matrix once for all rows.
 // Both operands must be stored with rows along k (trans_a = 0, trans_b = 1)
 // and allow 16-byte chunks that never straddle a row end.
 bool skinny_args(const GemmPlan& p, mmk::SkinnyArgs* g) {
     if (p.ta || !p.tb) return false;
-    const bool x_is_a = p.m >= 2 && p.m <= 16 && p.n >= 2;
-    const bool x_is_b = !x_is_a && p.n >= 2 && p.n <= 16 && p.m >= 2;
+    const bool x_is_a = p.m >= 2 && p.m <= 64 && p.n >= 2;
+    const bool x_is_b = !x_is_a && p.n >= 2 && p.n <= 64 && p.m >= 2;
     if (!x_is_a && !x_is_b) return false;
     const int64_t ch = 16 / (int64_t)elt_size(p.dt);
     const auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
@@ -482,6 +482,34 @@ mm_status dispatch_gemm(const GemmPlan& p, void* stream, mm_receipt* receipt) {
     return run_gemm(p, s, receipt);
 }
 
+// Route suggestion. Crossover between the routes, in routed rows per expert
+// (m * top_k / n_experts), measured on MI355X over token counts 1..512 for
+// 64-expert 1408 x 2048 and 16-expert 2048 x 2048 layers with bf16, f16 and
+// f32 weights: the grouped route wins from 2 rows per expert on, where the
+// direct route would read each expert's weights about twice. Routing
+// concentrated on a hot subset of 8 to 32 experts moves the crossover by at
+// most one doubling of the token count, because the grouped pass sizes its
+// tiles for min(n_experts, m * top_k) experts. Layouts that leave the
+// grouped pass on FMA tiles (f16/f32 weights with k % 128 != 0 or unaligned
+// operands) need about 16 rows per expert.
+mm_status route_hint(mm_dtype weight_dtype, const mm_id_params* params, uint32_t* route) {
+    if (!params || !route) return fail(MM_ERR_INVALID_ARGUMENT, "matmul_id route hint: null argument");
+    mm_id_params q = *params;
+    q.route = 0;
+    mm_id_capability tmp;
+    mm_status st = id_query(weight_dtype, &q, &tmp);
+    if (st != MM_OK) return st;
+    const uint64_t rows = (uint64_t)q.m * q.top_k;
+    uint32_t r = 0;
+    if (q.multiplicity == 0 && q.n_experts <= MM_ID_GROUPED_MAX_EXPERTS) {
+        const bool fma_tiles = weight_dtype != MM_BF16 && q.k % 128 != 0;
+        const uint64_t per_expert = fma_tiles ? 16 : 2;
+        if (rows >= per_expert * q.n_experts) r = 1;
+    }
+    *route = r;
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -504,6 +532,35 @@ mm_status mm_gemm_ex(const mm_gemm_desc* desc, float alpha, float beta, mm_buf a
     return dispatch_gemm(p, stream, receipt);
 }
 
+mm_status mm_gemm_route(const mm_gemm_desc* desc, uint32_t route, float alpha, float beta,
+                        mm_buf a, mm_buf b, mm_buf c, void* stream, mm_receipt* receipt) {
+    GemmPlan p;
+    mm_status st = plan_gemm(desc, a, b, c, &p);
+    if (st != MM_OK) return st;
+    p.alpha = alpha;
+    p.beta = beta;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    switch (route) {
+        case MM_ROUTE_GEMV:
+            if (p.m != 1 && p.n != 1)
+                return fail(MM_ERR_UNSUPPORTED, "gemm route: GEMV needs m == 1 or n == 1 (got m = %lld, n = %lld)",
+                            (long long)p.m, (long long)p.n);
+            return run_gemv(p, s, receipt);
+        case MM_ROUTE_GEMV_WIDE: {
+            mmk::SkinnyArgs g;
+            if (!skinny_args(p, &g))
+                return fail(MM_ERR_UNSUPPORTED,
+                            "gemm route: the skinny route needs trans_a = 0, trans_b = 1, one side of "
+                            "2..64 rows and the 16-byte layout");
+            return run_skinny(g, p.dt, s, receipt);
+        }
+        case MM_ROUTE_GEMM:
+            return run_gemm(p, s, receipt);
+        default:
+            return fail(MM_ERR_INVALID_ARGUMENT, "gemm route: %u is not a GEMM route", route);
+    }
+}
+
 mm_status mm_gemv(const mm_gemm_desc* desc, mm_buf a, mm_buf b, mm_buf c, void* stream,
                   mm_receipt* receipt) {
     GemmPlan p;
@@ -521,28 +578,8 @@ mm_status mm_id_query(mm_dtype weight_dtype, const mm_id_params* params, mm_id_c
     return st == MM_OK ? ok() : st;
 }
 
-// Crossover between the routes, in routed rows per expert (m * top_k /
-// n_experts), measured on MI355X over token counts 1..512 for 64-expert
-// 1408 x 2048 and 16-expert 2048 x 2048 layers with bf16, f16 and f32
-// weights: the grouped route wins from 2 rows per expert on, where the
-// direct route would read each expert's weights about twice. Layouts that
-// leave the grouped pass on FMA tiles (f16/f32 weights with k % 128 != 0 or
-// unaligned operands) need about 16 rows per expert.
 mm_status mm_id_route_hint(mm_dtype weight_dtype, const mm_id_params* params, uint32_t* route) {
-    if (!params || !route) return fail(MM_ERR_INVALID_ARGUMENT, "matmul_id route hint: null argument");
-    mm_id_params q = *params;
-    q.route = 0;
-    mm_id_capability tmp;
-    mm_status st = id_query(weight_dtype, &q, &tmp);
-    if (st != MM_OK) return st;
-    uint32_t r = 0;
-    if (q.multiplicity == 0 && q.n_experts <= MM_ID_GROUPED_MAX_EXPERTS) {
-        const bool fma_tiles = weight_dtype != MM_BF16 && q.k % 128 != 0;
-        const uint64_t per_expert = fma_tiles ? 16 : 2;
-        if ((uint64_t)q.m * q.top_k >= per_expert * q.n_experts) r = 1;
-    }
-    *route = r;
-    return ok();
+    return route_hint(weight_dtype, params, route);
 }
 
 mm_status mm_id_direct(const mm_id_params* params, mm_dtype weight_dtype, mm_buf weights,

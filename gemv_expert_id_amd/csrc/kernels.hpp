@@ -40,7 +40,7 @@ struct GemvArgs {
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t s, Launched* L);
 
 // Skinny product: out[b][x * out_sx + w * out_sw] = sum_p W[b](w, p) * X[b](x, p)
-// for w < nw, x < nx (nx <= 16); W(w, p) = W[w * ldw + p], X(x, p) = X[x * ldx + p].
+// for w < nw, x < nx (nx <= 64); W(w, p) = W[w * ldw + p], X(x, p) = X[x * ldx + p].
 struct SkinnyArgs {
     const void* W;
     const void* X;

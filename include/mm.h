@@ -78,7 +78,7 @@ typedef enum {
     MM_ROUTE_ID_MAP = 3,
     MM_ROUTE_ID_GROUPED = 4,
     MM_ROUTE_ID_PREFILL = 5, /* map + grouped in one call */
-    MM_ROUTE_GEMV_WIDE = 6   /* skinny product: 2..16 rows on one side */
+    MM_ROUTE_GEMV_WIDE = 6   /* skinny product: 2..64 rows on one side */
 } mm_route;
 
 /* Kernel family of a launch (reported in receipts; the choice depends on
@@ -95,7 +95,7 @@ typedef enum {
     MM_KERNEL_ID_MAP = 8,            /* map pass */
     MM_KERNEL_ID_GROUPED_MFMA = 9,   /* grouped pass on MFMA (bf16 weights; f16/f32 when k % 128 == 0 and aligned) */
     MM_KERNEL_ID_GROUPED_FMA = 10,   /* grouped pass, FMA tiles (other f16/f32 layouts) */
-    MM_KERNEL_GEMV_WIDE = 11,        /* skinny route, one 16 x 16 MFMA fragment per block */
+    MM_KERNEL_GEMV_WIDE = 11,        /* skinny route, one to four 16 x 16 MFMA fragments per block */
     MM_KERNEL_GEMM_F32_SMALL = 12,   /* f32, k <= 128, few tiles: one wave per 16 x 16 f32 MFMA tile */
     MM_KERNEL_GEMM_PANEL = 13        /* NT, k in {32, 64, 128}: 64-row A panel in LDS, B tiles streamed */
 } mm_kernel;
@@ -114,8 +114,12 @@ typedef struct {
                                  when activations come from L2, 1 when the
                                  block stages its activation row in LDS, 2
                                  when it also reuses a repeated expert's
-                                 weights across slots (slotted layout); 0 for
-                                 every other family */
+                                 weights across slots (slotted layout); for
+                                 MM_KERNEL_GEMV_WIDE the activation fragments
+                                 per block (one per 16 rows, up to 4);
+                                 for MM_KERNEL_GEMM_PANEL the number of blocks
+                                 a 64-row panel's B tiles are split over; 0
+                                 for every other family */
 } mm_receipt;
 
 /* ------------------------------------------------------------------------ */
@@ -158,7 +162,7 @@ typedef struct {
  * Dispatch (tract-metal `dispatch_eval`, with `gemv_wide_config` deciding the
  * skinny case first):
  *   - skinny route (MM_ROUTE_GEMV_WIDE) when trans_a == 0, trans_b == 1, one
- *     of m, n is in 2..16 and the other is >= 2, and the 16-byte layout holds:
+ *     of m, n is in 2..64 and the other is >= 2, and the 16-byte layout holds:
  *     k, lda, ldb, stride_a and stride_b multiples of 16 / element size and
  *     16-byte aligned A and B (after their offsets);
  *   - the GEMV route when m == 1 or n == 1 (the matrix operand is B when
@@ -183,6 +187,20 @@ mm_status mm_gemm(const mm_gemm_desc *desc, mm_buf a, mm_buf b, mm_buf c, void *
  */
 mm_status mm_gemm_ex(const mm_gemm_desc *desc, float alpha, float beta, mm_buf a, mm_buf b,
                      mm_buf c, void *stream, mm_receipt *receipt);
+
+/*
+ * The same product on a route the caller names (route = MM_ROUTE_GEMV,
+ * MM_ROUTE_GEMV_WIDE or MM_ROUTE_GEMM), with the mm_gemm_ex epilogue. For
+ * callers that choose or calibrate routes themselves (mlx-native
+ * dense_matmul_id.rs, `DenseMatmulIdParams`: route selection belongs to the
+ * caller; rlx-metal mps_blas.rs module doc: the route crossover is measured,
+ * not assumed). Every route computes the same values. Fails with
+ * UNSUPPORTED when the named route cannot take the problem (GEMV: m != 1 and
+ * n != 1; skinny: the conditions of mm_gemm's skinny case), else as
+ * mm_gemm_ex; INVALID_ARGUMENT for any other route value.
+ */
+mm_status mm_gemm_route(const mm_gemm_desc *desc, uint32_t route, float alpha, float beta,
+                        mm_buf a, mm_buf b, mm_buf c, void *stream, mm_receipt *receipt);
 
 /* The GEMV route only; INVALID_ARGUMENT unless m == 1 or n == 1
  * (tract-metal `dispatch_metal_mlx_gemv`). Same validation as mm_gemm. */

@@ -126,13 +126,13 @@ class GemmRun:
 
 def expected_gemm_route(case: wl.GemmCase) -> int:
     """The route mm_gemm documents for this case (mm.h, dispatch): skinny when
-    A and B keep rows along k, one side has 2..16 rows, the other >= 2, and
+    A and B keep rows along k, one side has 2..64 rows, the other >= 2, and
     the 16-byte layout holds (device buffers are 256-byte aligned, so only the
     offsets matter); GEMV when m == 1 or n == 1; GEMM otherwise."""
     c = case
     ch = 16 // wl.ELT[c.dtype]
     skinny = (not c.trans_a and c.trans_b
-              and ((2 <= c.m <= 16 and c.n >= 2) or (2 <= c.n <= 16 and c.m >= 2))
+              and ((2 <= c.m <= 64 and c.n >= 2) or (2 <= c.n <= 64 and c.m >= 2))
               and c.k % ch == 0 and c.lda % ch == 0 and c.ldb % ch == 0
               and c.stride_a % ch == 0 and c.stride_b % ch == 0
               and c.off_a % 16 == 0 and c.off_b % 16 == 0)

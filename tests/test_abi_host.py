@@ -265,6 +265,54 @@ def test_noalloc_prefill_rejects_before_enqueue():
     lib.mm_test_inject_resolve_failure(None)
 
 
+def test_gemm_route_refusals():
+    """mm_gemm_route refuses a route that cannot take the problem, before
+    anything is enqueued: GEMV with m, n > 1; skinny with 65 rows or more on
+    both sides or a transposed A; an unknown route value."""
+    d = mm.gemm_desc(mm.MM_F16, 8, 300, 256, trans_b=True)
+    bufs = _gemm_bufs(mm.MM_F16, 8, 300, 256)
+    _fails(2, mm.mm_gemm_route, d, mm.MM_ROUTE_GEMV, *bufs)
+    d65 = mm.gemm_desc(mm.MM_F16, 65, 300, 256, trans_b=True)
+    _fails(2, mm.mm_gemm_route, d65, mm.MM_ROUTE_GEMV_WIDE, *_gemm_bufs(mm.MM_F16, 65, 300, 256))
+    dta = mm.gemm_desc(mm.MM_F16, 8, 300, 256, trans_a=True, trans_b=True)
+    _fails(2, mm.mm_gemm_route, dta, mm.MM_ROUTE_GEMV_WIDE, *bufs)
+    _fails(1, mm.mm_gemm_route, d, mm.MM_ROUTE_ID_DIRECT, *bufs)
+    _fails(1, mm.mm_gemm_route, d, 99, *bufs)
+
+
+@pytest.mark.parametrize("dt", [mm.MM_F32, mm.MM_F16, mm.MM_BF16])
+def test_dispatch_crossover_skinny_vs_tiled(dt):
+    """The measured route crossover of mm_gemm for x[m,k] . W[n,k]^T: the
+    skinny route up to 64 rows on either side (faster than the tiled GEMM at
+    every calibrated m <= 64 and (n, k)), the tiled GEMM from 65 rows, the
+    GEMV route at one row. The resolve-failure hook names the family the
+    dispatch chose, before anything is enqueued."""
+    lib = mm.load()
+    n, k = 4096, 4096
+
+    def family(m, nn):
+        d = mm.gemm_desc(dt, m, nn, k, trans_b=True)
+        for fam in (b"gemv_wide", b"gemm", b"gemv"):
+            lib.mm_test_inject_resolve_failure(fam)
+            before = lib.mm_test_launch_count()
+            try:
+                mm.mm_gemm(d, *_gemm_bufs(dt, m, nn, k))
+            except mm.MmError as e:
+                if e.status == 2 and "injected" in str(e):
+                    lib.mm_test_inject_resolve_failure(None)
+                    assert lib.mm_test_launch_count() == before
+                    return fam.decode()
+            lib.mm_test_inject_resolve_failure(None)
+        raise AssertionError("no family resolved")
+
+    for m in (2, 16, 17, 32, 33, 48, 64):
+        assert family(m, n) == "gemv_wide", m
+        assert family(n, m) == "gemv_wide", ("mirrored", m)
+    for m in (65, 128):
+        assert family(m, n) == "gemm", m
+    assert family(1, n) == "gemv"
+
+
 def test_capabilities_without_gpu():
     import torch
     if torch.cuda.is_available():

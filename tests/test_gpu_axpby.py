@@ -85,7 +85,7 @@ ROUTE_CASES = [
     (1, 300, 200, 300, False, False, mm.MM_ROUTE_GEMM, None),
     (2, 256, 256, 96, False, True, mm.MM_ROUTE_GEMM, None),
     # batched short-K NT: the panel kernel when beta == 0, else the tiled one
-    (128, 64, 256, 64, False, True, mm.MM_ROUTE_GEMM, None),
+    (64, 128, 256, 64, False, True, mm.MM_ROUTE_GEMM, None),
 ]
 
 
@@ -105,7 +105,7 @@ def test_axpby_every_route(dt, shape, alpha, beta):
     if dt == wl.F32 and route == mm.MM_ROUTE_GEMM:
         small = k <= 128 and ((m + 15) // 16) * ((n + 15) // 16) <= 1024
         assert rec.kernel == (mm.MM_KERNEL_GEMM_F32_SMALL if small else mm.MM_KERNEL_GEMM_F32)
-    if dt != wl.F32 and (b, m, n, k) == (128, 64, 256, 64):
+    if dt != wl.F32 and (b, m, n, k) == (64, 128, 256, 64):
         assert rec.kernel == (mm.MM_KERNEL_GEMM_PANEL if beta == 0 else mm.MM_KERNEL_GEMM_TILED)
 
 

@@ -317,7 +317,7 @@ def test_large_tile_route_full_compare(dt, seed):
 
 @pytest.mark.parametrize("dt", [wl.F16, wl.BF16])
 @pytest.mark.parametrize("k", [32, 64, 128])
-@pytest.mark.parametrize("n,nsplit", [(64, 1), (128, 2), (384, 4), (640, 4), (1536, 4)])
+@pytest.mark.parametrize("n,nsplit", [(128, 2), (192, 3), (384, 4), (640, 4), (1536, 4)])
 def test_panel_kernel(dt, k, n, nsplit):
     """Batched short-K NT products on the panel kernel (A panel resident in
     LDS, B tiles of 64 rows streamed through three stages, a panel's tiles
@@ -362,3 +362,28 @@ def test_large_shape_other_k_takes_tiled_kernel(k):
     _say(f"NT f16 m=4096 n=8192 k={k} (tiled kernel)")
     case = wl.random_gemm_case(43, wl.F16, 1, 4096, 8192, k, False, True)
     _sampled_check(case, 2048, 6, kernel=mm.MM_KERNEL_GEMM_TILED)
+
+
+@pytest.mark.parametrize("dt", DTYPES)
+def test_forced_routes_agree_bit_exact(dt):
+    """mm_gemm_route: the skinny, tiled-GEMM and (m GEMVs sharing W) GEMV routes
+    of one 8-row product give the rounded oracle's bits on ramp inputs."""
+    import torch
+    from gpu_util import GemmRun
+    import oracle
+    m, n, k = 8, 300, 256
+    _say(f"forced routes dt={wl.DTYPE_NAMES[dt]} m={m} n={n} k={k}")
+    a = wl.ramp(m * k, 1).reshape(1, m, k)
+    bb = wl.ramp(n * k, 2).reshape(1, n, k)
+    case = wl.make_gemm_case(dt, a, bb, False, True)
+    ref_bits = oracle.round_to(dt, GemmRun(case).oracle_full()).reshape(m, n)
+    for route in (mm.MM_ROUTE_GEMV_WIDE, mm.MM_ROUTE_GEMM, mm.MM_ROUTE_GEMV):
+        run = GemmRun(case, c_extra=0)
+        desc = run.desc
+        if route == mm.MM_ROUTE_GEMV:  # m GEMVs in one launch, W shared
+            desc = mm.gemm_desc(dt, 1, n, k, batch=m, trans_b=True, stride_a=k, stride_b=0,
+                                stride_c=n)
+        rec = mm.mm_gemm_route(desc, route, *run.bufs, stream=torch.cuda.current_stream())
+        assert rec.route == route
+        got = run.c_bits()[: m * n].reshape(m, n)
+        np.testing.assert_array_equal(got, ref_bits, err_msg=f"route {route}")

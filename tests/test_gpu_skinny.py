@@ -5,7 +5,8 @@ Shapes follow the pages' skinny tests (tract-metal mlx_gemm/mod.rs,
 `gemv_wide_tests`: m = 2..15 at n = 128, k = 256 in f16, m in {2, 5, 8, 15}
 in f32, and the tail-row cases) on the same ramp inputs, which keep every
 partial sum exact so the comparison is bit for bit; random operands add
-m = 16, the mirrored case (n small, m large), contraction tails, batches,
+m = 16 to 64 (one activation fragment per 16 rows), the mirrored case (n
+small, m large), contraction tails, batches,
 broadcast operands, padded leading dimensions and byte offsets. Layouts the
 route does not take (misaligned offsets, k not a whole number of 16-byte
 chunks) must fall through to the other routes and stay correct.
@@ -82,10 +83,23 @@ def test_page_skinny_tails_ramp_exact(dt, m, n, k):
 
 
 @pytest.mark.parametrize("dt", DTYPES)
+@pytest.mark.parametrize("m", [17, 24, 32, 33, 45, 48, 49, 63, 64])
+def test_skinny_fragments_ramp_exact(dt, m):
+    """17 to 64 rows: one activation fragment per 16 rows (receipt variant
+    2, 3 or 4), ragged n and k tails, bit for bit on ramp inputs."""
+    _say(f"skinny fragments {wl.DTYPE_NAMES[dt]} m={m}")
+    rec = _run(_ramp_case(dt, m, 130, 264), True, f"{m}x130x264")
+    assert rec.route == mm.MM_ROUTE_GEMV_WIDE and rec.variant == (m + 15) // 16, (rec.route, rec.variant)
+
+
+@pytest.mark.parametrize("dt", DTYPES)
 @pytest.mark.parametrize("m,n,k", [(16, 1000, 1024), (5, 4099, 264), (2, 64, 4096),
-                                   (300, 5, 256), (4097, 16, 136), (12, 12, 40)])
+                                   (300, 5, 256), (4097, 16, 136), (12, 12, 40),
+                                   (32, 1000, 1024), (20, 4099, 264), (300, 29, 256),
+                                   (18, 24, 40), (64, 1000, 1024), (40, 4099, 264),
+                                   (300, 57, 256)])
 def test_skinny_random(dt, m, n, k):
-    """Random operands, both roles: few rows in A (m <= 16) or in B (n <= 16)."""
+    """Random operands, both roles: few rows in A (m <= 64) or in B (n <= 64)."""
     _say(f"skinny random {wl.DTYPE_NAMES[dt]} m={m} n={n} k={k}")
     case = wl.random_gemm_case(31, dt, 1, m, n, k, False, True)
     rec = _run(case, False, f"{m}x{n}x{k}")
