@@ -70,6 +70,10 @@ def parse():
                     help="only time the expert-ID direct route against map + grouped over a "
                          "range of token counts and hot-expert set sizes (route crossover) and "
                          "print one JSON line")
+    ap.add_argument("--decode-sweep", action="store_true",
+                    help="only time the expert-ID direct route at one token against the number "
+                         "of distinct experts it reads (fixed cost and marginal bandwidth) and the "
+                         "smallest call (a one-element GEMV), and print one JSON line")
     ap.add_argument("--calibrate-gemm", action="store_true",
                     help="only time the skinny, tiled-GEMM and GEMV routes of x[m,k] . W[n,k]^T "
                          "for m = 2..64 at three (n, k) (route crossover) and print one JSON line")
@@ -221,6 +225,59 @@ def calibrate_id(torch, mm, wl, dev, stream, args):
         del Ws, wb, w
         torch.cuda.empty_cache()
     print(json.dumps({"calibration": "matmul_id direct vs map+grouped", "rows": table}))
+
+
+def decode_sweep(torch, mm, wl, dev, stream, args):
+    """Per-call cost of the direct expert-ID route at one token against the
+    bytes it streams: u distinct experts (top_k = u) of a 64-expert bf16
+    [1408, 2048] stack, u = 1..16, the calls cycling through three copies of
+    the stack so that an expert is read again only after >= 1 GiB. A least-squares line through (bytes, time) gives the
+    fixed cost per call and the marginal bandwidth. The smallest call
+    (a 1 x 1 x 1 f32 GEMV through mm_gemm) shows the per-launch floor of a
+    graph-replayed call."""
+    timer = Timer(torch, stream, True)
+    E, n, k = 64, 1408, 2048
+    rng = np.random.default_rng(4)
+    w = to_dev_bits(torch, dev, wl.to_storage(0.02 * rng.standard_normal(E * n * k), wl.BF16))
+    Ws = [w, w.clone(), w.clone()]  # 3 x 369 MB
+    wb = [mm.buf(t) for t in Ws]
+    x = torch.from_numpy(rng.standard_normal(k).astype(np.float32)).to(dev)
+    rows = []
+    for u in [1, 2, 4, 7, 8, 12, 16]:
+        # Call c reads stack c % 3, experts u * (c // 3) .. + u - 1 (mod 64): a
+        # cycle touches every expert of the three stacks before it repeats one.
+        cycle = 3 * (E // math.gcd(u, E))
+        id_bufs = []
+        for c in range(cycle):
+            base = (u * (c // 3)) % E
+            ids_c = ((base + rng.permutation(u)) % E).astype(np.int32)
+            id_bufs.append(torch.from_numpy(ids_c).to(dev))
+        out = torch.empty(u * n, dtype=torch.float32, device=dev)
+        p = mm.id_params(1, n, k, u, E, n * k * 2, 0, 0, 0)
+        xb, ob = mm.buf(x), mm.buf(out)
+        ib = [mm.buf(t) for t in id_bufs]
+
+        def step(i):
+            mm.mm_id_direct(p, wl.BF16, wb[i % 3], xb, ib[i], ob, stream=stream)
+        t, _ = timer.time(step, cycle, max(cycle, 48), 5)
+        nbytes = u * n * k * 2 + k * 4 + u * 4 + u * n * 4
+        rows.append({"experts": u, "bytes": nbytes, "us": t * 1e3, "gbs": nbytes / (t * 1e6),
+                     "reuse_distance_bytes": (cycle - 1) * u * n * k * 2})
+        log(f"direct decode u={u:2d}: {t * 1e3:7.2f} us  {nbytes / 1e6:7.2f} MB  {nbytes / (t * 1e6):7.1f} GB/s")
+    bx = np.array([r["bytes"] for r in rows], dtype=np.float64)
+    ty = np.array([r["us"] for r in rows], dtype=np.float64)
+    slope, fixed = np.polyfit(bx, ty, 1)
+    a = torch.zeros(1, dtype=torch.float32, device=dev)
+    b = torch.zeros(1, dtype=torch.float32, device=dev)
+    c = torch.zeros(1, dtype=torch.float32, device=dev)
+    d1 = mm.gemm_desc(wl.F32, 1, 1, 1)
+    bufs = (mm.buf(a), mm.buf(b), mm.buf(c))
+    t1, _ = timer.time(lambda i: mm.mm_gemm(d1, *bufs, stream=stream), 1, 200, 20)
+    res = {"sweep": "direct decode vs distinct experts", "rows": rows,
+           "fixed_us": fixed, "marginal_gbs": 1e-3 / slope, "smallest_call_us": t1 * 1e3}
+    log(f"fit: fixed {fixed:.2f} us per call, marginal {1e-3 / slope:.0f} GB/s; "
+        f"smallest call (1x1x1 GEMV) {t1 * 1e3:.2f} us")
+    print(json.dumps(res))
 
 
 def calibrate_gemm(torch, mm, wl, dev, stream, args):
@@ -429,6 +486,9 @@ def main():
         return
     if args.calibrate_gemm:
         calibrate_gemm(torch, mm, wl, dev, stream, args)
+        return
+    if args.decode_sweep:
+        decode_sweep(torch, mm, wl, dev, stream, args)
         return
 
     def to_dev(bits):
