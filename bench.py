@@ -74,6 +74,10 @@ def parse():
                     help="only time the expert-ID direct route at one token against the number "
                          "of distinct experts it reads (fixed cost and marginal bandwidth) and the "
                          "smallest call (a one-element GEMV), and print one JSON line")
+    ap.add_argument("--host-cost", action="store_true",
+                    help="only time the CPU cost per eager call (binding, validation, route "
+                         "decision and HIP launch) of the library against torch's matmul on "
+                         "tiny f16 products, and print one JSON line")
     ap.add_argument("--calibrate-gemm", action="store_true",
                     help="only time the skinny, tiled-GEMM and GEMV routes of x[m,k] . W[n,k]^T "
                          "for m = 2..64 at three (n, k) (route crossover) and print one JSON line")
@@ -450,6 +454,61 @@ def cpu_baselines(wl, want):
     return out
 
 
+def host_cost(torch, mm, dev, stream, args):
+    """CPU time per eager call on the launch stream, for products small enough
+    that the GPU keeps up with the host: the library's whole call (Python
+    binding, validation, route decision, HIP launch) against torch's own
+    matmul of the same product (rlx-metal 0.2.14 mps_blas.rs, module doc: the
+    per-call bridge cost), and the ctypes floor (a call of mm_last_error)."""
+    lib = mm.load()
+    calls = 4000
+    res = {}
+    shapes = [("gemv_f16_1x64_64", 1, 64, 64), ("skinny_f16_8x64_64", 8, 64, 64),
+              ("gemm_f16_128x128_128", 128, 128, 128)]
+    with torch.cuda.stream(stream):
+        for name, m, n, k in shapes:
+            a = torch.randn(m, k, device=dev, dtype=torch.float16)
+            b = torch.randn(n, k, device=dev, dtype=torch.float16)
+            c = torch.empty(m, n, device=dev, dtype=torch.float16)
+            bt = b.t()
+            d = mm.gemm_desc(mm.MM_F16, m, n, k, trans_b=True)
+            A, B, C = mm.buf(a), mm.buf(b), mm.buf(c)
+            sp = stream.cuda_stream
+
+            def ours():
+                mm.mm_gemm(d, A, B, C, stream=sp)
+
+            def theirs():
+                torch.mm(a, bt, out=c)
+
+            row = {}
+            for label, f in (("mm_gemm", ours), ("torch_mm", theirs)):
+                for _ in range(200):
+                    f()
+                stream.synchronize()
+                best = float("inf")
+                for _ in range(3):
+                    t0 = time.perf_counter()
+                    for _ in range(calls):
+                        f()
+                    t1 = time.perf_counter()
+                    stream.synchronize()
+                    best = min(best, (t1 - t0) / calls * 1e6)
+                row[label] = round(best, 3)
+            row["route"] = mm.mm_gemm(d, A, B, C, stream=sp).route
+            stream.synchronize()
+            res[name] = row
+            log(f"{name}: mm_gemm {row['mm_gemm']:.2f} us/call, torch.mm {row['torch_mm']:.2f} us/call (host)")
+    best = float("inf")
+    for _ in range(3):
+        t0 = time.perf_counter()
+        for _ in range(calls):
+            lib.mm_last_error()
+        best = min(best, (time.perf_counter() - t0) / calls * 1e6)
+    print(json.dumps({"host_cost_us_per_call": res, "ctypes_floor_us": round(best, 3),
+                      "calls": calls}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -486,6 +545,9 @@ def main():
         return
     if args.calibrate_gemm:
         calibrate_gemm(torch, mm, wl, dev, stream, args)
+        return
+    if args.host_cost:
+        host_cost(torch, mm, dev, stream, args)
         return
     if args.decode_sweep:
         decode_sweep(torch, mm, wl, dev, stream, args)

@@ -381,7 +381,8 @@ const char *mm_last_error(void);
 /* ------------------------------------------------------------------------ */
 
 /* Make the next launch-resolution step on this thread fail for the kernel
- * family `name` ("gemv", "gemm", "id_direct", "id_map", "id_grouped"), before
+ * family `name` ("gemv", "gemv_wide", "gemm", "id_direct", "id_map",
+ * "id_grouped"), before
  * anything is enqueued, like the pipeline-lookup failure injected in
  * mlx-native's `grouped_pipeline_resolution_failure_does_not_mutate_encoder`.
  * NULL clears it. */
