@@ -425,20 +425,22 @@ __device__ __forceinline__ int lswz(int r) { return (r >> 2) & 3; }
 // With k this short the product is bound by memory (the batched 32 x 512 x
 // 512 x 128 workload does 85 FLOP per byte, below the MFMA ridge), and the
 // 128 x 128 kernels run fetch, MFMA and stores in lockstep across the whole
-// grid. Here a block owns one 64-row panel of A (kept in LDS for the whole
-// block) and walks the batch's B in tiles of 128 rows through three LDS
-// stages: B tile t+2 is in flight by DMA (buffer_load ... lds, 1 KiB per
-// instruction) while tile t is multiplied and its 64 x 128 output leaves
-// through a per-wave LDS stage as 16-byte row pieces, so the output stores
-// of one tile overlap the fetch of the next ones. Each wave computes 32 x 64
-// (2 x 4 fragments of v_mfma_f32_16x16x32). Rows of S = k / 8 16-byte chunks
+// grid. Here a block owns one panel of PMT = 64 or 128 rows of A (kept in LDS
+// for the whole block) and walks the batch's B in tiles of PN rows through
+// three LDS stages: B tile t+2 is in flight by DMA (buffer_load ... lds,
+// 1 KiB per instruction) while tile t is multiplied and its PMT x PN output
+// leaves through a per-wave LDS stage as 16-byte row pieces, so the output
+// stores of one tile overlap the fetch of the next ones. The block has
+// PMT / 16 waves, each computing 32 x PN / 2 (2 x PN / 32 fragments of
+// v_mfma_f32_16x16x32); a 128-row panel streams each B tile once for twice
+// the rows of a 64-row one, halving B's reads from L2. Rows of S = k / 8 16-byte chunks
 // are stored with chunk c of row r at slot c ^ ((r / (16 / S)) & (S - 1)), so
 // the fragment reads of 16 consecutive rows at one chunk index hit 16
 // distinct 16-byte bank groups; each DMA lane fetches the chunk that belongs
 // at its slot. Blocks are ordered so that the panels of one batch item run
 // on one XCD and share its B in L2.
 // ---------------------------------------------------------------------------
-constexpr int PM = 64, PThreads = 256, PStages = 3;
+constexpr int PStages = 3;
 
 template <int S>
 __device__ __forceinline__ int pswz(int r) {
@@ -449,28 +451,31 @@ __device__ __forceinline__ int pswz(int r) {
 // of padding put the 16 rows one staging write covers in distinct banks.
 __host__ __device__ constexpr int panel_pitch(int PN) { return PN / 2 + 8; }
 
-// LDS of one block: A panel, PStages B stages of PN rows, four 32-row
-// epilogue stages.
-__host__ __device__ constexpr size_t panel_lds_bytes(int S, int PN) {
-    return ((size_t)(PM + PStages * PN) * S * 8 + 4 * 32 * panel_pitch(PN)) * sizeof(uint16_t);
+// LDS of one block: A panel of PMT rows, PStages B stages of PN rows, one
+// 32-row epilogue stage per wave (PMT / 16 waves).
+__host__ __device__ constexpr size_t panel_lds_bytes(int S, int PN, int PMT) {
+    return ((size_t)(PMT + PStages * PN) * S * 8 + (PMT / 16) * 32 * panel_pitch(PN)) *
+           sizeof(uint16_t);
 }
 
-// Block = one (batch item, 64-row panel of A, group of B tiles); `nsplit`
+// Block = one (batch item, PMT-row panel of A, group of B tiles); `nsplit`
 // groups split the batch item's n / PN tiles (more blocks when there are few
 // panels), and the groups of one panel follow each other in the block order.
-template <class T, int S, int PN>
-__global__ __launch_bounds__(PThreads, 1) void gemm_nt_panel(GemmArgs a, int nsplit) {
+template <class T, int S, int PN, int PMT>
+__global__ __launch_bounds__(PMT * 4, 1) void gemm_nt_panel(GemmArgs a, int nsplit) {
     constexpr int K = S * 8;          // contraction length
+    constexpr int NW = PMT / 16;      // waves: PMT / 32 row slabs x 2 column halves
     constexpr int RPI = 64 / S;       // tile rows per 1 KiB DMA instruction
-    constexpr int NA = PM / RPI / 4;  // A instructions per wave (= S / 4)
-    constexpr int NB = PN / RPI / 4;  // B instructions per wave per tile
+    constexpr int NA = PMT / RPI / NW;  // A instructions per wave (= S / 4)
+    constexpr int NB = PN / RPI / NW;   // B instructions per wave per tile
+    static_assert(NA * RPI * NW == PMT && NB * RPI * NW == PN, "whole DMA instructions per wave");
     constexpr int NV = S / 4;         // lane offset patterns (the swizzle repeats every 16 rows)
     constexpr int WN = PN / 2;        // wave tile: 32 rows x WN columns
     constexpr int FN = WN / 16;       // 16-column fragments per wave
     constexpr int NST = PN / 32;      // store instructions per wave per tile (1 KiB each)
     constexpr int SRW = 1024 / PN;    // rows per store instruction
     constexpr int SLN = PN / 16;      // lanes per stored row (16 bytes each)
-    constexpr int AH = PM * K, BH = PN * K;  // halves per A panel / B stage
+    constexpr int AH = PMT * K, BH = PN * K;  // halves per A panel / B stage
     constexpr int PSP = panel_pitch(PN);
     extern __shared__ __attribute__((aligned(1024))) uint16_t lds[];
     uint16_t* const As = lds;
@@ -480,14 +485,14 @@ __global__ __launch_bounds__(PThreads, 1) void gemm_nt_panel(GemmArgs a, int nsp
     const int wm = w >> 1, wn = w & 1;
     uint16_t* const stg = lds + AH + PStages * BH + w * 32 * PSP;
 
-    const int64_t panels = a.m / PM;
+    const int64_t panels = a.m / PMT;
     const int64_t items = panels * a.batch * nsplit;
     const int64_t per_xcd = (items + 7) / 8;
     const int64_t item = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
     if (item >= items) return;
     const int64_t pi = item / nsplit;
     const int h = (int)(item % nsplit);
-    const int64_t b = pi / panels, m0 = (pi % panels) * PM;
+    const int64_t b = pi / panels, m0 = (pi % panels) * PMT;
     const int all_tiles = (int)(a.n / PN);
     const int t_begin = (int)((int64_t)all_tiles * h / nsplit);
     const int ntiles = (int)((int64_t)all_tiles * (h + 1) / nsplit) - t_begin;
@@ -501,9 +506,10 @@ __global__ __launch_bounds__(PThreads, 1) void gemm_nt_panel(GemmArgs a, int nsp
         const_cast<uint16_t*>(Bb), (short)0, (int)(((a.n - 1) * a.ldb + K) * 2), 0x00020000);
     // DMA lane offsets (bytes): the lane covers row lane / S of an
     // instruction and fetches the chunk that the swizzle puts at slot
-    // lane % S. The swizzle depends on the row modulo 16 and every wave's
-    // first instruction starts at a multiple of 16 rows, so instruction jj
-    // uses pattern jj % NV (NV <= 4); named scalars, one per pattern.
+    // lane % S. The swizzle depends on the row modulo 16, so instruction j
+    // of a tile (rows j * RPI ..) uses pattern j % NV (NV <= 4); named
+    // scalars, one per pattern. (A wave's first B instruction need not start
+    // at a multiple of 16 rows: with eight waves it starts at row 8 * w.)
     const int lrow = lane / S, lslot = lane % S;
     const int c0 = lslot ^ pswz<S>(lrow), c1 = lslot ^ pswz<S>(RPI + lrow);
     const int c2 = lslot ^ pswz<S>(2 * RPI + lrow), c3 = lslot ^ pswz<S>(3 * RPI + lrow);
@@ -514,18 +520,18 @@ __global__ __launch_bounds__(PThreads, 1) void gemm_nt_panel(GemmArgs a, int nsp
     auto dma_a = [&]() {
 #pragma unroll
         for (int jj = 0; jj < NA; ++jj) {
-            const int j = w * NA + jj;
+            const int j = w * NA + jj, pat = j % NV;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, MM_LDS(As + j * RPI * K), 16,
-                                                     jj % NV == 0 ? voa0 : jj % NV == 1 ? voa1 : jj % NV == 2 ? voa2 : voa3,
+                                                     pat == 0 ? voa0 : pat == 1 ? voa1 : pat == 2 ? voa2 : voa3,
                                                      (int)((m0 + j * RPI) * lda * 2), 0, 0);
         }
     };
     auto dma_b = [&](int t, int st) {  // t: tile index within the batch item
 #pragma unroll
         for (int jj = 0; jj < NB; ++jj) {
-            const int j = w * NB + jj;
+            const int j = w * NB + jj, pat = j % NV;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, MM_LDS(Bs + st * BH + j * RPI * K), 16,
-                                                     jj % NV == 0 ? vob0 : jj % NV == 1 ? vob1 : jj % NV == 2 ? vob2 : vob3,
+                                                     pat == 0 ? vob0 : pat == 1 ? vob1 : pat == 2 ? vob2 : vob3,
                                                      (t * PN + j * RPI) * ldb * 2, 0, 0);
         }
     };
@@ -999,34 +1005,42 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, Launched* L) {
         L->kernel = MM_KERNEL_GEMM_LARGE;
         return hipLaunchKernel(fn, dim3(grid, gy), dim3(LThreads), args, kLargeLds, s);
     }
-    const int64_t panel_items = (a.m / PM) * a.batch;
     constexpr int PNW = 64;  // B tile rows of the panel kernel
-    if (vec && !a.ta && a.tb && (a.k == 32 || a.k == 64 || a.k == 128) && a.m % PM == 0 &&
+    const int64_t panel_items = (a.m / 64) * a.batch;
+    if (vec && !a.ta && a.tb && (a.k == 32 || a.k == 64 || a.k == 128) && a.m % 64 == 0 &&
         a.n % PNW == 0 && a.beta == 0.f && a.ldc % 8 == 0 && aligned16(a.C) && a.sc % 8 == 0 &&
         panel_items >= 128 && panel_items < (1ll << 28)) {
-        // Batched short-K NT products: A panel resident, B tiles streamed. Two
-        // blocks fit per CU (74 KiB of LDS each at k = 128); the tiles of a
-        // panel are split over up to four blocks so that at least 512 blocks
-        // run.
-        static_assert(2 * panel_lds_bytes(16, PNW) <= 160 * 1024, "two blocks per CU");
+        // Batched short-K NT products: A panel resident, B tiles streamed, the
+        // tiles of a panel split over up to four blocks. 128-row panels (one
+        // 8-wave block per CU, 100 KiB of LDS at k = 128) read each B tile
+        // once per 128 rows; they are taken for k = 64 or 128 when they can
+        // still fill every CU. Otherwise 64-row panels (two 4-wave blocks per
+        // CU, 74 KiB each at k = 128), split so that at least 512 blocks run.
+        static_assert(2 * panel_lds_bytes(16, PNW, 64) <= 160 * 1024, "two blocks per CU");
+        static_assert(panel_lds_bytes(16, PNW, 128) <= 160 * 1024, "one block per CU");
         const int S = (int)(a.k / 8);
         const int64_t tiles = a.n / PNW;
-        int nsplit = (int)((512 + panel_items - 1) / panel_items);
-        if (nsplit > 4) nsplit = 4;
-        if (nsplit > tiles) nsplit = (int)tiles;
+        const int64_t max_split = tiles < 4 ? tiles : 4;
+        const bool tall = S >= 8 && a.m % 128 == 0 && (a.m / 128) * a.batch * max_split >= 256;
+        const int pm = tall ? 128 : 64;
+        const int64_t items0 = (a.m / pm) * a.batch;
+        const int64_t want = tall ? 256 : 512;
+        int nsplit = (int)((want + items0 - 1) / items0);
+        if (nsplit > max_split) nsplit = (int)max_split;
         const void* fn = nullptr;
-        if (a.dtype == 1)
-            fn = S == 4 ? (const void*)&gemm_nt_panel<TF16, 4, PNW>
-               : S == 8 ? (const void*)&gemm_nt_panel<TF16, 8, PNW> : (const void*)&gemm_nt_panel<TF16, 16, PNW>;
-        else
-            fn = S == 4 ? (const void*)&gemm_nt_panel<TBF16, 4, PNW>
-               : S == 8 ? (const void*)&gemm_nt_panel<TBF16, 8, PNW> : (const void*)&gemm_nt_panel<TBF16, 16, PNW>;
-        const int64_t items = panel_items * nsplit;
+#define MM_PANEL(T) (tall ? (S == 8 ? (const void*)&gemm_nt_panel<T, 8, PNW, 128>           \
+                                    : (const void*)&gemm_nt_panel<T, 16, PNW, 128>)          \
+                          : S == 4 ? (const void*)&gemm_nt_panel<T, 4, PNW, 64>              \
+                          : S == 8 ? (const void*)&gemm_nt_panel<T, 8, PNW, 64>              \
+                                   : (const void*)&gemm_nt_panel<T, 16, PNW, 64>)
+        fn = a.dtype == 1 ? MM_PANEL(TF16) : MM_PANEL(TBF16);
+#undef MM_PANEL
+        const int64_t items = items0 * nsplit;
         const unsigned grid = (unsigned)(((items + 7) / 8) * 8);
         void* pargs[] = {const_cast<GemmArgs*>(&a), &nsplit};
         L->kernel = MM_KERNEL_GEMM_PANEL;
-        L->variant = nsplit;
-        return hipLaunchKernel(fn, dim3(grid), dim3(PThreads), pargs, panel_lds_bytes(S, PNW), s);
+        L->variant = nsplit | (pm << 8);
+        return hipLaunchKernel(fn, dim3(grid), dim3(pm * 4), pargs, panel_lds_bytes(S, PNW, pm), s);
     }
     const int64_t total = ((a.m + GBM - 1) / GBM) * ((a.n + GBN - 1) / GBN) * a.batch;
     int64_t per_xcd = (total + 7) / 8;

@@ -97,7 +97,7 @@ typedef enum {
     MM_KERNEL_ID_GROUPED_FMA = 10,   /* grouped pass, FMA tiles (other f16/f32 layouts) */
     MM_KERNEL_GEMV_WIDE = 11,        /* skinny route, one to four 16 x 16 MFMA fragments per block */
     MM_KERNEL_GEMM_F32_SMALL = 12,   /* f32, k <= 128, few tiles: one wave per 16 x 16 f32 MFMA tile */
-    MM_KERNEL_GEMM_PANEL = 13        /* NT, k in {32, 64, 128}: 64-row A panel in LDS, B tiles streamed */
+    MM_KERNEL_GEMM_PANEL = 13        /* NT, k in {32, 64, 128}: 64- or 128-row A panel in LDS, B tiles streamed */
 } mm_kernel;
 
 typedef struct {
@@ -118,8 +118,9 @@ typedef struct {
                                  MM_KERNEL_GEMV_WIDE the activation fragments
                                  per block (one per 16 rows, up to 4);
                                  for MM_KERNEL_GEMM_PANEL the number of blocks
-                                 a 64-row panel's B tiles are split over; 0
-                                 for every other family */
+                                 a panel's B tiles are split over, plus 256
+                                 times the panel height in rows (64 or 128);
+                                 0 for every other family */
 } mm_receipt;
 
 /* ------------------------------------------------------------------------ */

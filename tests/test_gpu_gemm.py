@@ -315,30 +315,64 @@ def test_large_tile_route_full_compare(dt, seed):
     _say(f"  max err {err:.3e}")
 
 
+def panel_variant(b, m, n, k):
+    """(split, panel rows) the panel kernel takes: 128-row panels for k = 64
+    or 128 when m % 128 == 0 and (m / 128) * b * min(4, n / 64) reaches 256
+    blocks, split to reach 256 blocks; else 64-row panels split to reach 512
+    blocks; the split is at most 4 and at most the n / 64 tiles."""
+    tiles = n // 64
+    most = min(4, tiles)
+    tall = k >= 64 and m % 128 == 0 and (m // 128) * b * most >= 256
+    pm = 128 if tall else 64
+    items = (m // pm) * b
+    want = 256 if tall else 512
+    return min(most, -(-want // items)), pm
+
+
+def check_panel_variant(rec, b, m, n, k):
+    assert rec.kernel == mm.MM_KERNEL_GEMM_PANEL, rec.kernel
+    got = (rec.variant & 0xff, rec.variant >> 8)
+    assert got == panel_variant(b, m, n, k), f"(split, panel rows) {got}"
+    return got
+
+
 @pytest.mark.parametrize("dt", [wl.F16, wl.BF16])
 @pytest.mark.parametrize("k", [32, 64, 128])
-@pytest.mark.parametrize("n,nsplit", [(128, 2), (192, 3), (384, 4), (640, 4), (1536, 4)])
-def test_panel_kernel(dt, k, n, nsplit):
+@pytest.mark.parametrize("n", [128, 192, 384, 640, 1536])
+def test_panel_kernel(dt, k, n):
     """Batched short-K NT products on the panel kernel (A panel resident in
     LDS, B tiles of 64 rows streamed through three stages, a panel's tiles
-    split over up to four blocks): every admissible k, 1 to 6 tiles per
-    block (every pipeline depth), all outputs against the oracle; the
-    receipt names the split."""
+    split over up to four blocks): every admissible k, 64-row panels (n =
+    128, 192, and every n at k = 32) and 128-row panels (n >= 384 at k = 64
+    and 128), 1 to 6 tiles per block (every pipeline depth), all outputs
+    against the oracle; the receipt names the split and the panel height."""
     b, m = 16, 512
     _say(f"panel NT dt={wl.DTYPE_NAMES[dt]} b={b} m={m} n={n} k={k}")
     case = wl.random_gemm_case(47 + k + n, dt, b, m, n, k, False, True)
     rec = check_gemm(case, what=f"panel k={k} n={n}")
-    assert rec.kernel == mm.MM_KERNEL_GEMM_PANEL, rec.kernel
-    assert rec.variant == nsplit, rec.variant
+    split, pm = check_panel_variant(rec, b, m, n, k)
+    assert pm == (128 if k >= 64 and n >= 384 else 64), pm
+    assert split == {128: 2, 192: 3}.get(n, 4), split
 
 
-def test_panel_kernel_unsplit_long_rows():
-    """Enough panels that no split is needed: each block walks all 8 B tiles."""
-    b, m, n, k = 64, 512, 512, 128
-    _say("panel NT unsplit bf16 b=64 m=512 n=512 k=128")
-    case = wl.random_gemm_case(48, wl.BF16, b, m, n, k, False, True)
+@pytest.mark.parametrize("k", [64, 128])
+def test_panel_kernel_unsplit_long_rows(k):
+    """Enough 128-row panels that no split is needed: each block walks all 8
+    B tiles."""
+    b, m, n = 64, 512, 512
+    _say(f"panel NT unsplit bf16 b=64 m=512 n=512 k={k}")
+    case = wl.random_gemm_case(48 + k, wl.BF16, b, m, n, k, False, True)
     rec = check_gemm(case, what="panel unsplit")
-    assert rec.kernel == mm.MM_KERNEL_GEMM_PANEL and rec.variant == 1, (rec.kernel, rec.variant)
+    assert check_panel_variant(rec, b, m, n, k) == (1, 128)
+
+
+def test_panel_kernel_unsplit_64_row_panels():
+    """k = 32 keeps 64-row panels; enough of them that no split is needed."""
+    b, m, n, k = 64, 512, 512, 32
+    _say("panel NT unsplit f16 b=64 m=512 n=512 k=32")
+    case = wl.random_gemm_case(49, wl.F16, b, m, n, k, False, True)
+    rec = check_gemm(case, what="panel unsplit k=32")
+    assert check_panel_variant(rec, b, m, n, k) == (1, 64)
 
 
 @pytest.mark.parametrize("dt", [wl.F16, wl.BF16])
@@ -353,7 +387,7 @@ def test_panel_kernel_padded_offsets_ramp_exact(dt):
                              off_a=8, off_b=16, off_c=8, stride_a=m * (k + 8) + 64,
                              stride_b=n * (k + 24) + 8, stride_c=m * (n + 8) + 16)
     rec = check_gemm(case, exact=True, what="panel padded ramp")
-    assert rec.kernel == mm.MM_KERNEL_GEMM_PANEL, rec.kernel
+    assert check_panel_variant(rec, b, m, n, k) == (4, 128)
 
 
 @pytest.mark.parametrize("k", [128, 192, 320])

@@ -56,6 +56,8 @@ def test_gemm_f16_batched():
     run = GemmRun(case)
     rec = run.run()
     assert rec.route == mm.MM_ROUTE_GEMM and rec.kernel == mm.MM_KERNEL_GEMM_PANEL, rec.kernel
+    # 128-row panels, each panel's 8 B tiles split over 2 blocks (256 blocks).
+    assert (rec.variant & 0xff, rec.variant >> 8) == (2, 128), rec.variant
     bits = run.c_bits()
     got, mask = run.logical_c(bits)
     run.check_untouched(bits, mask)
