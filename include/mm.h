@@ -333,7 +333,9 @@ mm_status mm_id(const mm_id_params *params, mm_dtype weight_dtype, mm_buf weight
  * (round_up(4 * n_experts, 256) + 4 * n_experts * m bytes above the limit)
  * fails with MM_ERR_SCRATCH before anything is enqueued. The call makes no
  * hipMalloc / hipFree and calls no allocating routine; its first call on a
- * GPU looks up that GPU's array address once. Every call on one GPU shares
+ * GPU looks up that GPU's array address once (a runtime query, not a stream
+ * operation: make that first call outside stream capture; later calls can be
+ * captured in a HIP graph and replayed). Every call on one GPU shares
  * the array: calls that overlap on one GPU (two streams at once) race and
  * give unspecified results. The caller still passes inputs and outputs.
  */

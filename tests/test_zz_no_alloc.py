@@ -49,3 +49,41 @@ def test_noalloc_matches_caller_scratch_twice(wdt):
         np.testing.assert_array_equal(got.view(np.uint32), ref_bits.view(np.uint32))
         wmax, xmax = run.absmax()
         assert_close(got.astype(np.float64), run.oracle(), wdt, k, wmax, xmax, "no-alloc")
+
+
+def test_noalloc_under_graph_capture_replays():
+    """Captured in a HIP graph after one eager call on the GPU (which looks up
+    the array's address), the allocation-free prefill replays correctly: three
+    replays, with eager calls between them that overwrite the library's array
+    with another problem's counts and lists, each replay's output bit-equal
+    to the eager result with caller-owned scratch."""
+    wdt = wl.BF16
+    m, n, k, top_k, E = 128, 704, 256, 8, 64
+    _say(f"no-alloc prefill under graph capture m={m} n={n} k={k} top_k={top_k} E={E}")
+    case = wl.random_id_case(210, wdt, m, n, k, top_k, E)
+    case.ids.reshape(-1)[5] = E + 1  # an out-of-range id: a +0.0 row
+    run = IdRun(case, route=1)
+    run.run()
+    ref = from_dev(run.out, np.float32).reshape(m * top_k, n).view(np.uint32).copy()
+
+    other = IdRun(wl.random_id_case(211, wdt, 40, 96, 128, 4, 32), route=1)
+    _noalloc_out(other)  # eager: the first call on this GPU looks up the address
+
+    out = empty_like_bits(m * top_k * n, wl.F32)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        rec = mm.mm_id_prefill_noalloc(run.params, wdt, mm.buf(run.w), mm.buf(run.x),
+                                       mm.buf(run.ids), mm.buf(out), stream=side)
+    assert rec.route == mm.MM_ROUTE_ID_PREFILL and rec.dispatch_count == 2
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.fill_(-1)  # a fill kernel, not a memset node: every replay rewrites all of it
+        _noalloc_out(other)  # overwrites the shared array with another problem
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = from_dev(out, np.float32).reshape(m * top_k, n).view(np.uint32)
+        _say(f"  replay {rep}")
+        np.testing.assert_array_equal(got, ref)
