@@ -251,8 +251,9 @@ __global__ __launch_bounds__(kThreads) void id_direct_fast(IdArgs a) {
     }
 }
 
-// Direct route, staged form: the same block shape and weight stream as
-// id_direct_fast, with the activation row of the block's (token, slot) staged
+// Direct route, staged form: the same block shape (the REUSE form: one weight
+// row per wave) and weight stream as id_direct_fast, with the activation row
+// of the block's (token, slot) staged
 // in LDS once per block (k * 4 bytes, k = 1024 * XPT with XPT in {1, 2, 4, 8}).
 // Its loads are issued next to the id load, before the expert is known, and
 // each wave then reads its activation chunks from LDS instead of from L2.
@@ -265,9 +266,12 @@ __global__ __launch_bounds__(kThreads) void id_direct_staged(IdArgs a) {
     using S = typename T::store_t;
     constexpr int CH = T::Elems16;
     constexpr int G = kWave * DU;  // chunks per group
+    // Weight rows per wave: one when slots reuse a repeated expert (measured
+    // faster for that form), DR otherwise.
+    constexpr int R = REUSE ? 1 : DR;
     extern __shared__ __attribute__((aligned(16))) float xs[];  // k floats
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const int64_t per_block = (int64_t)kWaves * DR;
+    const int64_t per_block = (int64_t)kWaves * R;
     const int64_t nchunks = (a.n + per_block - 1) / per_block;
     const int64_t rows = (int64_t)a.m * a.top_k;
     const int64_t ngroups = (int64_t)a.k / CH / G;
@@ -276,7 +280,7 @@ __global__ __launch_bounds__(kThreads) void id_direct_staged(IdArgs a) {
         // (r, t, s, e depend on the work item only), so every wave reaches
         // the same barriers.
         const int64_t r = work / nchunks;
-        const int64_t j0 = (work % nchunks) * per_block + (int64_t)wave * DR;
+        const int64_t j0 = (work % nchunks) * per_block + (int64_t)wave * R;
         const int64_t t = r / a.top_k;
         const int s = (int)(r % a.top_k);
         const uint32_t v = lane < a.top_k ? a.ids[t * a.top_k + lane] : 0xffffffffu;
@@ -296,7 +300,7 @@ __global__ __launch_bounds__(kThreads) void id_direct_staged(IdArgs a) {
         const uint32_t e = __builtin_amdgcn_readlane(v, s);
         float* out_r = a.out + r * a.n;
         if (e >= a.n_experts) {  // no weight address is formed
-            if (lane < DR && j0 + lane < a.n) out_r[j0 + lane] = 0.f;
+            if (lane < R && j0 + lane < a.n) out_r[j0 + lane] = 0.f;
             continue;
         }
         // Slots of this token naming expert e: the shared layout writes one
@@ -305,15 +309,15 @@ __global__ __launch_bounds__(kThreads) void id_direct_staged(IdArgs a) {
         if (same & ((1ull << s) - 1)) continue;  // an earlier slot owns this expert
         const S* We = reinterpret_cast<const S*>(reinterpret_cast<const char*>(a.W) +
                                                  (uint64_t)e * a.expert_stride_bytes);
-        const S* rowp[DR];
+        const S* rowp[R];
 #pragma unroll
-        for (int q = 0; q < DR; ++q) {
+        for (int q = 0; q < R; ++q) {
             const int64_t j = j0 + q < a.n ? j0 + q : a.n - 1;
             rowp[q] = We + j * a.k;
         }
-        u32x4 wv[DR][DU];
+        u32x4 wv[R][DU];
 #pragma unroll
-        for (int q = 0; q < DR; ++q)
+        for (int q = 0; q < R; ++q)
 #pragma unroll
             for (int u = 0; u < DU; ++u) wv[q][u] = ld16_stream(rowp[q] + (lane + kWave * u) * CH);
         __syncthreads();  // the previous work item's readers are done with xs
@@ -322,15 +326,15 @@ __global__ __launch_bounds__(kThreads) void id_direct_staged(IdArgs a) {
         __syncthreads();
 
         // acc[q] = W rows . staged activation row
-        auto dot = [&](float (&acc)[DR]) {
+        auto dot = [&](float (&acc)[R]) {
 #pragma unroll
-            for (int q = 0; q < DR; ++q) acc[q] = 0.f;
+            for (int q = 0; q < R; ++q) acc[q] = 0.f;
             for (int64_t g = 0; g < (ONE ? 1 : ngroups); ++g) {
-                u32x4 nv[ONE ? 1 : DR][DU];
+                u32x4 nv[ONE ? 1 : R][DU];
                 const bool more = !ONE && g + 1 < ngroups;
                 if constexpr (!ONE) if (more) {
 #pragma unroll
-                    for (int q = 0; q < DR; ++q)
+                    for (int q = 0; q < R; ++q)
 #pragma unroll
                         for (int u = 0; u < DU; ++u)
                             nv[q][u] = ld16_stream(rowp[q] + ((g + 1) * G + lane + kWave * u) * CH);
@@ -343,7 +347,7 @@ __global__ __launch_bounds__(kThreads) void id_direct_staged(IdArgs a) {
                     for (int h = 0; h < CH / 4; ++h)
                         unpack4(*reinterpret_cast<const u32x4*>(xl + 4 * h), &xf[4 * h]);
 #pragma unroll
-                    for (int q = 0; q < DR; ++q) {
+                    for (int q = 0; q < R; ++q) {
                         float wf[CH];
                         unpack_w<T>(wv[q][u], wf);
 #pragma unroll
@@ -352,19 +356,19 @@ __global__ __launch_bounds__(kThreads) void id_direct_staged(IdArgs a) {
                 }
                 if constexpr (!ONE) if (more) {
 #pragma unroll
-                    for (int q = 0; q < DR; ++q)
+                    for (int q = 0; q < R; ++q)
 #pragma unroll
                         for (int u = 0; u < DU; ++u) wv[q][u] = nv[q][u];
                 }
             }
 #pragma unroll
-            for (int q = 0; q < DR; ++q) acc[q] = wave_sum(acc[q]);
+            for (int q = 0; q < R; ++q) acc[q] = wave_sum(acc[q]);
         };
-        float acc[DR];
+        float acc[R];
         dot(acc);
         const uint64_t later = same & ~((2ull << s) - 1);  // s < 64
 #pragma unroll
-        for (int q = 0; q < DR; ++q) {
+        for (int q = 0; q < R; ++q) {
             if (lane == q && j0 + q < a.n) {
                 out_r[j0 + q] = acc[q];
                 if constexpr (!REUSE)
@@ -388,7 +392,7 @@ __global__ __launch_bounds__(kThreads) void id_direct_staged(IdArgs a) {
                 __syncthreads();
                 dot(acc);
 #pragma unroll
-                for (int q = 0; q < DR; ++q)
+                for (int q = 0; q < R; ++q)
                     if (lane == q && j0 + q < a.n) a.out[(t * a.top_k + s3) * a.n + j0 + q] = acc[q];
             }
         }
@@ -1286,18 +1290,19 @@ hipError_t launch_id_direct(const IdArgs& a, hipStream_t s, Launched* L) {
     const bool aligned = a.expert_stride_bytes % 16 == 0 && aligned16(a.W) && aligned16(a.X) &&
                          a.x_tok_stride_bytes % 16 == 0 && a.x_slot_stride_bytes % 16 == 0;
     if (aligned && a.k % (ch * kWave * DU) == 0 && a.top_k <= kWave) {
-        const int64_t per_block = kWaves * DR;
+        const bool one = a.k == ch * kWave * DU;
+        const int64_t xpt = a.k / 4 / kThreads;  // k is a multiple of 1024 here
+        const bool staged = xpt == 1 || xpt == 2 || xpt == 4 || xpt == 8;
+        // Activation row staged in LDS; the slotted layout with one weight
+        // group per row reuses a repeated expert's weights across slots (one
+        // weight row per wave). One weight group is k = 2048 (2-byte weights,
+        // XPT 2) or k = 1024 (f32, XPT 1).
+        const bool reuse = staged && a.layout == 1 && one;
+        const int64_t per_block = kWaves * (reuse ? 1 : DR);
         const int64_t work = (int64_t)a.m * a.top_k * ((a.n + per_block - 1) / per_block);
         const unsigned grid = (unsigned)(work < (1ll << 30) ? work : (1ll << 30));
-        const bool one = a.k == ch * kWave * DU;
         L->kernel = MM_KERNEL_ID_DIRECT_FAST;
-        const int64_t xpt = a.k / 4 / kThreads;  // k is a multiple of 1024 here
-        if (xpt == 1 || xpt == 2 || xpt == 4 || xpt == 8) {
-            // Activation row staged in LDS; the slotted layout with one weight
-            // group per row reuses a repeated expert's weights across slots.
-            // One weight group is k = 2048 (2-byte weights, XPT 2) or k = 1024
-            // (f32, XPT 1).
-            const bool reuse = a.layout == 1 && one;
+        if (staged) {
             L->variant = reuse ? 2 : 1;
             const void* fn = nullptr;
             if (one) {
