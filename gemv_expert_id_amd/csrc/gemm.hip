@@ -425,8 +425,9 @@ __device__ __forceinline__ int lswz(int r) { return (r >> 2) & 3; }
 // With k this short the product is bound by memory (the batched 32 x 512 x
 // 512 x 128 workload does 85 FLOP per byte, below the MFMA ridge), and the
 // 128 x 128 kernels run fetch, MFMA and stores in lockstep across the whole
-// grid. Here a block owns one panel of PMT = 64 or 128 rows of A (kept in LDS
-// for the whole block) and walks the batch's B in tiles of PN rows through
+// grid. Here a block owns one panel of PMT = 64 or 128 rows of A (loaded into
+// LDS once; each wave then keeps its A fragments in registers for the whole
+// block) and walks the batch's B in tiles of PN rows through
 // three LDS stages: B tile t+2 is in flight by DMA (buffer_load ... lds,
 // 1 KiB per instruction) while tile t is multiplied and its PMT x PN output
 // leaves through a per-wave LDS stage as 16-byte row pieces, so the output
@@ -559,6 +560,14 @@ __global__ __launch_bounds__(PMT * 4, 1) void gemm_nt_panel(GemmArgs a, int nspl
     }
     __builtin_amdgcn_s_barrier();
 
+    // The wave's A fragments do not change from tile to tile: read them from
+    // LDS once (2 x K / 32 fragments, at most 32 registers) and keep them.
+    u32x4 fa[K / 32][2];
+#pragma unroll
+    for (int ks = 0; ks < K / 32; ++ks)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) fa[ks][i] = frag(As, wm * 32 + i * 16, ks);
+
     uint16_t* const Cb = reinterpret_cast<uint16_t*>(a.C) + b * a.sc + (m0 + wm * 32) * a.ldc + wn * WN;
     for (int t = 0; t < ntiles; ++t) {
         const int st = t % PStages;
@@ -572,16 +581,14 @@ __global__ __launch_bounds__(PMT * 4, 1) void gemm_nt_panel(GemmArgs a, int nspl
             for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < K / 32; ++ks) {
-            u32x4 fa[2], fb[FN];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) fa[i] = frag(As, wm * 32 + i * 16, ks);
+            u32x4 fb[FN];
 #pragma unroll
             for (int j = 0; j < FN; ++j) fb[j] = frag(Bt, wn * WN + j * 16, ks);
             // D[n][m] = sum_k B(n,k) A(m,k): lane holds C[m = lane%16][n = 4*(lane/16) + q].
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j) acc[i][j] = mfma16<T>(fb[j], fa[i], acc[i][j]);
+                for (int j = 0; j < FN; ++j) acc[i][j] = mfma16<T>(fb[j], fa[ks][i], acc[i][j]);
         }
         // Epilogue: the wave's 32 x WN piece through its LDS stage (LDS
         // instructions of one wave complete in order), then 16-byte row
