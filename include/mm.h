@@ -108,9 +108,10 @@ typedef struct {
     uint32_t kernel;          /* mm_kernel of the last launch */
     uint32_t variant;         /* instance of that kernel family: for
                                  MM_KERNEL_ID_GROUPED_MFMA the 16-output
-                                 fragment slots per wave (2, 4 or 6) of the
-                                 pipelined form, 0 for its 8-wave LDS-split
-                                 bf16 form; for MM_KERNEL_ID_DIRECT_FAST 0
+                                 fragment slots per wave of the pipelined
+                                 form (2 or 4 on 4 waves; 3 + 256 * 8 for its
+                                 8-wave instance), 0 for the 8-wave
+                                 LDS-split bf16 form; for MM_KERNEL_ID_DIRECT_FAST 0
                                  when activations come from L2, 1 when the
                                  block stages its activation row in LDS, 2
                                  when it also reuses a repeated expert's

@@ -117,7 +117,8 @@ def test_moe_prefill(moe):
     assert int(counts.sum()) == case.m * case.top_k
     for e in range(case.n_experts):
         np.testing.assert_array_equal(routed[e, :counts[e]], rr[e, :rc[e]])
-    assert rec.kernel == mm.MM_KERNEL_ID_GROUPED_MFMA and rec.variant == 6, \
+    # 352-wide tiles: 8 waves of 3 sixteen-output fragment slots (3 + 256 * 8).
+    assert rec.kernel == mm.MM_KERNEL_ID_GROUPED_MFMA and rec.variant == 3 | (8 << 8), \
         (rec.kernel, rec.variant)
     got = run.out_f64()
     ref = run.oracle()
