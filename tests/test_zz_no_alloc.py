@@ -51,19 +51,22 @@ def test_noalloc_matches_caller_scratch_twice(wdt):
         assert_close(got.astype(np.float64), run.oracle(), wdt, k, wmax, xmax, "no-alloc")
 
 
-def test_noalloc_under_graph_capture_replays():
+@pytest.mark.parametrize("n,variant", [(704, 4), (1408, 3 | (8 << 8))])
+def test_noalloc_under_graph_capture_replays(n, variant):
     """Captured in a HIP graph after one eager call on the GPU (which looks up
     the array's address), the allocation-free prefill replays correctly: three
     replays, with eager calls between them that overwrite the library's array
     with another problem's counts and lists, each replay's output bit-equal
-    to the eager result with caller-owned scratch."""
+    to the eager result with caller-owned scratch. 704 outputs land on the
+    4-wave grouped instance, 1408 on the 8-wave one."""
     wdt = wl.BF16
-    m, n, k, top_k, E = 128, 704, 256, 8, 64
+    m, k, top_k, E = 128, 256, 8, 64
     _say(f"no-alloc prefill under graph capture m={m} n={n} k={k} top_k={top_k} E={E}")
     case = wl.random_id_case(210, wdt, m, n, k, top_k, E)
     case.ids.reshape(-1)[5] = E + 1  # an out-of-range id: a +0.0 row
     run = IdRun(case, route=1)
-    run.run()
+    rec0 = run.run()
+    assert rec0.kernel == mm.MM_KERNEL_ID_GROUPED_MFMA and rec0.variant == variant, rec0.variant
     ref = from_dev(run.out, np.float32).reshape(m * top_k, n).view(np.uint32).copy()
 
     other = IdRun(wl.random_id_case(211, wdt, 40, 96, 128, 4, 32), route=1)
