@@ -202,6 +202,26 @@ def test_grouped_fragment_slots(wdt, shape, slots, layout):
     _check_all_rows(run, f"grouped slots={slots}")
 
 
+@pytest.mark.parametrize("wdt", DTYPES)
+@pytest.mark.parametrize("layout", [0, 1])
+def test_grouped_max_experts_pipelined(wdt, layout):
+    """The expert limit (1024) on the pipelined grouped kernel: 512 routed
+    rows over 1024 experts, 272-wide tiles (2-byte weights: the 8-wave
+    instance, whose 512 threads rebuild the tile schedule from 1024 counts at
+    two experts each; f32: 4 waves), out-of-range ids, every routed row
+    against the oracle."""
+    m, n, k, top_k, E = 64, 272, 128, 8, 1024
+    _say(f"grouped max experts wdt={wl.DTYPE_NAMES[wdt]} layout={layout} E={E}")
+    case = _with_bad_ids(wl.random_id_case(90, wdt, m, n, k, top_k, E, layout=layout))
+    run = IdRun(case, route=1)
+    rec = run.run()
+    assert rec.kernel == mm.MM_KERNEL_ID_GROUPED_MFMA, rec.kernel
+    if wdt != wl.F32:
+        assert rec.variant == 3 | (8 << 8), rec.variant
+    _check_map(run)
+    _check_all_rows(run, "grouped max experts")
+
+
 @pytest.mark.parametrize("wdt,slots", [(wl.BF16, 6), (wl.F16, 6), (wl.F32, 4)])
 def test_grouped_wide_tiles_full_row_tiles_ramp_exact(wdt, slots):
     """The widest tile of each weight dtype with more than 128 routed rows per
