@@ -10,9 +10,9 @@
 // (X = A) and C = W . X^T (W = A).
 //
 // One block computes NXF (1 to 4) 16 x 16 MFMA fragments: 16 weight rows
-// against all activation rows, 16 per fragment (padded by repeating the last
-// one; padded results are never stored; weight rows past the end repeat the
-// last row the same way). Each weight fragment read from LDS feeds NXF MFMAs.
+// against all activation rows, 16 per fragment (padded rows read zeros
+// without a memory access and their results are never stored; weight rows
+// past the end repeat the last row, also never stored). Each weight fragment read from LDS feeds NXF MFMAs.
 // The weight rows stream through a ring of SST LDS stages, each 16 rows x 1 KB:
 // one DMA instruction (buffer_load ... lds) moves 1 KB of one row, so HBM
 // sees whole contiguous row pieces as in the GEMV row form. Lane i of that
@@ -102,10 +102,14 @@ __global__ __launch_bounds__(SThreads) void gemv_wide(SkinnyArgs a) {
         dbyte[d] = (uint32_t)(gr * a.ldw * (int64_t)sizeof(S));
     }
     constexpr int SOPS = sops(NXF);
-    uint32_t xbyte[NXF];  // activation row of fragment f for this lane
+    // Activation row of fragment f for this lane; padded rows (past nx) read
+    // zeros through an offset beyond the resource range, without a memory access.
+    uint32_t xbyte[NXF];
+    bool xlive[NXF];
 #pragma unroll
     for (int f = 0; f < NXF; ++f) {
-        const int64_t xrow = 16 * f + r < a.nx ? 16 * f + r : a.nx - 1;
+        xlive[f] = 16 * f + r < a.nx;
+        const int64_t xrow = xlive[f] ? 16 * f + r : 0;
         xbyte[f] = (uint32_t)(xrow * a.ldx * (int64_t)sizeof(S));
     }
 
@@ -132,7 +136,7 @@ __global__ __launch_bounds__(SThreads) void gemv_wide(SkinnyArgs a) {
                 for (int j = 0; j < 4; ++j) {
                     const int64_t c = st * SCH + 4 * (4 * wave + j) + g;
                     xv[f][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                   xrs, c < nch ? xbyte[f] + (uint32_t)(c * 16) : kOff, 0, 0));
+                                   xrs, xlive[f] && c < nch ? xbyte[f] + (uint32_t)(c * 16) : kOff, 0, 0));
                 }
         };
         f32x4 acc[NXF];
