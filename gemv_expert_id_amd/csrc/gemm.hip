@@ -427,11 +427,14 @@ __device__ __forceinline__ int lswz(int r) { return (r >> 2) & 3; }
 // 128 x 128 kernels run fetch, MFMA and stores in lockstep across the whole
 // grid. Here a block owns one panel of PMT = 64 or 128 rows of A (loaded into
 // LDS once; each wave then keeps its A fragments in registers for the whole
-// block) and walks the batch's B in tiles of PN rows through
-// three LDS stages: B tile t+2 is in flight by DMA (buffer_load ... lds,
+// block) and walks the batch's B in tiles of PN rows through LA + 1 LDS
+// stages: B tiles t+1 .. t+LA are in flight by DMA (buffer_load ... lds,
 // 1 KiB per instruction) while tile t is multiplied and its PMT x PN output
 // leaves through a per-wave LDS stage as 16-byte row pieces, so the output
-// stores of one tile overlap the fetch of the next ones. The block has
+// stores of one tile overlap the fetch of the next ones. Those stores carry
+// the device-scope write-through policy (sc0 sc1 nt): the output then
+// streams to HBM while the blocks run, instead of staying dirty in the L2s
+// (it fits there) until the write-back at the end of the kernel. The block has
 // PMT / 16 waves, each computing 32 x PN / 2 (2 x PN / 32 fragments of
 // v_mfma_f32_16x16x32); a 128-row panel streams each B tile once for twice
 // the rows of a 64-row one, halving B's reads from L2. Rows of S = k / 8 16-byte chunks
@@ -441,7 +444,12 @@ __device__ __forceinline__ int lswz(int r) { return (r >> 2) & 3; }
 // at its slot. Blocks are ordered so that the panels of one batch item run
 // on one XCD and share its B in L2.
 // ---------------------------------------------------------------------------
-constexpr int PStages = 3;
+// B stages: three for 64-row panels (two blocks per CU), four for 128-row
+// ones (one block per CU; a block's four B tiles of the batched workload are
+// then all in flight from its start).
+__host__ __device__ constexpr int panel_stages(int PMT) { return PMT == 128 ? 4 : 3; }
+// Cache-policy bits of a buffer store: sc0 (1) | nt (2) | sc1 (16).
+constexpr int kStoreThrough = 1 | 2 | 16;
 
 template <int S>
 __device__ __forceinline__ int pswz(int r) {
@@ -452,10 +460,10 @@ __device__ __forceinline__ int pswz(int r) {
 // of padding put the 16 rows one staging write covers in distinct banks.
 __host__ __device__ constexpr int panel_pitch(int PN) { return PN / 2 + 8; }
 
-// LDS of one block: A panel of PMT rows, PStages B stages of PN rows, one
+// LDS of one block: A panel of PMT rows, panel_stages(PMT) B stages of PN rows, one
 // 32-row epilogue stage per wave (PMT / 16 waves).
 __host__ __device__ constexpr size_t panel_lds_bytes(int S, int PN, int PMT) {
-    return ((size_t)(PMT + PStages * PN) * S * 8 + (PMT / 16) * 32 * panel_pitch(PN)) *
+    return ((size_t)(PMT + panel_stages(PMT) * PN) * S * 8 + (PMT / 16) * 32 * panel_pitch(PN)) *
            sizeof(uint16_t);
 }
 
@@ -478,13 +486,14 @@ __global__ __launch_bounds__(PMT * 4, 1) void gemm_nt_panel(GemmArgs a, int nspl
     constexpr int SLN = PN / 16;      // lanes per stored row (16 bytes each)
     constexpr int AH = PMT * K, BH = PN * K;  // halves per A panel / B stage
     constexpr int PSP = panel_pitch(PN);
+    constexpr int PS = panel_stages(PMT), LA = PS - 1;  // B stages, tiles fetched ahead
     extern __shared__ __attribute__((aligned(1024))) uint16_t lds[];
     uint16_t* const As = lds;
     uint16_t* const Bs = lds + AH;
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = w >> 1, wn = w & 1;
-    uint16_t* const stg = lds + AH + PStages * BH + w * 32 * PSP;
+    uint16_t* const stg = lds + AH + PS * BH + w * 32 * PSP;
 
     const int64_t panels = a.m / PMT;
     const int64_t items = panels * a.batch * nsplit;
@@ -542,22 +551,29 @@ __global__ __launch_bounds__(PMT * 4, 1) void gemm_nt_panel(GemmArgs a, int nspl
         return *reinterpret_cast<const u32x4*>(base + (row0 + lr) * K +
                                                (((4 * ks + lq) ^ pswz<S>(lr)) << 3));
     };
-    auto wait_vm = [](int n) {  // vmcnt <= n, lgkmcnt <= 0
-        if (n == NST) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(NST));
-        else if (n == 2 * NST) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(2 * NST));
-        else if (n == NB + NST) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(NB + NST));
-        else __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(NB + 2 * NST));
+    // vmcnt <= NB * nb + NST * ns (lgkmcnt <= 0): at most nb < LA B tiles'
+    // DMA and 1 <= ns <= LA tiles' stores younger than the awaited tile.
+    auto wait_vm = [](int nb, int ns) {
+        static_for(std::make_integer_sequence<int, LA>{}, [&](auto NB_) {
+            static_for(std::make_integer_sequence<int, LA>{}, [&](auto NS_) {
+                constexpr int cnt = NB * decltype(NB_)::value + NST * (decltype(NS_)::value + 1);
+                static_assert(cnt <= 63, "vmcnt range");
+                if (nb == decltype(NB_)::value && ns == decltype(NS_)::value + 1)
+                    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(cnt));
+            });
+        });
     };
 
-    // Prologue: the A panel and the first two B tiles; wait for A and tile 0.
+    // Prologue: the A panel and the first LA B tiles; wait for A and tile 0.
     dma_a();
+    const int pre = ntiles < LA ? ntiles : LA;
     dma_b(t_begin, 0);
-    if (ntiles > 1) {
-        dma_b(t_begin + 1, 1);
-        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(NB));
-    } else {
-        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
-    }
+    if (pre > 1) dma_b(t_begin + 1, 1);
+    if (LA > 2 && pre > 2) dma_b(t_begin + 2, 2);
+    static_assert(LA <= 3, "prologue issues at most three tiles");
+    if (pre == 3) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(2 * NB));
+    else if (pre == 2) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(NB));
+    else __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
     __builtin_amdgcn_s_barrier();
 
     // The wave's A fragments do not change from tile to tile: read them from
@@ -568,11 +584,14 @@ __global__ __launch_bounds__(PMT * 4, 1) void gemm_nt_panel(GemmArgs a, int nspl
 #pragma unroll
         for (int i = 0; i < 2; ++i) fa[ks][i] = frag(As, wm * 32 + i * 16, ks);
 
-    uint16_t* const Cb = reinterpret_cast<uint16_t*>(a.C) + b * a.sc + (m0 + wm * 32) * a.ldc + wn * WN;
+    // C of this batch item spans below 2 GiB (checked by the launcher).
+    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<uint16_t*>(a.C) + b * a.sc, (short)0, (int)(((a.m - 1) * a.ldc + a.n) * 2), 0x00020000);
+    const int cbase = (int)(((m0 + wm * 32) * a.ldc + wn * WN) * 2);
     for (int t = 0; t < ntiles; ++t) {
-        const int st = t % PStages;
-        // Stage (t + 2) % 3 held tile t - 1, which every wave finished before the barrier.
-        if (t + 2 < ntiles) dma_b(t_begin + t + 2, (t + 2) % PStages);
+        const int st = t % PS;
+        // Stage (t + LA) % PS held tile t - 1, which every wave finished before the barrier.
+        if (t + LA < ntiles) dma_b(t_begin + t + LA, (t + LA) % PS);
         const uint16_t* Bt = Bs + st * BH;
         f32x4 acc[2][FN];
 #pragma unroll
@@ -592,7 +611,7 @@ __global__ __launch_bounds__(PMT * 4, 1) void gemm_nt_panel(GemmArgs a, int nspl
         }
         // Epilogue: the wave's 32 x WN piece through its LDS stage (LDS
         // instructions of one wave complete in order), then 16-byte row
-        // pieces, 1 KiB per store instruction.
+        // pieces, 1 KiB per store instruction, written through to memory.
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -608,12 +627,16 @@ __global__ __launch_bounds__(PMT * 4, 1) void gemm_nt_panel(GemmArgs a, int nspl
         for (int p = 0; p < NST; ++p) {
             const int r = p * SRW + lane / SLN, c = (lane % SLN) * 8;
             const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * PSP + c);
-            *reinterpret_cast<u32x4*>(Cb + (int64_t)r * a.ldc + col0 + c) = v;
+            __builtin_amdgcn_raw_buffer_store_b128(v, rc, cbase + (int)((r * a.ldc + col0 + c) * 2), 0,
+                                                   kStoreThrough);
         }
         if (t + 1 < ntiles) {
-            // Tile t + 1 has landed once at most these remain: tile t + 2's DMA
-            // (if issued), this tile's stores and the previous tile's.
-            wait_vm((t + 2 < ntiles ? NB : 0) + NST + (t > 0 ? NST : 0));
+            // Tile t + 1 has landed once at most these remain: the DMA of
+            // tiles t + 2 .. t + LA (those issued) and the stores of the
+            // iterations since tile t + 1's DMA was issued.
+            const int last = t + LA < ntiles - 1 ? t + LA : ntiles - 1;
+            const int since = t + 1 - LA > 0 ? t + 1 - LA : 0;
+            wait_vm(last - (t + 1), t - since + 1);
             __builtin_amdgcn_s_barrier();
         }
     }
@@ -1016,10 +1039,10 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, Launched* L) {
     const int64_t panel_items = (a.m / 64) * a.batch;
     if (vec && !a.ta && a.tb && (a.k == 32 || a.k == 64 || a.k == 128) && a.m % 64 == 0 &&
         a.n % PNW == 0 && a.beta == 0.f && a.ldc % 8 == 0 && aligned16(a.C) && a.sc % 8 == 0 &&
-        panel_items >= 128 && panel_items < (1ll << 28)) {
+        panel_items >= 128 && panel_items < (1ll << 28) && a.m * a.ldc < (1ll << 30)) {
         // Batched short-K NT products: A panel resident, B tiles streamed, the
         // tiles of a panel split over up to four blocks. 128-row panels (one
-        // 8-wave block per CU, 100 KiB of LDS at k = 128) read each B tile
+        // 8-wave block per CU, 116 KiB of LDS at k = 128) read each B tile
         // once per 128 rows; they are taken for k = 64 or 128 when they can
         // still fill every CU. Otherwise 64-row panels (two 4-wave blocks per
         // CU, 74 KiB each at k = 128), split so that at least 512 blocks run.

@@ -341,7 +341,8 @@ def check_panel_variant(rec, b, m, n, k):
 @pytest.mark.parametrize("n", [128, 192, 384, 640, 1536])
 def test_panel_kernel(dt, k, n):
     """Batched short-K NT products on the panel kernel (A panel resident in
-    LDS, B tiles of 64 rows streamed through three stages, a panel's tiles
+    LDS, B tiles of 64 rows streamed through three stages (64-row panels) or
+    four (128-row panels), output stores written through, a panel's tiles
     split over up to four blocks): every admissible k, 64-row panels (n =
     128, 192, and every n at k = 32) and 128-row panels (n >= 384 at k = 64
     and 128), 1 to 6 tiles per block (every pipeline depth), all outputs
@@ -358,7 +359,7 @@ def test_panel_kernel(dt, k, n):
 @pytest.mark.parametrize("k", [64, 128])
 def test_panel_kernel_unsplit_long_rows(k):
     """Enough 128-row panels that no split is needed: each block walks all 8
-    B tiles."""
+    B tiles, so its four B stages are reused twice."""
     b, m, n = 64, 512, 512
     _say(f"panel NT unsplit bf16 b=64 m=512 n=512 k={k}")
     case = wl.random_gemm_case(48 + k, wl.BF16, b, m, n, k, False, True)
