@@ -80,7 +80,9 @@ def parse():
                          "tiny f16 products, and print one JSON line")
     ap.add_argument("--calibrate-gemm", action="store_true",
                     help="only time the skinny, tiled-GEMM and GEMV routes of x[m,k] . W[n,k]^T "
-                         "for m = 2..64 at three (n, k) (route crossover) and print one JSON line")
+                         "for m = 2..64 at three (n, k), then the skinny and tiled-GEMM routes at "
+                         "short k (64..1024) with batch 1 and 32 (route crossover), and print one "
+                         "JSON line")
     return ap.parse_args()
 
 
@@ -325,7 +327,43 @@ def calibrate_gemm(torch, mm, wl, dev, stream, args):
             del x, c
         del Ws, wb, w
         torch.cuda.empty_cache()
-    print(json.dumps({"calibration": "skinny vs tiled GEMM vs GEMV routes", "rows": table}))
+    # Short contractions, one and 32 batch items: the skinny route's LDS stages
+    # hold 1 KiB of each weight row, so a short k leaves them partly empty.
+    short = []
+    for batch in (1, 32):
+        for n in (512, 4096):
+            for k in (64, 128, 256, 512, 1024):
+                rng = np.random.default_rng(22)
+                w = to_dev_bits(torch, dev, wl.to_storage(0.02 * rng.standard_normal(batch * n * k), wl.F16))
+                n_rot = min(64, max(2, math.ceil(ROTATE_BYTES / (batch * n * k * 2))))
+                Ws = [w] + [w.clone() for _ in range(n_rot - 1)]
+                wb = [mm.buf(t) for t in Ws]
+                for m in (4, 16, 64):
+                    x = to_dev_bits(torch, dev, wl.to_storage(rng.standard_normal(batch * m * k), wl.F16))
+                    c = torch.empty(batch * m * n, dtype=torch.float16, device=dev)
+                    xb, cbuf = mm.buf(x), mm.buf(c)
+                    d = mm.gemm_desc(wl.F16, m, n, k, batch=batch, trans_b=True, stride_a=m * k,
+                                     stride_b=n * k, stride_c=m * n)
+                    times = {}
+                    for name, route in (("skinny", mm.MM_ROUTE_GEMV_WIDE), ("gemm", mm.MM_ROUTE_GEMM)):
+                        def step(i, route=route):
+                            mm.mm_gemm_route(d, route, xb, wb[i], cbuf, stream=stream)
+                        t, _ = timer.time(step, n_rot, 4 * n_rot, 3)
+                        times[name] = t * 1e3
+                    picked = mm.mm_gemm(d, xb, wb[0], cbuf, stream=stream).route
+                    picked = {mm.MM_ROUTE_GEMV_WIDE: "skinny", mm.MM_ROUTE_GEMM: "gemm",
+                              mm.MM_ROUTE_GEMV: "gemv"}[picked]
+                    fastest = min(times, key=times.get)
+                    short.append({"batch": batch, "n": n, "k": k, "m": m, "us": times,
+                                  "fastest": fastest, "dispatch": picked})
+                    log(f"batch={batch:2d} n={n:5d} k={k:5d} m={m:2d}  "
+                        + "  ".join(f"{r} {t:7.2f} us" for r, t in times.items())
+                        + f"  -> fastest {fastest}, dispatch picks {picked}")
+                    del x, c
+                del Ws, wb, w
+                torch.cuda.empty_cache()
+    print(json.dumps({"calibration": "skinny vs tiled GEMM vs GEMV routes", "rows": table,
+                      "short_k_rows": short}))
 
 
 def to_dev_bits(torch, dev, bits):

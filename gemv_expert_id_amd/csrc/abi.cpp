@@ -296,6 +296,26 @@ bool skinny_args(const GemmPlan& p, mmk::SkinnyArgs* g) {
     return true;
 }
 
+// Whether the automatic dispatch takes the skinny route for a shape it fits
+// (a forced route skips this). The kernel's blocks each stream 16 rows of W
+// through LDS stages of 1 KiB per row, and a CU holds 3, 2, 1 or 1 of them
+// for 1, 2, 3 or 4 activation fragments (registers). When all blocks are
+// resident at once the route wins at every measured shape; when they come in
+// rounds, each block's fixed cost recurs per round, and the tiled GEMM wins
+// unless every block streams long rows (one or two fragments) or the rounds
+// are few (three or four fragments). Thresholds from the short-k, batch 1 and
+// 32 calibration on MI355X's 256 CUs.
+bool skinny_pays(const mmk::SkinnyArgs& g, int dt) {
+    const int nxf = (int)((g.nx + 15) / 16);
+    const int per_cu = nxf == 1 ? 3 : nxf == 2 ? 2 : 1;
+    const int64_t blocks = g.batch * ((g.nw + 15) / 16);
+    const int64_t rounds = (blocks + 256 * per_cu - 1) / (256 * per_cu);
+    if (rounds <= 1) return true;
+    const int64_t row_bytes = g.k * (int64_t)elt_size(dt);
+    if (nxf <= 2) return row_bytes >= (rounds <= 2 ? 512 : 1024);
+    return rounds <= 3;
+}
+
 mm_status run_skinny(const mmk::SkinnyArgs& g, int dt, hipStream_t s, mm_receipt* r) {
     mm_status st = resolve("gemv_wide");
     if (st != MM_OK) return st;
@@ -477,7 +497,7 @@ mmk::IdArgs fill_ptrs(mmk::IdArgs a, mm_buf weights, mm_buf input, mm_buf ids, m
 mm_status dispatch_gemm(const GemmPlan& p, void* stream, mm_receipt* receipt) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     mmk::SkinnyArgs g;
-    if (skinny_args(p, &g)) return run_skinny(g, p.dt, s, receipt);
+    if (skinny_args(p, &g) && skinny_pays(g, p.dt)) return run_skinny(g, p.dt, s, receipt);
     if (p.m == 1 || p.n == 1) return run_gemv(p, s, receipt);
     return run_gemm(p, s, receipt);
 }

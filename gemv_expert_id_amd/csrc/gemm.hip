@@ -434,7 +434,10 @@ __device__ __forceinline__ int lswz(int r) { return (r >> 2) & 3; }
 // stores of one tile overlap the fetch of the next ones. Those stores carry
 // the device-scope write-through policy (sc0 sc1 nt): the output then
 // streams to HBM while the blocks run, instead of staying dirty in the L2s
-// (it fits there) until the write-back at the end of the kernel. The block has
+// until the write-back at the end of the kernel. The 64-row form at k = 128
+// keeps plain stores: measured on MI355X, write-through was faster for the
+// 128-row form and for the 64-row form at k = 32 and 64, slower there. The
+// block has
 // PMT / 16 waves, each computing 32 x PN / 2 (2 x PN / 32 fragments of
 // v_mfma_f32_16x16x32); a 128-row panel streams each B tile once for twice
 // the rows of a 64-row one, halving B's reads from L2. Rows of S = k / 8 16-byte chunks
@@ -487,6 +490,7 @@ __global__ __launch_bounds__(PMT * 4, 1) void gemm_nt_panel(GemmArgs a, int nspl
     constexpr int AH = PMT * K, BH = PN * K;  // halves per A panel / B stage
     constexpr int PSP = panel_pitch(PN);
     constexpr int PS = panel_stages(PMT), LA = PS - 1;  // B stages, tiles fetched ahead
+    constexpr int CPOL = PMT == 64 && S == 16 ? 0 : kStoreThrough;  // output store policy
     extern __shared__ __attribute__((aligned(1024))) uint16_t lds[];
     uint16_t* const As = lds;
     uint16_t* const Bs = lds + AH;
@@ -611,7 +615,8 @@ __global__ __launch_bounds__(PMT * 4, 1) void gemm_nt_panel(GemmArgs a, int nspl
         }
         // Epilogue: the wave's 32 x WN piece through its LDS stage (LDS
         // instructions of one wave complete in order), then 16-byte row
-        // pieces, 1 KiB per store instruction, written through to memory.
+        // pieces, 1 KiB per store instruction (written through but in the
+        // 64-row form at k = 128).
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -628,7 +633,7 @@ __global__ __launch_bounds__(PMT * 4, 1) void gemm_nt_panel(GemmArgs a, int nspl
             const int r = p * SRW + lane / SLN, c = (lane % SLN) * 8;
             const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * PSP + c);
             __builtin_amdgcn_raw_buffer_store_b128(v, rc, cbase + (int)((r * a.ldc + col0 + c) * 2), 0,
-                                                   kStoreThrough);
+                                                   CPOL);
         }
         if (t + 1 < ntiles) {
             // Tile t + 1 has landed once at most these remain: the DMA of

@@ -166,7 +166,12 @@ typedef struct {
  *   - skinny route (MM_ROUTE_GEMV_WIDE) when trans_a == 0, trans_b == 1, one
  *     of m, n is in 2..64 and the other is >= 2, and the 16-byte layout holds:
  *     k, lda, ldb, stride_a and stride_b multiples of 16 / element size and
- *     16-byte aligned A and B (after their offsets);
+ *     16-byte aligned A and B (after their offsets); and the route's blocks
+ *     (batch x ceil(other side / 16), 768, 512 or 256 resident at once for
+ *     up to 16, 32 or 64 skinny rows) run in one round, or in more rounds with
+ *     long rows: k x element size >= 512 bytes for two rounds and >= 1024
+ *     beyond with up to 32 skinny rows, at most three rounds with 33..64
+ *     (measured crossover against the tiled GEMM);
  *   - the GEMV route when m == 1 or n == 1 (the matrix operand is B when
  *     n != 1, else A);
  *   - the tiled MFMA GEMM route otherwise.
@@ -198,7 +203,8 @@ mm_status mm_gemm_ex(const mm_gemm_desc *desc, float alpha, float beta, mm_buf a
  * caller; rlx-metal mps_blas.rs module doc: the route crossover is measured,
  * not assumed). Every route computes the same values. Fails with
  * UNSUPPORTED when the named route cannot take the problem (GEMV: m != 1 and
- * n != 1; skinny: the conditions of mm_gemm's skinny case), else as
+ * n != 1; skinny: the shape and layout conditions of mm_gemm's skinny case,
+ * without its rounds rule), else as
  * mm_gemm_ex; INVALID_ARGUMENT for any other route value.
  */
 mm_status mm_gemm_route(const mm_gemm_desc *desc, uint32_t route, float alpha, float beta,

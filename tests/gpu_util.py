@@ -124,18 +124,38 @@ class GemmRun:
                                                                           self.case.dtype)
 
 
+def skinny_rounds_rule(batch: int, nx: int, nw: int, row_bytes: int) -> bool:
+    """mm.h's rounds rule for the skinny route: its blocks (batch x
+    ceil(nw / 16); 768, 512 or 256 resident at once for nx up to 16, 32 or
+    64) in one round; else rows of at least 512 bytes (two rounds) or 1024
+    (more) for nx <= 32, and at most three rounds for nx in 33..64."""
+    nxf = (nx + 15) // 16
+    cap = 256 * (3 if nxf == 1 else 2 if nxf == 2 else 1)
+    rounds = -(-(batch * -(-nw // 16)) // cap)
+    if rounds <= 1:
+        return True
+    if nxf <= 2:
+        return row_bytes >= (512 if rounds <= 2 else 1024)
+    return rounds <= 3
+
+
 def expected_gemm_route(case: wl.GemmCase) -> int:
     """The route mm_gemm documents for this case (mm.h, dispatch): skinny when
-    A and B keep rows along k, one side has 2..64 rows, the other >= 2, and
-    the 16-byte layout holds (device buffers are 256-byte aligned, so only the
-    offsets matter); GEMV when m == 1 or n == 1; GEMM otherwise."""
+    A and B keep rows along k, one side has 2..64 rows, the other >= 2, the
+    16-byte layout holds (device buffers are 256-byte aligned, so only the
+    offsets matter) and the rounds rule allows it; GEMV when m == 1 or
+    n == 1; GEMM otherwise."""
     c = case
     ch = 16 // wl.ELT[c.dtype]
+    x_is_a = 2 <= c.m <= 64 and c.n >= 2
     skinny = (not c.trans_a and c.trans_b
-              and ((2 <= c.m <= 64 and c.n >= 2) or (2 <= c.n <= 64 and c.m >= 2))
+              and (x_is_a or (2 <= c.n <= 64 and c.m >= 2))
               and c.k % ch == 0 and c.lda % ch == 0 and c.ldb % ch == 0
               and c.stride_a % ch == 0 and c.stride_b % ch == 0
               and c.off_a % 16 == 0 and c.off_b % 16 == 0)
+    if skinny:
+        nx, nw = (c.m, c.n) if x_is_a else (c.n, c.m)
+        skinny = skinny_rounds_rule(c.batch, nx, nw, c.k * wl.ELT[c.dtype])
     if skinny:
         return mm.MM_ROUTE_GEMV_WIDE
     if c.m == 1 or c.n == 1:

@@ -313,6 +313,47 @@ def test_dispatch_crossover_skinny_vs_tiled(dt):
     assert family(1, n) == "gemv"
 
 
+def _dispatch_family(lib, dt, batch, m, n, k):
+    """The launch family mm_gemm resolves for C[b] = A[b] . B[b]^T, found with
+    the resolve-failure hook before anything is enqueued."""
+    d = mm.gemm_desc(dt, m, n, k, batch=batch, trans_b=True, stride_a=m * k, stride_b=n * k,
+                     stride_c=m * n)
+    for fam in (b"gemv_wide", b"gemm", b"gemv"):
+        lib.mm_test_inject_resolve_failure(fam)
+        before = lib.mm_test_launch_count()
+        try:
+            mm.mm_gemm(d, *_gemm_bufs(dt, m, n, k, batch))
+        except mm.MmError as e:
+            if e.status == 2 and "injected" in str(e):
+                lib.mm_test_inject_resolve_failure(None)
+                assert lib.mm_test_launch_count() == before
+                return fam.decode()
+        lib.mm_test_inject_resolve_failure(None)
+    raise AssertionError("no family resolved")
+
+
+@pytest.mark.parametrize("dt,batch,m,n,k,fam", [
+    (mm.MM_F16, 32, 64, 512, 64, "gemm"),         # 4 rounds of 1-per-CU blocks
+    (mm.MM_F16, 32, 4, 512, 128, "gemm"),         # 2 rounds, 256-byte rows
+    (mm.MM_F16, 32, 4, 512, 256, "gemv_wide"),    # 2 rounds, 512-byte rows
+    (mm.MM_F16, 32, 4, 4096, 256, "gemm"),        # 11 rounds, 512-byte rows
+    (mm.MM_F16, 32, 4, 4096, 512, "gemv_wide"),   # 11 rounds, 1 KiB rows
+    (mm.MM_BF16, 3, 40, 4096, 64, "gemv_wide"),   # 3 rounds, three fragments
+    (mm.MM_BF16, 4, 40, 4096, 64, "gemm"),        # 4 rounds, three fragments
+    (mm.MM_F32, 16, 20, 2048, 256, "gemv_wide"),  # 4 rounds of 2-per-CU blocks, 1 KiB rows
+    (mm.MM_F32, 16, 20, 2048, 128, "gemm"),       # same, 512-byte rows
+    (mm.MM_F16, 32, 512, 4, 128, "gemm"),         # mirrored: few rows in B
+    (mm.MM_F16, 32, 512, 4, 256, "gemv_wide"),
+    (mm.MM_F16, 1, 64, 11008, 4096, "gemv_wide"),  # 3 rounds, four fragments
+])
+def test_dispatch_skinny_rounds_rule(dt, batch, m, n, k, fam):
+    """The skinny route's rounds rule (mm.h, mm_gemm): when its blocks do not
+    all fit on the GPU at once, the dispatch keeps it only for long rows (one
+    or two activation fragments) or few rounds (three or four), else the
+    tiled GEMM, as the short-k calibration measured."""
+    assert _dispatch_family(mm.load(), dt, batch, m, n, k) == fam
+
+
 def test_capabilities_without_gpu():
     import torch
     if torch.cuda.is_available():

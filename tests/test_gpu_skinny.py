@@ -134,6 +134,20 @@ def test_skinny_broadcast(dt, which):
     assert rec.route == mm.MM_ROUTE_GEMV_WIDE
 
 
+@pytest.mark.parametrize("dt,batch,m,n,k", [
+    (wl.F16, 32, 64, 512, 64), (wl.F16, 32, 4, 512, 256), (wl.F16, 32, 4, 512, 128),
+    (wl.BF16, 3, 40, 4096, 64), (wl.BF16, 4, 40, 4096, 64),
+    (wl.F32, 16, 20, 2048, 256), (wl.F32, 16, 20, 2048, 128)])
+def test_skinny_rounds_rule_both_sides(dt, batch, m, n, k):
+    """Batched shapes on both sides of the skinny route's rounds rule (its
+    blocks in more than one round: kept for long rows or few rounds, else
+    the tiled GEMM): the receipt names the route the rule picks, and every
+    output matches the oracle."""
+    _say(f"skinny rounds rule {wl.DTYPE_NAMES[dt]} batch={batch} m={m} n={n} k={k}")
+    case = wl.random_gemm_case(39 + k, dt, batch, m, n, k, False, True)
+    _run(case, False, f"rounds {batch}x{m}x{n}x{k}")
+
+
 @pytest.mark.parametrize("dt", [wl.F16, wl.BF16])
 def test_layouts_the_route_declines(dt):
     """Not a whole number of 16-byte chunks (k = 36), an offset off the
