@@ -1042,24 +1042,31 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, Launched* L) {
     }
     constexpr int PNW = 64;  // B tile rows of the panel kernel
     const int64_t panel_items = (a.m / 64) * a.batch;
+    const int64_t ptiles = a.n / PNW;
+    const int64_t split64 = ptiles < 32 ? ptiles : 32;  // most blocks per 64-row panel
     if (vec && !a.ta && a.tb && (a.k == 32 || a.k == 64 || a.k == 128) && a.m % 64 == 0 &&
         a.n % PNW == 0 && a.beta == 0.f && a.ldc % 8 == 0 && aligned16(a.C) && a.sc % 8 == 0 &&
-        panel_items >= 128 && panel_items < (1ll << 28) && a.m * a.ldc < (1ll << 30)) {
-        // Batched short-K NT products: A panel resident, B tiles streamed, the
-        // tiles of a panel split over up to four blocks. 128-row panels (one
-        // 8-wave block per CU, 116 KiB of LDS at k = 128) read each B tile
-        // once per 128 rows; they are taken for k = 64 or 128 when they can
-        // still fill every CU. Otherwise 64-row panels (two 4-wave blocks per
-        // CU, 74 KiB each at k = 128), split so that at least 512 blocks run.
+        (panel_items >= 128 || panel_items * split64 >= 512) && panel_items < (1ll << 28) &&
+        a.m * a.ldc < (1ll << 30)) {
+        // Short-K NT products: A panel resident, B tiles streamed, the tiles
+        // of a panel split over several blocks, so that few panels still
+        // fill the GPU. 128-row panels (one 8-wave block per CU, 116 KiB of
+        // LDS at k = 128) read each B tile once per 128 rows; they are taken
+        // for k = 64 or 128 when they can fill every CU with up to 4 blocks
+        // per panel, or, for panels of more than 8 tiles, up to 16 blocks of
+        // at least two tiles each. Otherwise 64-row panels (two 4-wave blocks
+        // per CU, 74 KiB each at k = 128), split over up to 32 blocks so that
+        // at least 512 blocks run.
         static_assert(2 * panel_lds_bytes(16, PNW, 64) <= 160 * 1024, "two blocks per CU");
         static_assert(panel_lds_bytes(16, PNW, 128) <= 160 * 1024, "one block per CU");
         const int S = (int)(a.k / 8);
-        const int64_t tiles = a.n / PNW;
-        const int64_t max_split = tiles < 4 ? tiles : 4;
-        const bool tall = S >= 8 && a.m % 128 == 0 && (a.m / 128) * a.batch * max_split >= 256;
+        const int64_t tiles = ptiles;
+        const int64_t split128 = tiles <= 8 ? (tiles < 4 ? tiles : 4) : (tiles / 2 < 16 ? tiles / 2 : 16);
+        const bool tall = S >= 8 && a.m % 128 == 0 && (a.m / 128) * a.batch * split128 >= 256;
         const int pm = tall ? 128 : 64;
         const int64_t items0 = (a.m / pm) * a.batch;
         const int64_t want = tall ? 256 : 512;
+        const int64_t max_split = tall ? split128 : split64;
         int nsplit = (int)((want + items0 - 1) / items0);
         if (nsplit > max_split) nsplit = (int)max_split;
         const void* fn = nullptr;

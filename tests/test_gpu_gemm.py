@@ -317,16 +317,27 @@ def test_large_tile_route_full_compare(dt, seed):
 
 def panel_variant(b, m, n, k):
     """(split, panel rows) the panel kernel takes: 128-row panels for k = 64
-    or 128 when m % 128 == 0 and (m / 128) * b * min(4, n / 64) reaches 256
-    blocks, split to reach 256 blocks; else 64-row panels split to reach 512
-    blocks; the split is at most 4 and at most the n / 64 tiles."""
+    or 128 when m % 128 == 0 and (m / 128) * b * most128 reaches 256 blocks,
+    split to reach 256 blocks, where most128 is min(4, tiles) for up to 8
+    tiles of 64 columns and min(16, tiles / 2) beyond; else 64-row panels
+    split to reach 512 blocks, at most min(32, tiles) ways."""
     tiles = n // 64
-    most = min(4, tiles)
-    tall = k >= 64 and m % 128 == 0 and (m // 128) * b * most >= 256
+    most128 = min(4, tiles) if tiles <= 8 else min(16, tiles // 2)
+    tall = k >= 64 and m % 128 == 0 and (m // 128) * b * most128 >= 256
     pm = 128 if tall else 64
     items = (m // pm) * b
     want = 256 if tall else 512
+    most = most128 if tall else min(32, tiles)
     return min(most, -(-want // items)), pm
+
+
+def panel_taken(b, m, n, k):
+    """Whether the panel kernel takes an aligned NT short-K product: at least
+    128 panels of 64 rows, or few enough that up to min(32, n / 64) blocks
+    each still reach 512."""
+    items = (m // 64) * b
+    return (k in (32, 64, 128) and m % 64 == 0 and n % 64 == 0
+            and (items >= 128 or items * min(32, n // 64) >= 512))
 
 
 def check_panel_variant(rec, b, m, n, k):
@@ -343,7 +354,7 @@ def test_panel_kernel(dt, k, n):
     """Batched short-K NT products on the panel kernel (A panel resident in
     LDS, B tiles of 64 rows streamed through three stages (64-row panels) or
     four (128-row panels), output stores written through, a panel's tiles
-    split over up to four blocks): every admissible k, 64-row panels (n =
+    split over several blocks): every admissible k, 64-row panels (n =
     128, 192, and every n at k = 32) and 128-row panels (n >= 384 at k = 64
     and 128), 1 to 6 tiles per block (every pipeline depth), all outputs
     against the oracle; the receipt names the split and the panel height."""
@@ -354,6 +365,25 @@ def test_panel_kernel(dt, k, n):
     split, pm = check_panel_variant(rec, b, m, n, k)
     assert pm == (128 if k >= 64 and n >= 384 else 64), pm
     assert split == {128: 2, 192: 3}.get(n, 4), split
+
+
+@pytest.mark.parametrize("dt,b,m,n,k", [
+    (wl.F16, 96, 64, 512, 64), (wl.BF16, 8, 960, 512, 64), (wl.F16, 8, 192, 2048, 128),
+    (wl.BF16, 4, 512, 4096, 128), (wl.F16, 16, 128, 1024, 64), (wl.F16, 64, 64, 1024, 32),
+    (wl.BF16, 2, 512, 8192, 128), (wl.F16, 16, 128, 128, 64)])
+def test_panel_kernel_few_panels(dt, b, m, n, k):
+    """Fewer than 128 panels of 64 rows: each panel's B tiles split over up
+    to 32 blocks (64-row panels) or 16 blocks of two tiles or more (128-row
+    panels) so that the GPU still fills; shapes too small for that stay on
+    the tiled kernel. All outputs against the oracle; the receipt names the
+    kernel and, on the panel kernel, the split and the panel height."""
+    _say(f"panel NT few panels dt={wl.DTYPE_NAMES[dt]} b={b} m={m} n={n} k={k}")
+    case = wl.random_gemm_case(50 + k + b, dt, b, m, n, k, False, True)
+    rec = check_gemm(case, what=f"few panels {b}x{m}x{n}x{k}")
+    if panel_taken(b, m, n, k):
+        check_panel_variant(rec, b, m, n, k)
+    else:
+        assert rec.kernel == mm.MM_KERNEL_GEMM_TILED, rec.kernel
 
 
 @pytest.mark.parametrize("k", [64, 128])
@@ -392,11 +422,15 @@ def test_panel_kernel_padded_offsets_ramp_exact(dt):
 
 
 @pytest.mark.parametrize("k", [128, 192, 320])
-def test_large_shape_other_k_takes_tiled_kernel(k):
-    """k below 256 or not a multiple of 128: the 128 x 128 kernel, same results."""
-    _say(f"NT f16 m=4096 n=8192 k={k} (tiled kernel)")
+def test_large_shape_other_k(k):
+    """k below 256 or not a multiple of 128, so not the 256 x 256 kernel: at
+    k = 128 the panel kernel (32 panels of 128 rows, each split over 8
+    blocks), at 192 and 320 the 128 x 128 kernel; same results."""
+    _say(f"NT f16 m=4096 n=8192 k={k}")
     case = wl.random_gemm_case(43, wl.F16, 1, 4096, 8192, k, False, True)
-    _sampled_check(case, 2048, 6, kernel=mm.MM_KERNEL_GEMM_TILED)
+    want = mm.MM_KERNEL_GEMM_PANEL if panel_taken(1, 4096, 8192, k) else mm.MM_KERNEL_GEMM_TILED
+    assert (want == mm.MM_KERNEL_GEMM_PANEL) == (k == 128)
+    _sampled_check(case, 2048, 6, kernel=want)
 
 
 @pytest.mark.parametrize("dt", DTYPES)
