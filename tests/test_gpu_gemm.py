@@ -256,7 +256,7 @@ def _sampled_check(case, n_samples, seed, exact=False, kernel=None):
 @pytest.mark.parametrize("dt", [wl.F16, wl.BF16])
 @pytest.mark.parametrize("k", [256, 640])
 def test_large_tile_route(dt, k):
-    """m, n multiples of 256 with >= 512 tiles, k % 128 == 0, k >= 256: the
+    """m, n multiples of 256 with >= 128 tiles, k % 128 == 0, k >= 256: the
     256 x 256 MFMA kernel (k = 256: first and last rounds only; k = 640: the
     steady loop runs too)."""
     _say(f"large-tile NT dt={wl.DTYPE_NAMES[dt]} m=4096 n=8192 k={k}")
@@ -271,6 +271,21 @@ def test_large_tile_route_ramp_exact():
     b = wl.ramp(n * k, 2).reshape(1, n, k)
     case = wl.make_gemm_case(wl.F16, a, b, False, True)
     _sampled_check(case, 4096, 4, exact=True, kernel=mm.MM_KERNEL_GEMM_LARGE)
+
+
+@pytest.mark.parametrize("dt,b,m,n,k,kernel", [
+    (wl.F16, 1, 2048, 4096, 256, mm.MM_KERNEL_GEMM_LARGE),   # 128 tiles of 256 x 256
+    (wl.BF16, 2, 2048, 2048, 384, mm.MM_KERNEL_GEMM_LARGE),  # 64 per batch item, 128 in all
+    (wl.F16, 1, 1024, 2048, 512, mm.MM_KERNEL_GEMM_TILED),   # 32 tiles: the 128 x 128 kernel
+])
+def test_large_tile_threshold(dt, b, m, n, k, kernel):
+    """The 256 x 256 kernel takes NT products with at least 128 of its tiles
+    over the batch, fewer go to the 128 x 128 kernel; every output against
+    the oracle."""
+    _say(f"large-tile threshold dt={wl.DTYPE_NAMES[dt]} b={b} m={m} n={n} k={k}")
+    case = wl.random_gemm_case(46 + k, dt, b, m, n, k, False, True)
+    rec = check_gemm(case, what=f"threshold {b}x{m}x{n}x{k}")
+    assert rec.kernel == kernel, rec.kernel
 
 
 def test_large_tile_route_batched_padded():
