@@ -78,6 +78,9 @@ def parse():
                     help="only time the CPU cost per eager call (binding, validation, route "
                          "decision and HIP launch) of the library against torch's matmul on "
                          "tiny f16 products, and print one JSON line")
+    ap.add_argument("--gemm-sweep", action="store_true",
+                    help="only time mm_gemm against torch's matmul on f16 NT products of medium "
+                         "size (single and batched), and print one JSON line")
     ap.add_argument("--calibrate-gemm", action="store_true",
                     help="only time the skinny, tiled-GEMM and GEMV routes of x[m,k] . W[n,k]^T "
                          "for m = 2..64 at three (n, k), then the skinny and tiled-GEMM routes at "
@@ -366,6 +369,62 @@ def calibrate_gemm(torch, mm, wl, dev, stream, args):
                       "short_k_rows": short}))
 
 
+def gemm_sweep(torch, mm, wl, dev, stream, args):
+    """mm_gemm against torch's own matmul on f16 NT products C[b] = A[b] .
+    B[b]^T of medium size, where the kernel choice (tile size, panel or
+    tiled kernel) matters most. Operands rotate through copies (1 GiB reuse
+    distance, at most 32 copies); both sides are timed the same way. torch's
+    batched product is given B already transposed (contiguous), never a
+    transposed view."""
+    timer = Timer(torch, stream, True)
+    shapes = [(1, 512, 4096, 4096), (1, 1024, 4096, 4096), (1, 2048, 4096, 4096),
+              (1, 3072, 4096, 4096), (1, 4096, 4096, 4096), (1, 8192, 4096, 4096),
+              (1, 512, 11008, 4096), (1, 2048, 11008, 4096), (1, 512, 4096, 11008),
+              (1, 1024, 1024, 1024), (1, 2048, 2048, 2048), (1, 4096, 4096, 1024),
+              (1, 4096, 8192, 128), (1, 1024, 8192, 32),
+              (4, 1024, 1024, 1024), (8, 512, 512, 2048), (16, 512, 1024, 1024),
+              (4, 2048, 2048, 512), (96, 64, 512, 128)]
+    rows = []
+    for (bt, m, n, k) in shapes:
+        rng = np.random.default_rng(7)
+        a = to_dev_bits(torch, dev, wl.to_storage(0.1 * rng.standard_normal(bt * m * k), wl.F16))
+        b = to_dev_bits(torch, dev, wl.to_storage(0.1 * rng.standard_normal(bt * n * k), wl.F16))
+        n_rot = max(2, min(32, math.ceil(ROTATE_BYTES / (bt * (m + n) * k * 2))))
+        As = [a] + [a.clone() for _ in range(n_rot - 1)]
+        Bs = [b] + [b.clone() for _ in range(n_rot - 1)]
+        c = torch.empty(bt * m * n, dtype=torch.float16, device=dev)
+        d = mm.gemm_desc(wl.F16, m, n, k, batch=bt, trans_b=True, stride_a=m * k,
+                         stride_b=n * k, stride_c=m * n)
+        bufs = [(mm.buf(As[i]), mm.buf(Bs[i])) for i in range(n_rot)]
+        cbuf = mm.buf(c)
+        rec = mm.mm_gemm(d, bufs[0][0], bufs[0][1], cbuf, stream=stream)
+
+        def step(i):
+            mm.mm_gemm(d, bufs[i][0], bufs[i][1], cbuf, stream=stream)
+        t, _ = timer.time(step, n_rot, 4 * n_rot, 3)
+        Ah = [x.view(torch.float16).view(bt, m, k) for x in As]
+        Bt = [x.view(torch.float16).view(bt, n, k).transpose(1, 2).contiguous() for x in Bs]
+        ch = c.view(torch.float16).view(bt, m, n)
+
+        def vstep(i):
+            if bt == 1:
+                torch.mm(Ah[i][0], Bt[i][0], out=ch[0])
+            else:
+                torch.bmm(Ah[i], Bt[i], out=ch)
+        tv, _ = timer.time(vstep, n_rot, 4 * n_rot, 3)
+        flops = 2.0 * bt * m * n * k
+        row = {"batch": bt, "m": m, "n": n, "k": k, "kernel": rec.kernel, "variant": rec.variant,
+               "us": t * 1e3, "tflops": flops / (t * 1e-3) / 1e12, "torch_us": tv * 1e3,
+               "torch_tflops": flops / (tv * 1e-3) / 1e12, "ratio": t / tv}
+        rows.append(row)
+        log(f"b={bt:3d} m={m:5d} n={n:6d} k={k:6d} kernel={rec.kernel:2d}/{rec.variant:<4d} "
+            f"ours {row['us']:8.2f} us {row['tflops']:7.1f} TF  torch {row['torch_us']:8.2f} us "
+            f"{row['torch_tflops']:7.1f} TF  time ratio {row['ratio']:.2f}")
+        del As, Bs, Ah, Bt, a, b, c
+        torch.cuda.empty_cache()
+    print(json.dumps({"sweep": "f16 NT GEMM, mm_gemm vs torch", "rows": rows}))
+
+
 def to_dev_bits(torch, dev, bits):
     bits = np.ascontiguousarray(bits)
     view = {np.dtype(np.float32): None, np.dtype(np.uint16): np.int16,
@@ -580,6 +639,9 @@ def main():
 
     if args.calibrate_id:
         calibrate_id(torch, mm, wl, dev, stream, args)
+        return
+    if args.gemm_sweep:
+        gemm_sweep(torch, mm, wl, dev, stream, args)
         return
     if args.calibrate_gemm:
         calibrate_gemm(torch, mm, wl, dev, stream, args)

@@ -360,13 +360,18 @@ __global__ __launch_bounds__(GThreads) void gemm_mfma_shortk(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Large f16 / bf16 kernel: C = A . B^T with A [m,k] and B [n,k] both
-// K-contiguous, m % 256 == n % 256 == 0, k % 128 == 0, k >= 256, 16-byte aligned.
+// Pipelined f16 / bf16 kernel: C = A . B^T with A [m,k] and B [n,k] both
+// K-contiguous, k % 128 == 0, k >= 256, 16-byte aligned, m and n multiples of
+// the tile edge 32 TF (TF = 8: 256; TF = 4: 128).
 //
-// Block = 4 waves (one per SIMD), tile 256 x 256, each wave 128 x 128 as 8 x 8
-// fragments of 16 x 16 (v_mfma_f32_16x16x32, 64 accumulators of 4 f32 in
-// AGPRs). A 128 x 128 wave tile halves the LDS fragment reads per MFMA
-// compared with 128 x 64.
+// Block = 4 waves, each 16 TF x 16 TF as TF x TF fragments of 16 x 16
+// (v_mfma_f32_16x16x32). TF = 8 is the large-product form: one block per CU,
+// one wave per SIMD with 64 accumulators of 4 f32 in AGPRs; a 128 x 128 wave
+// tile halves the LDS fragment reads per MFMA compared with 128 x 64. TF = 4
+// gives four times the tiles for products too small to fill the GPU with
+// 256 x 256 ones, at two blocks per CU. The description below is for TF = 8;
+// TF = 4 halves every tile dimension, the DMA instructions per wave and the
+// MFMAs per group.
 //
 // Operands go from global memory straight into LDS (buffer_load ... lds, no
 // VGPR staging) in k-tiles of 32: four LDS stages of 32 KiB (A 16 KiB, B 16 KiB).
@@ -393,15 +398,21 @@ __global__ __launch_bounds__(GThreads) void gemm_mfma_shortk(GemmArgs a) {
 // (blockIdx % 8) taking a contiguous run, so resident blocks on one XCD share
 // A and B panels in its L2.
 // ---------------------------------------------------------------------------
-constexpr int LBM = 256, LBN = 256, LBK = 32, LSTAGES = 4;
+constexpr int LBK = 32, LSTAGES = 4;
 constexpr int LThreads = 256;
-constexpr int LSTAGE_H = (LBM + LBN) * LBK;   // halves per stage
 constexpr int LCPR = LBK / 8;                  // 16-byte chunks per tile row
 constexpr int LRPI = 64 / LCPR;                // tile rows per 1 KiB DMA instruction
-constexpr int LIPW = 64 / LRPI;                // DMA instructions per wave per operand per tile
-constexpr int LLPS = 2 * LIPW;                 // DMA instructions per wave per tile
 constexpr int LGM = 4;                         // tile-rows per group
-constexpr size_t kLargeLds = (size_t)LSTAGES * LSTAGE_H * sizeof(uint16_t);
+// Shape of the kernel with TF x TF fragments per wave: 16 TF x 16 TF wave
+// tiles, 32 TF x 32 TF block tiles (256 for TF = 8, 128 for TF = 4).
+template <int TF>
+struct LTile {
+    static constexpr int BM = 32 * TF;              // block tile edge
+    static constexpr int STAGE_H = 2 * BM * LBK;    // halves per stage (A then B)
+    static constexpr int IPW = BM / 4 / LRPI;       // DMA instructions per wave per operand per tile
+    static constexpr int LPS = 2 * IPW;             // DMA instructions per wave per tile
+    static constexpr size_t LDS = (size_t)LSTAGES * STAGE_H * sizeof(uint16_t);
+};
 
 template <int... I, class F>
 __device__ __forceinline__ void static_for(std::integer_sequence<int, I...>, F&& f) {
@@ -647,13 +658,20 @@ __global__ __launch_bounds__(PMT * 4, 1) void gemm_nt_panel(GemmArgs a, int nspl
     }
 }
 
-template <class T>
-__global__ __launch_bounds__(LThreads, 1) void gemm_mfma_large(GemmArgs a) {
+template <class T, int TF>
+__global__ __launch_bounds__(LThreads, TF == 8 ? 1 : 2) void gemm_mfma_large(GemmArgs a) {
+    using L = LTile<TF>;
+    constexpr int BM = L::BM, SH = L::STAGE_H, IPW = L::IPW, LLPS = L::LPS;
+    constexpr int HF = TF / 2;        // A fragments per half of the wave tile
+    constexpr int WT = 16 * TF;       // wave tile edge
+    constexpr int RPW = BM / 4;       // tile rows each wave moves per operand and k-tile
+    constexpr int NR = IPW;           // DMA instructions per half k-tile = MFMA runs per group
+    constexpr int MPR = HF * TF / NR; // MFMAs per run
     extern __shared__ __attribute__((aligned(1024))) uint16_t lds[];  // [stage][A | B][row][32]
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = w >> 1, wn = w & 1;
-    const int64_t tiles_m = a.m / LBM, tiles_n = a.n / LBN;
+    const int64_t tiles_m = a.m / BM, tiles_n = a.n / BM;
     const int64_t ntiles = tiles_m * tiles_n;
 
     // XCD-aware grouped tile order.
@@ -666,16 +684,16 @@ __global__ __launch_bounds__(LThreads, 1) void gemm_mfma_large(GemmArgs a) {
     const int64_t gsize = tiles_m - first_m < LGM ? tiles_m - first_m : LGM;
     const int64_t tm = first_m + (t % (LGM * tiles_n)) % gsize;
     const int64_t tn = (t % (LGM * tiles_n)) / gsize;
-    const int64_t m0 = tm * LBM, n0 = tn * LBN;
+    const int64_t m0 = tm * BM, n0 = tn * BM;
     const int nk = (int)(a.k / LBK);  // a multiple of LSTAGES, at least 2 * LSTAGES
     const int lda = (int)a.lda, ldb = (int)a.ldb;
 
-    // DMA lane mapping: instruction j of a wave covers tile rows w*64 + j*16 +
+    // DMA lane mapping: instruction j of a wave covers tile rows w*RPW + j*16 +
     // lane/4; lane writes LDS slot lane%4 of its row with the chunk that the
     // swizzle puts there. The row's swizzle does not depend on j.
     const int chunk = (lane % LCPR) ^ lswz(lane / LCPR);
-    const int voa = ((w * 64 + lane / LCPR) * lda + chunk * 8) * 2;
-    const int vob = ((w * 64 + lane / LCPR) * ldb + chunk * 8) * 2;
+    const int voa = ((w * RPW + lane / LCPR) * lda + chunk * 8) * 2;
+    const int vob = ((w * RPW + lane / LCPR) * ldb + chunk * 8) * 2;
     // Fragment reads: lane -> row lane%16 of a 16-row slab, chunk lane/16.
     const int lr = lane & 15, lq = lane >> 4;
     const int foff = lr * LBK + ((lq ^ lswz(lr)) << 3);
@@ -684,57 +702,57 @@ __global__ __launch_bounds__(LThreads, 1) void gemm_mfma_large(GemmArgs a) {
         const uint16_t* A = reinterpret_cast<const uint16_t*>(a.A) + b * a.sa + m0 * a.lda;
         const uint16_t* B = reinterpret_cast<const uint16_t*>(a.B) + b * a.sb + n0 * a.ldb;
         const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(A), (short)0, LBM * lda * 2, 0x00020000);
+            const_cast<uint16_t*>(A), (short)0, BM * lda * 2, 0x00020000);
         const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(B), (short)0, LBN * ldb * 2, 0x00020000);
+            const_cast<uint16_t*>(B), (short)0, BM * ldb * 2, 0x00020000);
 
-        // Half p (instructions 2p, 2p+1 of each operand) of k-tile kt into a stage.
+        // Half p (instructions IPW/2 * p .. of each operand) of k-tile kt into a stage.
         auto dma_half = [&](int stage, int kt, int p) {
-            uint16_t* sa = lds + stage * LSTAGE_H + w * 64 * LBK;
-            uint16_t* sb = sa + LBM * LBK;
+            uint16_t* sa = lds + stage * SH + w * RPW * LBK;
+            uint16_t* sb = sa + BM * LBK;
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                const int j = 2 * p + jj;
+            for (int jj = 0; jj < IPW / 2; ++jj) {
+                const int j = IPW / 2 * p + jj;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, MM_LDS(sa + j * LRPI * LBK), 16, voa,
                                                          (j * LRPI * lda + kt * LBK) * 2, 0, 0);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, MM_LDS(sb + j * LRPI * LBK), 16, vob,
                                                          (j * LRPI * ldb + kt * LBK) * 2, 0, 0);
             }
         };
-        f32x4 acc[8][8];
+        f32x4 acc[TF][TF];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < TF; ++i)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // A fragments of half hh (wave rows hh*64 + 16i) / all 8 B fragments of a stage.
-        auto rda = [&](int stage, int hh, u32x4 (&fa)[4]) {
-            const uint16_t* sa = lds + stage * LSTAGE_H + (wm * 128 + hh * 64) * LBK;
+            for (int j = 0; j < TF; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // A fragments of half hh (wave rows hh*WT/2 + 16i) / all TF B fragments of a stage.
+        auto rda = [&](int stage, int hh, u32x4 (&fa)[HF]) {
+            const uint16_t* sa = lds + stage * SH + (wm * WT + hh * (WT / 2)) * LBK;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const u32x4*>(sa + i * 16 * LBK + foff);
+            for (int i = 0; i < HF; ++i) fa[i] = *reinterpret_cast<const u32x4*>(sa + i * 16 * LBK + foff);
         };
-        auto rdb = [&](int stage, u32x4 (&fb)[8]) {
-            const uint16_t* sb = lds + stage * LSTAGE_H + LBM * LBK + wn * 128 * LBK;
+        auto rdb = [&](int stage, u32x4 (&fb)[TF]) {
+            const uint16_t* sb = lds + stage * SH + BM * LBK + wn * WT * LBK;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) fb[j] = *reinterpret_cast<const u32x4*>(sb + j * 16 * LBK + foff);
+            for (int j = 0; j < TF; ++j) fb[j] = *reinterpret_cast<const u32x4*>(sb + j * 16 * LBK + foff);
         };
         // D[n][m] = sum_k B(n,k) A(m,k): the lane's four consecutive values run along n.
-        auto mm = [&](int hh, const u32x4 (&fa)[4], const u32x4 (&fb)[8]) {
+        auto mm = [&](int hh, const u32x4 (&fa)[HF], const u32x4 (&fb)[TF]) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < HF; ++i)
 #pragma unroll
-                for (int j = 0; j < 8; ++j) acc[hh * 4 + i][j] = mfma16<T>(fb[j], fa[i], acc[hh * 4 + i][j]);
+                for (int j = 0; j < TF; ++j) acc[hh * HF + i][j] = mfma16<T>(fb[j], fa[i], acc[hh * HF + i][j]);
         };
-        // Scheduling of one group: its NDS fragment reads first, then 32 MFMAs
-        // with a DMA instruction after every eighth when ndma == 4.
+        // Scheduling of one group: its NDS fragment reads first, then NR runs
+        // of MPR MFMAs, each followed by one DMA instruction when ndma == NR.
         auto weave = [&](auto NDS, int ndma) {
             __builtin_amdgcn_sched_group_barrier(0x100, decltype(NDS)::value, 0);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+            for (int q = 0; q < NR; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, MPR, 0);
                 if (q < ndma) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
             }
         };
-        u32x4 fa0[4], fa1[4], fb0[8], fb1[8];
+        u32x4 fa0[HF], fa1[HF], fb0[TF], fb1[TF];
         // One k-tile. S_: stage (kt % 4), whose B fragments sit in fb0 (even
         // stage) or fb1; P1: finish tile kt+3 (second half); NEXT: tile kt+1
         // exists; DMA0: start tile kt+4; VM: DMA instructions allowed in
@@ -746,7 +764,7 @@ __global__ __launch_bounds__(LThreads, 1) void gemm_mfma_large(GemmArgs a) {
             rda(s, 1, fa1);
             if constexpr (decltype(P1)::value) dma_half((s + 3) % LSTAGES, kt + 3, 1);
             mm(0, fa0, fb);
-            weave(ic<4>{}, decltype(P1)::value ? 4 : 0);
+            weave(ic<HF>{}, decltype(P1)::value ? NR : 0);
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (decltype(NEXT)::value) {
                 __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(decltype(VM)::value));
@@ -756,7 +774,7 @@ __global__ __launch_bounds__(LThreads, 1) void gemm_mfma_large(GemmArgs a) {
                 if constexpr (decltype(DMA0)::value) dma_half(s, kt + LSTAGES, 0);
             }
             mm(1, fa1, fb);
-            weave(ic<decltype(NEXT)::value ? 12 : 0>{}, decltype(DMA0)::value ? 4 : 0);
+            weave(ic<decltype(NEXT)::value ? HF + TF : 0>{}, decltype(DMA0)::value ? NR : 0);
             __builtin_amdgcn_sched_barrier(0);
         };
 
@@ -792,11 +810,11 @@ __global__ __launch_bounds__(LThreads, 1) void gemm_mfma_large(GemmArgs a) {
         // Lane holds C[m = 16i-slab base + lane%16][n = 16j-slab base + 4 (lane/16) + q].
         uint16_t* C = reinterpret_cast<uint16_t*>(a.C) + b * a.sc;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int64_t gm = m0 + wm * 128 + i * 16 + lr;
+        for (int i = 0; i < TF; ++i) {
+            const int64_t gm = m0 + wm * WT + i * 16 + lr;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int64_t gn = n0 + wn * 128 + j * 16 + lq * 4;
+            for (int j = 0; j < TF; ++j) {
+                const int64_t gn = n0 + wn * WT + j * 16 + lq * 4;
                 uint16_t* dst = C + gm * a.ldc + gn;
                 if (a.beta == 0.f) {
                     u32x2 v;
@@ -1028,18 +1046,29 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, Launched* L) {
     const int64_t span_b = a.tb ? (a.n - 1) * a.ldb + a.k : (a.k - 1) * a.ldb + a.n;
     const bool vec = aligned16(a.A) && aligned16(a.B) && a.lda % 8 == 0 && a.ldb % 8 == 0 &&
                      a.sa % 8 == 0 && a.sb % 8 == 0 && span_a < (1ll << 30) && span_b < (1ll << 30);
-    const int64_t big_tiles = (a.m / LBM) * (a.n / LBN);
-    if (vec && !a.ta && a.tb && a.m % LBM == 0 && a.n % LBN == 0 &&
-        a.k % (LSTAGES * LBK) == 0 && a.k >= 2 * LSTAGES * LBK && big_tiles * a.batch >= 128 &&
-        a.lda < (1 << 22) && a.ldb < (1 << 22) && a.ldc % 4 == 0 &&
-        (reinterpret_cast<uintptr_t>(a.C) & 7) == 0 && a.sc % 4 == 0) {
-        // Large NT products: 256 x 256 tiles, at least 128 of them over the batch
-        // (measured: with fewer, the 128 x 128 tiles were as fast or faster).
-        const void* fn = a.dtype == 1 ? (const void*)&gemm_mfma_large<TF16>
-                                      : (const void*)&gemm_mfma_large<TBF16>;
-        const unsigned grid = (unsigned)(((big_tiles + 7) / 8) * 8);
+    // NT products on the DMA-pipelined MFMA kernel: 256 x 256 tiles when at
+    // least 192 of them cover the batch, else 128 x 128 tiles of the same
+    // pipeline (two blocks per CU). Measured on MI355X: 256 x 256 from 192
+    // tiles on, 128 x 128 at 128 tiles and below, and 128 x 128 ahead of the
+    // 128 x 128 register-staged kernel at every measured shape.
+    const bool pipelined = vec && !a.ta && a.tb && a.k % (LSTAGES * LBK) == 0 &&
+                           a.k >= 2 * LSTAGES * LBK && a.lda < (1 << 22) && a.ldb < (1 << 22) &&
+                           a.ldc % 4 == 0 && (reinterpret_cast<uintptr_t>(a.C) & 7) == 0 && a.sc % 4 == 0;
+    const int64_t big_tiles = (a.m / LTile<8>::BM) * (a.n / LTile<8>::BM);
+    const bool big = pipelined && a.m % LTile<8>::BM == 0 && a.n % LTile<8>::BM == 0 &&
+                     big_tiles * a.batch >= 192;
+    const bool mid = !big && pipelined && a.m % LTile<4>::BM == 0 && a.n % LTile<4>::BM == 0;
+    if (big || mid) {
+        const int64_t tiles = big ? big_tiles : (a.m / LTile<4>::BM) * (a.n / LTile<4>::BM);
+        const void* fn = big ? (a.dtype == 1 ? (const void*)&gemm_mfma_large<TF16, 8>
+                                             : (const void*)&gemm_mfma_large<TBF16, 8>)
+                             : (a.dtype == 1 ? (const void*)&gemm_mfma_large<TF16, 4>
+                                             : (const void*)&gemm_mfma_large<TBF16, 4>);
+        const unsigned grid = (unsigned)(((tiles + 7) / 8) * 8);
         L->kernel = MM_KERNEL_GEMM_LARGE;
-        return hipLaunchKernel(fn, dim3(grid, gy), dim3(LThreads), args, kLargeLds, s);
+        L->variant = big ? LTile<8>::BM : LTile<4>::BM;
+        return hipLaunchKernel(fn, dim3(grid, gy), dim3(LThreads), args,
+                               big ? LTile<8>::LDS : LTile<4>::LDS, s);
     }
     constexpr int PNW = 64;  // B tile rows of the panel kernel
     const int64_t panel_items = (a.m / 64) * a.batch;

@@ -226,13 +226,15 @@ def test_large_k_many_tiles_f16():
     check_gemm(case, what="large k")
 
 
-def _sampled_check(case, n_samples, seed, exact=False, kernel=None):
+def _sampled_check(case, n_samples, seed, exact=False, kernel=None, variant=None):
     from gpu_util import GemmRun, assert_close
     import oracle
     run = GemmRun(case)
     rec = run.run()
     if kernel is not None:
         assert rec.kernel == kernel, f"kernel {rec.kernel}, expected {kernel}"
+    if variant is not None:
+        assert rec.variant == variant, f"variant {rec.variant}, expected {variant}"
     bits = run.c_bits()
     rng = np.random.default_rng(seed)
     bs = rng.integers(0, case.batch, n_samples)
@@ -261,7 +263,7 @@ def test_large_tile_route(dt, k):
     steady loop runs too)."""
     _say(f"large-tile NT dt={wl.DTYPE_NAMES[dt]} m=4096 n=8192 k={k}")
     case = wl.random_gemm_case(41, dt, 1, 4096, 8192, k, False, True)
-    _sampled_check(case, 4096, 3, kernel=mm.MM_KERNEL_GEMM_LARGE)
+    _sampled_check(case, 4096, 3, kernel=mm.MM_KERNEL_GEMM_LARGE, variant=256)
 
 
 def test_large_tile_route_ramp_exact():
@@ -270,22 +272,69 @@ def test_large_tile_route_ramp_exact():
     a = wl.ramp(m * k, 1).reshape(1, m, k)
     b = wl.ramp(n * k, 2).reshape(1, n, k)
     case = wl.make_gemm_case(wl.F16, a, b, False, True)
-    _sampled_check(case, 4096, 4, exact=True, kernel=mm.MM_KERNEL_GEMM_LARGE)
+    _sampled_check(case, 4096, 4, exact=True, kernel=mm.MM_KERNEL_GEMM_LARGE, variant=256)
 
 
-@pytest.mark.parametrize("dt,b,m,n,k,kernel", [
-    (wl.F16, 1, 2048, 4096, 256, mm.MM_KERNEL_GEMM_LARGE),   # 128 tiles of 256 x 256
-    (wl.BF16, 2, 2048, 2048, 384, mm.MM_KERNEL_GEMM_LARGE),  # 64 per batch item, 128 in all
-    (wl.F16, 1, 1024, 2048, 512, mm.MM_KERNEL_GEMM_TILED),   # 32 tiles: the 128 x 128 kernel
+@pytest.mark.parametrize("dt,b,m,n,k,kernel,variant", [
+    (wl.F16, 1, 3072, 4096, 256, mm.MM_KERNEL_GEMM_LARGE, 256),  # 192 tiles of 256 x 256
+    (wl.F16, 1, 2048, 4096, 256, mm.MM_KERNEL_GEMM_LARGE, 128),  # 128 of them: 128 x 128 tiles
+    (wl.BF16, 2, 2048, 2048, 384, mm.MM_KERNEL_GEMM_LARGE, 128),  # 64 per batch item
+    (wl.F16, 1, 1024, 2048, 512, mm.MM_KERNEL_GEMM_LARGE, 128),
+    (wl.BF16, 3, 384, 640, 256, mm.MM_KERNEL_GEMM_LARGE, 128),   # 15 tiles per batch item
+    (wl.F16, 1, 128, 128, 1024, mm.MM_KERNEL_GEMM_LARGE, 128),   # a single tile
+    (wl.F16, 1, 1000, 2048, 512, mm.MM_KERNEL_GEMM_TILED, 0),    # m not a multiple of 128
 ])
-def test_large_tile_threshold(dt, b, m, n, k, kernel):
-    """The 256 x 256 kernel takes NT products with at least 128 of its tiles
-    over the batch, fewer go to the 128 x 128 kernel; every output against
-    the oracle."""
+def test_large_tile_threshold(dt, b, m, n, k, kernel, variant):
+    """The pipelined kernel takes NT products whose m and n are multiples of
+    its tile edge: 256 x 256 tiles when at least 192 of them cover the batch,
+    else 128 x 128 tiles; other shapes go to the 128 x 128 register-staged
+    kernel. Every output against the oracle; the receipt names the tile edge."""
     _say(f"large-tile threshold dt={wl.DTYPE_NAMES[dt]} b={b} m={m} n={n} k={k}")
     case = wl.random_gemm_case(46 + k, dt, b, m, n, k, False, True)
     rec = check_gemm(case, what=f"threshold {b}x{m}x{n}x{k}")
-    assert rec.kernel == kernel, rec.kernel
+    assert (rec.kernel, rec.variant) == (kernel, variant), (rec.kernel, rec.variant)
+
+
+@pytest.mark.parametrize("dt", [wl.F16, wl.BF16])
+def test_mid_tile_ramp_exact(dt):
+    """128 x 128 tiles of the pipelined kernel (k = 1024: the steady loop
+    runs), ramp inputs, every output bit for bit."""
+    m, n, k = 384, 512, 1024
+    _say(f"mid-tile NT ramp exact dt={wl.DTYPE_NAMES[dt]} m={m} n={n} k={k}")
+    a = wl.ramp(m * k, 1).reshape(1, m, k)
+    b = wl.ramp(n * k, 2).reshape(1, n, k)
+    rec = check_gemm(wl.make_gemm_case(dt, a, b, False, True), exact=True, what="mid ramp")
+    assert (rec.kernel, rec.variant) == (mm.MM_KERNEL_GEMM_LARGE, 128), (rec.kernel, rec.variant)
+
+
+@pytest.mark.parametrize("dt", [wl.F16, wl.BF16])
+def test_mid_tile_batched_padded_offsets(dt):
+    """128 x 128 tiles with padded leading dimensions, batch strides with
+    gaps and element offsets on every operand; every output."""
+    _say(f"mid-tile NT batched padded dt={wl.DTYPE_NAMES[dt]}")
+    rng = np.random.default_rng(12)
+    b_, m, n, k = 3, 256, 640, 384
+    a = rng.standard_normal((b_, m, k))
+    bb = rng.standard_normal((b_, n, k)) / np.sqrt(k)
+    case = wl.make_gemm_case(dt, a, bb, False, True, lda=k + 64, ldb=k + 8, ldc=n + 4,
+                             off_a=8, off_b=16, off_c=4, stride_a=m * (k + 64) + 64,
+                             stride_b=n * (k + 8) + 8, stride_c=m * (n + 4) + 12)
+    rec = check_gemm(case, what="mid batched padded")
+    assert (rec.kernel, rec.variant) == (mm.MM_KERNEL_GEMM_LARGE, 128), (rec.kernel, rec.variant)
+
+
+def test_mid_tile_broadcast_b():
+    """128 x 128 tiles, one B for a batch of four (batch stride 0)."""
+    _say("mid-tile NT B broadcast f16 b=4 m=512 n=256 k=512")
+    rng = np.random.default_rng(13)
+    b_, m, n, k = 4, 512, 256, 512
+    a = rng.uniform(-1, 1, (b_, m, k))
+    b1 = rng.uniform(-1, 1, (1, n, k)) / np.sqrt(k)
+    case = wl.make_gemm_case(wl.F16, a, np.broadcast_to(b1, (b_, n, k)), False, True,
+                             broadcast_b=True)
+    assert case.stride_b == 0
+    rec = check_gemm(case, what="mid broadcast")
+    assert (rec.kernel, rec.variant) == (mm.MM_KERNEL_GEMM_LARGE, 128), (rec.kernel, rec.variant)
 
 
 def test_large_tile_route_batched_padded():
@@ -295,7 +344,7 @@ def test_large_tile_route_batched_padded():
     a = rng.standard_normal((b_, m, k))
     bb = rng.standard_normal((b_, n, k)) / np.sqrt(k)
     case = wl.make_gemm_case(wl.BF16, a, bb, False, True, lda=k + 64, ldb=k + 8, ldc=n + 4)
-    _sampled_check(case, 4096, 5, kernel=mm.MM_KERNEL_GEMM_LARGE)
+    _sampled_check(case, 4096, 5, kernel=mm.MM_KERNEL_GEMM_LARGE, variant=256)
 
 
 def test_large_tile_route_broadcast_b():
@@ -309,7 +358,7 @@ def test_large_tile_route_broadcast_b():
     case = wl.make_gemm_case(wl.F16, a, np.broadcast_to(b1, (b_, n, k)), False, True,
                              broadcast_b=True, off_a=8, off_b=16, off_c=4)
     assert case.stride_b == 0
-    _sampled_check(case, 4096, 7, kernel=mm.MM_KERNEL_GEMM_LARGE)
+    _sampled_check(case, 4096, 7, kernel=mm.MM_KERNEL_GEMM_LARGE, variant=256)
 
 
 @pytest.mark.parametrize("dt,seed", [(wl.F16, 44), (wl.BF16, 45)])
@@ -321,7 +370,7 @@ def test_large_tile_route_full_compare(dt, seed):
     case = wl.random_gemm_case(seed, dt, 1, 4096, 8192, 256, False, True, dist="uniform")
     run = GemmRun(case)
     rec = run.run()
-    assert rec.kernel == mm.MM_KERNEL_GEMM_LARGE, rec.kernel
+    assert rec.kernel == mm.MM_KERNEL_GEMM_LARGE and rec.variant == 256, (rec.kernel, rec.variant)
     bits = run.c_bits()
     got, mask = run.logical_c(bits)
     run.check_untouched(bits, mask)
