@@ -370,12 +370,13 @@ def calibrate_gemm(torch, mm, wl, dev, stream, args):
 
 
 def gemm_sweep(torch, mm, wl, dev, stream, args):
-    """mm_gemm against torch's own matmul on f16 NT products C[b] = A[b] .
-    B[b]^T of medium size, where the kernel choice (tile size, panel or
-    tiled kernel) matters most. Operands rotate through copies (1 GiB reuse
-    distance, at most 32 copies); both sides are timed the same way. torch's
-    batched product is given B already transposed (contiguous), never a
-    transposed view."""
+    """mm_gemm against torch's own matmul on f16 products C[b] = op(A[b]) .
+    op(B[b]) of medium size, where the kernel choice (tile size, panel or
+    tiled kernel) matters most: NT shapes, then the other transpose layouts.
+    Operands rotate through copies (1 GiB reuse distance, at most 32 copies);
+    both sides are timed the same way. torch gets the same stored operands
+    as transposed views for one batch item; its batched product is given B
+    already in [b, k, n] (contiguous), never a transposed view."""
     timer = Timer(torch, stream, True)
     shapes = [(1, 512, 4096, 4096), (1, 1024, 4096, 4096), (1, 2048, 4096, 4096),
               (1, 3072, 4096, 4096), (1, 4096, 4096, 4096), (1, 8192, 4096, 4096),
@@ -384,8 +385,12 @@ def gemm_sweep(torch, mm, wl, dev, stream, args):
               (1, 4096, 8192, 128), (1, 1024, 8192, 32),
               (4, 1024, 1024, 1024), (8, 512, 512, 2048), (16, 512, 1024, 1024),
               (4, 2048, 2048, 512), (96, 64, 512, 128)]
+    shapes = [s + (False, True) for s in shapes]
+    for (ta, tb) in ((False, False), (True, True), (True, False)):
+        shapes += [(1, 512, 4096, 4096, ta, tb), (1, 4096, 4096, 4096, ta, tb),
+                   (1, 1024, 1024, 1024, ta, tb), (1, 8192, 8192, 8192, ta, tb)]
     rows = []
-    for (bt, m, n, k) in shapes:
+    for (bt, m, n, k, ta, tb) in shapes:
         rng = np.random.default_rng(7)
         a = to_dev_bits(torch, dev, wl.to_storage(0.1 * rng.standard_normal(bt * m * k), wl.F16))
         b = to_dev_bits(torch, dev, wl.to_storage(0.1 * rng.standard_normal(bt * n * k), wl.F16))
@@ -393,7 +398,7 @@ def gemm_sweep(torch, mm, wl, dev, stream, args):
         As = [a] + [a.clone() for _ in range(n_rot - 1)]
         Bs = [b] + [b.clone() for _ in range(n_rot - 1)]
         c = torch.empty(bt * m * n, dtype=torch.float16, device=dev)
-        d = mm.gemm_desc(wl.F16, m, n, k, batch=bt, trans_b=True, stride_a=m * k,
+        d = mm.gemm_desc(wl.F16, m, n, k, batch=bt, trans_a=ta, trans_b=tb, stride_a=m * k,
                          stride_b=n * k, stride_c=m * n)
         bufs = [(mm.buf(As[i]), mm.buf(Bs[i])) for i in range(n_rot)]
         cbuf = mm.buf(c)
@@ -402,22 +407,30 @@ def gemm_sweep(torch, mm, wl, dev, stream, args):
         def step(i):
             mm.mm_gemm(d, bufs[i][0], bufs[i][1], cbuf, stream=stream)
         t, _ = timer.time(step, n_rot, 4 * n_rot, 3)
-        Ah = [x.view(torch.float16).view(bt, m, k) for x in As]
-        Bt = [x.view(torch.float16).view(bt, n, k).transpose(1, 2).contiguous() for x in Bs]
+        if bt == 1:  # the stored operands, as the op() views torch.mm takes
+            Ah = [x.view(torch.float16).view(k, m).t() if ta else x.view(torch.float16).view(m, k)
+                  for x in As]
+            Bt = [x.view(torch.float16).view(n, k).t() if tb else x.view(torch.float16).view(k, n)
+                  for x in Bs]
+        else:  # NT only
+            Ah = [x.view(torch.float16).view(bt, m, k) for x in As]
+            Bt = [x.view(torch.float16).view(bt, n, k).transpose(1, 2).contiguous() for x in Bs]
         ch = c.view(torch.float16).view(bt, m, n)
 
         def vstep(i):
             if bt == 1:
-                torch.mm(Ah[i][0], Bt[i][0], out=ch[0])
+                torch.mm(Ah[i], Bt[i], out=ch[0])
             else:
                 torch.bmm(Ah[i], Bt[i], out=ch)
         tv, _ = timer.time(vstep, n_rot, 4 * n_rot, 3)
         flops = 2.0 * bt * m * n * k
-        row = {"batch": bt, "m": m, "n": n, "k": k, "kernel": rec.kernel, "variant": rec.variant,
+        row = {"batch": bt, "m": m, "n": n, "k": k, "trans_a": ta, "trans_b": tb,
+               "kernel": rec.kernel, "variant": rec.variant,
                "us": t * 1e3, "tflops": flops / (t * 1e-3) / 1e12, "torch_us": tv * 1e3,
                "torch_tflops": flops / (tv * 1e-3) / 1e12, "ratio": t / tv}
         rows.append(row)
-        log(f"b={bt:3d} m={m:5d} n={n:6d} k={k:6d} kernel={rec.kernel:2d}/{rec.variant:<4d} "
+        log(f"{'T' if ta else 'N'}{'T' if tb else 'N'} b={bt:3d} m={m:5d} n={n:6d} k={k:6d} "
+            f"kernel={rec.kernel:2d}/{rec.variant:<4d} "
             f"ours {row['us']:8.2f} us {row['tflops']:7.1f} TF  torch {row['torch_us']:8.2f} us "
             f"{row['torch_tflops']:7.1f} TF  time ratio {row['ratio']:.2f}")
         del As, Bs, Ah, Bt, a, b, c

@@ -658,7 +658,22 @@ __global__ __launch_bounds__(PMT * 4, 1) void gemm_nt_panel(GemmArgs a, int nspl
     }
 }
 
-template <class T, int TF>
+// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group,
+// output lane j receives element j % 4 of the four 16-bit elements at the
+// addresses of lanes j / 4, j / 4 + 4, j / 4 + 8 and j / 4 + 12 of the group.
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16*)(const_cast<void*>(p)));
+    return __builtin_bit_cast(u32x2, v);
+}
+
+// Chunk swizzle of a k-major stage row r (K-strided operands): the 16 rows
+// that one transposing read touches spread over 8 distinct 32-byte bank
+// segments.
+__device__ __forceinline__ int kswz(int r) { return 2 * ((r & 3) + 4 * ((r >> 3) & 1)); }
+
+template <class T, int TF, bool KA = true, bool KB = true>
 __global__ __launch_bounds__(LThreads, TF == 8 ? 1 : 2) void gemm_mfma_large(GemmArgs a) {
     using L = LTile<TF>;
     constexpr int BM = L::BM, SH = L::STAGE_H, IPW = L::IPW, LLPS = L::LPS;
@@ -688,35 +703,73 @@ __global__ __launch_bounds__(LThreads, TF == 8 ? 1 : 2) void gemm_mfma_large(Gem
     const int nk = (int)(a.k / LBK);  // a multiple of LSTAGES, at least 2 * LSTAGES
     const int lda = (int)a.lda, ldb = (int)a.ldb;
 
-    // DMA lane mapping: instruction j of a wave covers tile rows w*RPW + j*16 +
-    // lane/4; lane writes LDS slot lane%4 of its row with the chunk that the
-    // swizzle puts there. The row's swizzle does not depend on j.
+    // DMA lane mapping, K-contiguous operand (A [m,k], B [n,k]): instruction
+    // j of a wave covers tile rows w*RPW + j*16 + lane/4; lane writes LDS slot
+    // lane%4 of its row with the chunk that the swizzle puts there. The row's
+    // swizzle does not depend on j.
     const int chunk = (lane % LCPR) ^ lswz(lane / LCPR);
     const int voa = ((w * RPW + lane / LCPR) * lda + chunk * 8) * 2;
     const int vob = ((w * RPW + lane / LCPR) * ldb + chunk * 8) * 2;
-    // Fragment reads: lane -> row lane%16 of a 16-row slab, chunk lane/16.
+    // K-strided operand (A [k,m], B [k,n]): the stage holds the k-tile as 32
+    // rows of BM elements (row = k), chunk c of row r at slot c ^ kswz(r).
+    // Instruction j of a wave covers rows (w*IPW + j)*RPK + lane/CPK; the
+    // lane's slot is lane % CPK. The swizzle depends on j only through j % 2.
+    constexpr int CPK = BM / 8;   // 16-byte chunks per k-row
+    constexpr int RPK = 64 / CPK; // k-rows per DMA instruction
+    const int kr0 = (w * IPW) * RPK + lane / CPK, kr1 = kr0 + RPK, kslot = lane % CPK;
+    const int voka0 = ((lane / CPK) * lda + 8 * (kslot ^ kswz(kr0))) * 2;
+    const int voka1 = ((lane / CPK) * lda + 8 * (kslot ^ kswz(kr1))) * 2;
+    const int vokb0 = ((lane / CPK) * ldb + 8 * (kslot ^ kswz(kr0))) * 2;
+    const int vokb1 = ((lane / CPK) * ldb + 8 * (kslot ^ kswz(kr1))) * 2;
+    // Fragment reads, K-contiguous: lane -> row lane%16 of a 16-row slab, chunk lane/16.
     const int lr = lane & 15, lq = lane >> 4;
     const int foff = lr * LBK + ((lq ^ lswz(lr)) << 3);
+    // Fragment reads, K-strided: two transposing reads per fragment (k 0-3
+    // and 4-7 of the lane's eight). Lane s of 16-lane group g addresses row
+    // 8g + 4h + s/4 (h = read), columns 4 (s % 4) .. + 3 of the fragment;
+    // the byte offset of fragment f is the wave's base XOR 32 f.
+    const int kg = lane >> 4, ks = lane & 15, kx = (ks & 3) >> 1;
+    const int kr_0 = 8 * kg + (ks >> 2), kr_1 = kr_0 + 4;
+    const int kb0 = kr_0 * 2 * BM + 8 * (ks & 1) + 16 * (kx ^ kswz(kr_0));
+    const int kb1 = kr_1 * 2 * BM + 8 * (ks & 1) + 16 * (kx ^ kswz(kr_1));
+    const int kA0 = kb0 ^ (32 * TF * wm), kA1 = kb1 ^ (32 * TF * wm);
+    const int kB0 = kb0 ^ (32 * TF * wn), kB1 = kb1 ^ (32 * TF * wn);
+    constexpr int DSA = KA ? 1 : 2, DSB = KB ? 1 : 2;  // LDS reads per fragment
 
     for (int64_t b = blockIdx.y; b < a.batch; b += gridDim.y) {
-        const uint16_t* A = reinterpret_cast<const uint16_t*>(a.A) + b * a.sa + m0 * a.lda;
-        const uint16_t* B = reinterpret_cast<const uint16_t*>(a.B) + b * a.sb + n0 * a.ldb;
+        const uint16_t* A = reinterpret_cast<const uint16_t*>(a.A) + b * a.sa + (KA ? m0 * a.lda : m0);
+        const uint16_t* B = reinterpret_cast<const uint16_t*>(a.B) + b * a.sb + (KB ? n0 * a.ldb : n0);
         const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(A), (short)0, BM * lda * 2, 0x00020000);
+            const_cast<uint16_t*>(A), (short)0,
+            KA ? BM * lda * 2 : (int)(((a.k - 1) * a.lda + BM) * 2), 0x00020000);
         const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(B), (short)0, BM * ldb * 2, 0x00020000);
+            const_cast<uint16_t*>(B), (short)0,
+            KB ? BM * ldb * 2 : (int)(((a.k - 1) * a.ldb + BM) * 2), 0x00020000);
 
         // Half p (instructions IPW/2 * p .. of each operand) of k-tile kt into a stage.
         auto dma_half = [&](int stage, int kt, int p) {
             uint16_t* sa = lds + stage * SH + w * RPW * LBK;
             uint16_t* sb = sa + BM * LBK;
+            uint16_t* ska = lds + stage * SH;   // k-major A: row r at r * BM
+            uint16_t* skb = ska + BM * LBK;
 #pragma unroll
             for (int jj = 0; jj < IPW / 2; ++jj) {
                 const int j = IPW / 2 * p + jj;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, MM_LDS(sa + j * LRPI * LBK), 16, voa,
-                                                         (j * LRPI * lda + kt * LBK) * 2, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, MM_LDS(sb + j * LRPI * LBK), 16, vob,
-                                                         (j * LRPI * ldb + kt * LBK) * 2, 0, 0);
+                const int kr = (w * IPW + j) * RPK;  // first k-row of a k-major instruction
+                if constexpr (KA)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, MM_LDS(sa + j * LRPI * LBK), 16, voa,
+                                                             (j * LRPI * lda + kt * LBK) * 2, 0, 0);
+                else
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, MM_LDS(ska + kr * BM), 16,
+                                                             j % 2 ? voka1 : voka0,
+                                                             (kt * LBK + kr) * lda * 2, 0, 0);
+                if constexpr (KB)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, MM_LDS(sb + j * LRPI * LBK), 16, vob,
+                                                             (j * LRPI * ldb + kt * LBK) * 2, 0, 0);
+                else
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, MM_LDS(skb + kr * BM), 16,
+                                                             j % 2 ? vokb1 : vokb0,
+                                                             (kt * LBK + kr) * ldb * 2, 0, 0);
             }
         };
         f32x4 acc[TF][TF];
@@ -726,14 +779,33 @@ __global__ __launch_bounds__(LThreads, TF == 8 ? 1 : 2) void gemm_mfma_large(Gem
             for (int j = 0; j < TF; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
         // A fragments of half hh (wave rows hh*WT/2 + 16i) / all TF B fragments of a stage.
         auto rda = [&](int stage, int hh, u32x4 (&fa)[HF]) {
-            const uint16_t* sa = lds + stage * SH + (wm * WT + hh * (WT / 2)) * LBK;
+            if constexpr (KA) {
+                const uint16_t* sa = lds + stage * SH + (wm * WT + hh * (WT / 2)) * LBK;
 #pragma unroll
-            for (int i = 0; i < HF; ++i) fa[i] = *reinterpret_cast<const u32x4*>(sa + i * 16 * LBK + foff);
+                for (int i = 0; i < HF; ++i) fa[i] = *reinterpret_cast<const u32x4*>(sa + i * 16 * LBK + foff);
+            } else {
+                const char* sa = reinterpret_cast<const char*>(lds + stage * SH);
+#pragma unroll
+                for (int i = 0; i < HF; ++i) {
+                    const int f = 16 * TF * hh + 32 * i;
+                    const u32x2 lo = lds_read_tr16(sa + (kA0 ^ f)), hi = lds_read_tr16(sa + (kA1 ^ f));
+                    fa[i] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+                }
+            }
         };
         auto rdb = [&](int stage, u32x4 (&fb)[TF]) {
-            const uint16_t* sb = lds + stage * SH + BM * LBK + wn * WT * LBK;
+            if constexpr (KB) {
+                const uint16_t* sb = lds + stage * SH + BM * LBK + wn * WT * LBK;
 #pragma unroll
-            for (int j = 0; j < TF; ++j) fb[j] = *reinterpret_cast<const u32x4*>(sb + j * 16 * LBK + foff);
+                for (int j = 0; j < TF; ++j) fb[j] = *reinterpret_cast<const u32x4*>(sb + j * 16 * LBK + foff);
+            } else {
+                const char* sb = reinterpret_cast<const char*>(lds + stage * SH + BM * LBK);
+#pragma unroll
+                for (int j = 0; j < TF; ++j) {
+                    const u32x2 lo = lds_read_tr16(sb + (kB0 ^ (32 * j))), hi = lds_read_tr16(sb + (kB1 ^ (32 * j)));
+                    fb[j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+                }
+            }
         };
         // D[n][m] = sum_k B(n,k) A(m,k): the lane's four consecutive values run along n.
         auto mm = [&](int hh, const u32x4 (&fa)[HF], const u32x4 (&fb)[TF]) {
@@ -764,7 +836,7 @@ __global__ __launch_bounds__(LThreads, TF == 8 ? 1 : 2) void gemm_mfma_large(Gem
             rda(s, 1, fa1);
             if constexpr (decltype(P1)::value) dma_half((s + 3) % LSTAGES, kt + 3, 1);
             mm(0, fa0, fb);
-            weave(ic<HF>{}, decltype(P1)::value ? NR : 0);
+            weave(ic<HF * DSA>{}, decltype(P1)::value ? NR : 0);
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (decltype(NEXT)::value) {
                 __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(decltype(VM)::value));
@@ -774,7 +846,7 @@ __global__ __launch_bounds__(LThreads, TF == 8 ? 1 : 2) void gemm_mfma_large(Gem
                 if constexpr (decltype(DMA0)::value) dma_half(s, kt + LSTAGES, 0);
             }
             mm(1, fa1, fb);
-            weave(ic<decltype(NEXT)::value ? HF + TF : 0>{}, decltype(DMA0)::value ? NR : 0);
+            weave(ic<decltype(NEXT)::value ? HF * DSA + TF * DSB : 0>{}, decltype(DMA0)::value ? NR : 0);
             __builtin_amdgcn_sched_barrier(0);
         };
 
@@ -1008,6 +1080,16 @@ __global__ __launch_bounds__(kWave) void gemm_f32_mfma_small(GemmArgs a) {
     }
 }
 
+// The pipelined kernel for a transpose layout: A K-contiguous unless ta, B
+// K-contiguous when tb.
+template <class T, int TF>
+const void* pick_pipelined(bool ta, bool tb) {
+    if (!ta && tb) return reinterpret_cast<const void*>(&gemm_mfma_large<T, TF, true, true>);
+    if (!ta) return reinterpret_cast<const void*>(&gemm_mfma_large<T, TF, true, false>);
+    if (tb) return reinterpret_cast<const void*>(&gemm_mfma_large<T, TF, false, true>);
+    return reinterpret_cast<const void*>(&gemm_mfma_large<T, TF, false, false>);
+}
+
 template <int TILE>
 const void* pick_f32(bool ta, bool tb) {
     if (!ta && !tb) return reinterpret_cast<const void*>(&gemm_f32_fma<false, false, TILE>);
@@ -1046,12 +1128,13 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, Launched* L) {
     const int64_t span_b = a.tb ? (a.n - 1) * a.ldb + a.k : (a.k - 1) * a.ldb + a.n;
     const bool vec = aligned16(a.A) && aligned16(a.B) && a.lda % 8 == 0 && a.ldb % 8 == 0 &&
                      a.sa % 8 == 0 && a.sb % 8 == 0 && span_a < (1ll << 30) && span_b < (1ll << 30);
-    // NT products on the DMA-pipelined MFMA kernel: 256 x 256 tiles when at
-    // least 192 of them cover the batch, else 128 x 128 tiles of the same
-    // pipeline (two blocks per CU). Measured on MI355X: 256 x 256 from 192
-    // tiles on, 128 x 128 at 128 tiles and below, and 128 x 128 ahead of the
-    // 128 x 128 register-staged kernel at every measured shape.
-    const bool pipelined = vec && !a.ta && a.tb && a.k % (LSTAGES * LBK) == 0 &&
+    // Products on the DMA-pipelined MFMA kernel, any transpose layout: 256 x
+    // 256 tiles when at least 192 of them cover the batch, else 128 x 128
+    // tiles of the same pipeline (two blocks per CU). Measured on MI355X (NT):
+    // 256 x 256 from 192 tiles on, 128 x 128 at 128 tiles and below, and
+    // 128 x 128 ahead of the 128 x 128 register-staged kernel at every
+    // measured shape.
+    const bool pipelined = vec && a.k % (LSTAGES * LBK) == 0 &&
                            a.k >= 2 * LSTAGES * LBK && a.lda < (1 << 22) && a.ldb < (1 << 22) &&
                            a.ldc % 4 == 0 && (reinterpret_cast<uintptr_t>(a.C) & 7) == 0 && a.sc % 4 == 0;
     const int64_t big_tiles = (a.m / LTile<8>::BM) * (a.n / LTile<8>::BM);
@@ -1060,10 +1143,10 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, Launched* L) {
     const bool mid = !big && pipelined && a.m % LTile<4>::BM == 0 && a.n % LTile<4>::BM == 0;
     if (big || mid) {
         const int64_t tiles = big ? big_tiles : (a.m / LTile<4>::BM) * (a.n / LTile<4>::BM);
-        const void* fn = big ? (a.dtype == 1 ? (const void*)&gemm_mfma_large<TF16, 8>
-                                             : (const void*)&gemm_mfma_large<TBF16, 8>)
-                             : (a.dtype == 1 ? (const void*)&gemm_mfma_large<TF16, 4>
-                                             : (const void*)&gemm_mfma_large<TBF16, 4>);
+        const void* fn = big ? (a.dtype == 1 ? pick_pipelined<TF16, 8>(a.ta, a.tb)
+                                             : pick_pipelined<TBF16, 8>(a.ta, a.tb))
+                             : (a.dtype == 1 ? pick_pipelined<TF16, 4>(a.ta, a.tb)
+                                             : pick_pipelined<TBF16, 4>(a.ta, a.tb));
         const unsigned grid = (unsigned)(((tiles + 7) / 8) * 8);
         L->kernel = MM_KERNEL_GEMM_LARGE;
         L->variant = big ? LTile<8>::BM : LTile<4>::BM;

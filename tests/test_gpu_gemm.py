@@ -337,6 +337,58 @@ def test_mid_tile_broadcast_b():
     assert (rec.kernel, rec.variant) == (mm.MM_KERNEL_GEMM_LARGE, 128), (rec.kernel, rec.variant)
 
 
+LAYOUTS = [(False, True), (False, False), (True, True), (True, False)]  # (trans_a, trans_b)
+
+
+@pytest.mark.parametrize("dt", [wl.F16, wl.BF16])
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_pipelined_layouts_128_tiles(dt, ta, tb):
+    """Every transpose layout on the pipelined kernel's 128 x 128 tiles: a
+    K-strided operand (A stored [k, m], B stored [k, n]) lands k-major in
+    LDS and reaches the MFMA through transposing LDS reads. Every output
+    against the oracle; then ramp inputs bit for bit."""
+    m, n, k = 384, 640, 512
+    _say(f"pipelined 128 layouts dt={wl.DTYPE_NAMES[dt]} ta={int(ta)} tb={int(tb)} {m}x{n}x{k}")
+    case = wl.random_gemm_case(60 + 2 * ta + tb, dt, 1, m, n, k, ta, tb)
+    rec = check_gemm(case, what=f"layout {int(ta)}{int(tb)}")
+    assert (rec.kernel, rec.variant) == (mm.MM_KERNEL_GEMM_LARGE, 128), (rec.kernel, rec.variant)
+    a = wl.ramp(m * k, 1).reshape((1, k, m) if ta else (1, m, k))
+    b = wl.ramp(n * k, 2).reshape((1, n, k) if tb else (1, k, n))
+    rec = check_gemm(wl.make_gemm_case(dt, a, b, ta, tb), exact=True, what="layout ramp")
+    assert (rec.kernel, rec.variant) == (mm.MM_KERNEL_GEMM_LARGE, 128), (rec.kernel, rec.variant)
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_pipelined_layouts_batched_padded(ta, tb):
+    """Every layout on 128 x 128 tiles with padded leading dimensions, batch
+    strides with gaps and element offsets on every operand."""
+    _say(f"pipelined layouts batched padded ta={int(ta)} tb={int(tb)}")
+    rng = np.random.default_rng(14)
+    b_, m, n, k = 3, 256, 384, 384
+    a = rng.standard_normal((b_, k, m) if ta else (b_, m, k))
+    bb = rng.standard_normal((b_, n, k) if tb else (b_, k, n)) / np.sqrt(k)
+    lda = (m if ta else k) + 24
+    ldb = (k if tb else n) + 40
+    rows_a = k if ta else m
+    rows_b = n if tb else k
+    case = wl.make_gemm_case(wl.BF16, a, bb, ta, tb, lda=lda, ldb=ldb, ldc=n + 4, off_a=8,
+                             off_b=16, off_c=4, stride_a=rows_a * lda + 64,
+                             stride_b=rows_b * ldb + 8, stride_c=m * (n + 4) + 12)
+    rec = check_gemm(case, what="layouts batched padded")
+    assert (rec.kernel, rec.variant) == (mm.MM_KERNEL_GEMM_LARGE, 128), (rec.kernel, rec.variant)
+
+
+@pytest.mark.parametrize("dt", [wl.F16, wl.BF16])
+@pytest.mark.parametrize("ta,tb", LAYOUTS[1:])
+def test_pipelined_layouts_256_tiles(dt, ta, tb):
+    """NN, TN and TT products large enough for 256 x 256 tiles (192 of them),
+    sampled against the oracle."""
+    m, n, k = 3072, 4096, 256
+    _say(f"pipelined 256 layouts dt={wl.DTYPE_NAMES[dt]} ta={int(ta)} tb={int(tb)} {m}x{n}x{k}")
+    case = wl.random_gemm_case(64 + 2 * ta + tb, dt, 1, m, n, k, ta, tb)
+    _sampled_check(case, 4096, 15, kernel=mm.MM_KERNEL_GEMM_LARGE, variant=256)
+
+
 def test_large_tile_route_batched_padded():
     _say("large-tile NT batched, padded ld, bf16 m=4096 n=4096 k=256 batch 2")
     rng = np.random.default_rng(9)
