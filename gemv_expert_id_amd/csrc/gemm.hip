@@ -673,6 +673,25 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
 // segments.
 __device__ __forceinline__ int kswz(int r) { return 2 * ((r & 3) + 4 * ((r >> 3) & 1)); }
 
+// LDS stage S of K-strided operand OP (N halves): each stage its own array,
+// so that the compiler can tell the transposing reads of one stage apart from
+// DMA into the others (with one array for all stages it waits for every DMA
+// in flight before each such read).
+template <int N, int S, int OP>
+__device__ __forceinline__ uint16_t* kmajor_stage() {
+    __shared__ __attribute__((aligned(1024))) uint16_t st[N];
+    return st;
+}
+
+// Dynamic LDS of the pipelined kernel: both operands' stages when both are
+// K-contiguous, else only the K-contiguous operand's (K-strided ones use
+// kmajor_stage).
+template <int TF>
+constexpr size_t pipelined_lds_bytes(bool ka, bool kb) {
+    return ka && kb ? LTile<TF>::LDS
+                    : (ka || kb ? (size_t)LSTAGES * LTile<TF>::BM * LBK * sizeof(uint16_t) : 0);
+}
+
 template <class T, int TF, bool KA = true, bool KB = true>
 __global__ __launch_bounds__(LThreads, TF == 8 ? 1 : 2) void gemm_mfma_large(GemmArgs a) {
     using L = LTile<TF>;
@@ -735,6 +754,19 @@ __global__ __launch_bounds__(LThreads, TF == 8 ? 1 : 2) void gemm_mfma_large(Gem
     const int kA0 = kb0 ^ (32 * TF * wm), kA1 = kb1 ^ (32 * TF * wm);
     const int kB0 = kb0 ^ (32 * TF * wn), kB1 = kb1 ^ (32 * TF * wn);
     constexpr int DSA = KA ? 1 : 2, DSB = KB ? 1 : 2;  // LDS reads per fragment
+    // Stage bases by compile-time stage index: a K-contiguous operand in the
+    // dynamic array ([stage][A | B] when both are, else [stage][that one]),
+    // a K-strided one in its own per-stage arrays.
+    constexpr int DSTR = KA && KB ? SH : BM * LBK;
+    // (A K-contiguous operand's stage may also be named by a run-time int.)
+    auto stage_a = [&](auto S_) -> uint16_t* {
+        if constexpr (KA) return lds + (int)S_ * DSTR;
+        else return kmajor_stage<BM * LBK, decltype(S_)::value, 0>();
+    };
+    auto stage_b = [&](auto S_) -> uint16_t* {
+        if constexpr (KB) return lds + (int)S_ * DSTR + (KA ? BM * LBK : 0);
+        else return kmajor_stage<BM * LBK, decltype(S_)::value, 1>();
+    };
 
     for (int64_t b = blockIdx.y; b < a.batch; b += gridDim.y) {
         const uint16_t* A = reinterpret_cast<const uint16_t*>(a.A) + b * a.sa + (KA ? m0 * a.lda : m0);
@@ -747,11 +779,18 @@ __global__ __launch_bounds__(LThreads, TF == 8 ? 1 : 2) void gemm_mfma_large(Gem
             KB ? BM * ldb * 2 : (int)(((a.k - 1) * a.ldb + BM) * 2), 0x00020000);
 
         // Half p (instructions IPW/2 * p .. of each operand) of k-tile kt into a stage.
-        auto dma_half = [&](int stage, int kt, int p) {
-            uint16_t* sa = lds + stage * SH + w * RPW * LBK;
-            uint16_t* sb = sa + BM * LBK;
-            uint16_t* ska = lds + stage * SH;   // k-major A: row r at r * BM
-            uint16_t* skb = ska + BM * LBK;
+        auto dma_half = [&](auto S_, int kt, int p) {
+            uint16_t *sa, *sb;
+            if constexpr (KA && KB) {
+                const int stage = S_;
+                sa = lds + stage * SH + w * RPW * LBK;
+                sb = sa + BM * LBK;
+            } else {
+                sa = stage_a(S_) + w * RPW * LBK;
+                sb = stage_b(S_) + w * RPW * LBK;
+            }
+            uint16_t* ska = stage_a(S_);   // k-major: row r at r * BM
+            uint16_t* skb = stage_b(S_);
 #pragma unroll
             for (int jj = 0; jj < IPW / 2; ++jj) {
                 const int j = IPW / 2 * p + jj;
@@ -778,13 +817,18 @@ __global__ __launch_bounds__(LThreads, TF == 8 ? 1 : 2) void gemm_mfma_large(Gem
 #pragma unroll
             for (int j = 0; j < TF; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
         // A fragments of half hh (wave rows hh*WT/2 + 16i) / all TF B fragments of a stage.
-        auto rda = [&](int stage, int hh, u32x4 (&fa)[HF]) {
-            if constexpr (KA) {
+        auto rda = [&](auto S_, int hh, u32x4 (&fa)[HF]) {
+            if constexpr (KA && KB) {
+                const int stage = S_;
                 const uint16_t* sa = lds + stage * SH + (wm * WT + hh * (WT / 2)) * LBK;
 #pragma unroll
                 for (int i = 0; i < HF; ++i) fa[i] = *reinterpret_cast<const u32x4*>(sa + i * 16 * LBK + foff);
+            } else if constexpr (KA) {
+                const uint16_t* sa = stage_a(S_) + (wm * WT + hh * (WT / 2)) * LBK;
+#pragma unroll
+                for (int i = 0; i < HF; ++i) fa[i] = *reinterpret_cast<const u32x4*>(sa + i * 16 * LBK + foff);
             } else {
-                const char* sa = reinterpret_cast<const char*>(lds + stage * SH);
+                const char* sa = reinterpret_cast<const char*>(stage_a(S_));
 #pragma unroll
                 for (int i = 0; i < HF; ++i) {
                     const int f = 16 * TF * hh + 32 * i;
@@ -793,13 +837,18 @@ __global__ __launch_bounds__(LThreads, TF == 8 ? 1 : 2) void gemm_mfma_large(Gem
                 }
             }
         };
-        auto rdb = [&](int stage, u32x4 (&fb)[TF]) {
-            if constexpr (KB) {
+        auto rdb = [&](auto S_, u32x4 (&fb)[TF]) {
+            if constexpr (KA && KB) {
+                const int stage = S_;
                 const uint16_t* sb = lds + stage * SH + BM * LBK + wn * WT * LBK;
 #pragma unroll
                 for (int j = 0; j < TF; ++j) fb[j] = *reinterpret_cast<const u32x4*>(sb + j * 16 * LBK + foff);
+            } else if constexpr (KB) {
+                const uint16_t* sb = stage_b(S_) + wn * WT * LBK;
+#pragma unroll
+                for (int j = 0; j < TF; ++j) fb[j] = *reinterpret_cast<const u32x4*>(sb + j * 16 * LBK + foff);
             } else {
-                const char* sb = reinterpret_cast<const char*>(lds + stage * SH + BM * LBK);
+                const char* sb = reinterpret_cast<const char*>(stage_b(S_));
 #pragma unroll
                 for (int j = 0; j < TF; ++j) {
                     const u32x2 lo = lds_read_tr16(sb + (kB0 ^ (32 * j))), hi = lds_read_tr16(sb + (kB1 ^ (32 * j)));
@@ -833,17 +882,17 @@ __global__ __launch_bounds__(LThreads, TF == 8 ? 1 : 2) void gemm_mfma_large(Gem
             constexpr int s = decltype(S_)::value;
             auto& fb = (s % 2 == 0) ? fb0 : fb1;
             auto& fbn = (s % 2 == 0) ? fb1 : fb0;
-            rda(s, 1, fa1);
-            if constexpr (decltype(P1)::value) dma_half((s + 3) % LSTAGES, kt + 3, 1);
+            rda(ic<s>{}, 1, fa1);
+            if constexpr (decltype(P1)::value) dma_half(ic<(s + 3) % LSTAGES>{}, kt + 3, 1);
             mm(0, fa0, fb);
             weave(ic<HF * DSA>{}, decltype(P1)::value ? NR : 0);
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (decltype(NEXT)::value) {
                 __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(decltype(VM)::value));
                 __builtin_amdgcn_s_barrier();
-                rda((s + 1) % LSTAGES, 0, fa0);
-                rdb((s + 1) % LSTAGES, fbn);
-                if constexpr (decltype(DMA0)::value) dma_half(s, kt + LSTAGES, 0);
+                rda(ic<(s + 1) % LSTAGES>{}, 0, fa0);
+                rdb(ic<(s + 1) % LSTAGES>{}, fbn);
+                if constexpr (decltype(DMA0)::value) dma_half(ic<s>{}, kt + LSTAGES, 0);
             }
             mm(1, fa1, fb);
             weave(ic<decltype(NEXT)::value ? HF * DSA + TF * DSB : 0>{}, decltype(DMA0)::value ? NR : 0);
@@ -851,15 +900,22 @@ __global__ __launch_bounds__(LThreads, TF == 8 ? 1 : 2) void gemm_mfma_large(Gem
         };
 
         // Prologue: tiles 0-3 whole; wait for tile 0.
+        if constexpr (KA && KB) {
 #pragma unroll
-        for (int st = 0; st < LSTAGES; ++st) {
-            dma_half(st, st, 0);
-            dma_half(st, st, 1);
+            for (int st = 0; st < LSTAGES; ++st) {
+                dma_half(st, st, 0);
+                dma_half(st, st, 1);
+            }
+        } else {
+            static_for(std::make_integer_sequence<int, LSTAGES>{}, [&](auto S_) {
+                dma_half(S_, decltype(S_)::value, 0);
+                dma_half(S_, decltype(S_)::value, 1);
+            });
         }
         __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(LLPS * (LSTAGES - 1)));
         __builtin_amdgcn_s_barrier();
-        rda(0, 0, fa0);
-        rdb(0, fb0);
+        rda(ic<0>{}, 0, fa0);
+        rdb(ic<0>{}, fb0);
         constexpr int VMS = LLPS * (LSTAGES - 2);  // steady state: tiles kt+2, kt+3 in flight
         // First round: tile 3 went out whole, so no second half at kt = 0.
         ktile(ic<0>{}, bc<false>{}, bc<true>{}, bc<true>{}, ic<VMS>{}, 0);
@@ -1150,8 +1206,9 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, Launched* L) {
         const unsigned grid = (unsigned)(((tiles + 7) / 8) * 8);
         L->kernel = MM_KERNEL_GEMM_LARGE;
         L->variant = big ? LTile<8>::BM : LTile<4>::BM;
+        const bool ka = !a.ta, kb = a.tb;  // operands K-contiguous
         return hipLaunchKernel(fn, dim3(grid, gy), dim3(LThreads), args,
-                               big ? LTile<8>::LDS : LTile<4>::LDS, s);
+                               big ? pipelined_lds_bytes<8>(ka, kb) : pipelined_lds_bytes<4>(ka, kb), s);
     }
     constexpr int PNW = 64;  // B tile rows of the panel kernel
     const int64_t panel_items = (a.m / 64) * a.batch;
