@@ -389,6 +389,10 @@ def gemm_sweep(torch, mm, wl, dev, stream, args):
     for (ta, tb) in ((False, False), (True, True), (True, False)):
         shapes += [(1, 512, 4096, 4096, ta, tb), (1, 4096, 4096, 4096, ta, tb),
                    (1, 1024, 1024, 1024, ta, tb), (1, 8192, 8192, 8192, ta, tb)]
+    # m, n not multiples of 128 (edge tiles cut at the operands' extents)
+    shapes += [(1, 1000, 4096, 4096, False, True), (1, 777, 11008, 4096, False, True),
+               (1, 3000, 4000, 4096, False, False), (1, 1000, 1000, 1024, False, False),
+               (1, 4000, 3000, 2048, False, True)]
     rows = []
     for (bt, m, n, k, ta, tb) in shapes:
         rng = np.random.default_rng(7)

@@ -692,7 +692,11 @@ constexpr size_t pipelined_lds_bytes(bool ka, bool kb) {
                     : (ka || kb ? (size_t)LSTAGES * LTile<TF>::BM * LBK * sizeof(uint16_t) : 0);
 }
 
-template <class T, int TF, bool KA = true, bool KB = true>
+// RAG: m or n not a multiple of the tile edge. Edge tiles then read through
+// buffer resources cut at the operand's true extent (rows or columns past it
+// read zeros, and any other data in padding columns only feeds outputs that
+// are never stored), and the epilogue stores only inside C.
+template <class T, int TF, bool KA = true, bool KB = true, bool RAG = false>
 __global__ __launch_bounds__(LThreads, TF == 8 ? 1 : 2) void gemm_mfma_large(GemmArgs a) {
     using L = LTile<TF>;
     constexpr int BM = L::BM, SH = L::STAGE_H, IPW = L::IPW, LLPS = L::LPS;
@@ -705,7 +709,8 @@ __global__ __launch_bounds__(LThreads, TF == 8 ? 1 : 2) void gemm_mfma_large(Gem
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = w >> 1, wn = w & 1;
-    const int64_t tiles_m = a.m / BM, tiles_n = a.n / BM;
+    const int64_t tiles_m = RAG ? (a.m + BM - 1) / BM : a.m / BM;
+    const int64_t tiles_n = RAG ? (a.n + BM - 1) / BM : a.n / BM;
     const int64_t ntiles = tiles_m * tiles_n;
 
     // XCD-aware grouped tile order.
@@ -771,12 +776,19 @@ __global__ __launch_bounds__(LThreads, TF == 8 ? 1 : 2) void gemm_mfma_large(Gem
     for (int64_t b = blockIdx.y; b < a.batch; b += gridDim.y) {
         const uint16_t* A = reinterpret_cast<const uint16_t*>(a.A) + b * a.sa + (KA ? m0 * a.lda : m0);
         const uint16_t* B = reinterpret_cast<const uint16_t*>(a.B) + b * a.sb + (KB ? n0 * a.ldb : n0);
+        // Rows (K-contiguous) or columns (K-strided) of this tile inside the operand.
+        const int64_t mrows = RAG && a.m - m0 < BM ? a.m - m0 : BM;
+        const int64_t nrows = RAG && a.n - n0 < BM ? a.n - n0 : BM;
         const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t*>(A), (short)0,
-            KA ? BM * lda * 2 : (int)(((a.k - 1) * a.lda + BM) * 2), 0x00020000);
+            RAG ? (int)((KA ? (mrows - 1) * a.lda + a.k : (a.k - 1) * a.lda + mrows) * 2)
+                : (KA ? BM * lda * 2 : (int)(((a.k - 1) * a.lda + BM) * 2)),
+            0x00020000);
         const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t*>(B), (short)0,
-            KB ? BM * ldb * 2 : (int)(((a.k - 1) * a.ldb + BM) * 2), 0x00020000);
+            RAG ? (int)((KB ? (nrows - 1) * a.ldb + a.k : (a.k - 1) * a.ldb + nrows) * 2)
+                : (KB ? BM * ldb * 2 : (int)(((a.k - 1) * a.ldb + BM) * 2)),
+            0x00020000);
 
         // Half p (instructions IPW/2 * p .. of each operand) of k-tile kt into a stage.
         auto dma_half = [&](auto S_, int kt, int p) {
@@ -940,11 +952,16 @@ __global__ __launch_bounds__(LThreads, TF == 8 ? 1 : 2) void gemm_mfma_large(Gem
 #pragma unroll
         for (int i = 0; i < TF; ++i) {
             const int64_t gm = m0 + wm * WT + i * 16 + lr;
+            if (RAG && gm >= a.m) continue;
 #pragma unroll
             for (int j = 0; j < TF; ++j) {
                 const int64_t gn = n0 + wn * WT + j * 16 + lq * 4;
                 uint16_t* dst = C + gm * a.ldc + gn;
-                if (a.beta == 0.f) {
+                if (RAG && gn + 4 > a.n) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        if (gn + q < a.n) dst[q] = axpby<T>(acc[i][j][q], a.alpha, a.beta, dst + q);
+                } else if (a.beta == 0.f) {
                     u32x2 v;
                     v[0] = (uint32_t)narrow(T{}, a.alpha * acc[i][j][0]) |
                            ((uint32_t)narrow(T{}, a.alpha * acc[i][j][1]) << 16);
@@ -1138,12 +1155,16 @@ __global__ __launch_bounds__(kWave) void gemm_f32_mfma_small(GemmArgs a) {
 
 // The pipelined kernel for a transpose layout: A K-contiguous unless ta, B
 // K-contiguous when tb.
-template <class T, int TF>
+template <class T, int TF, bool RAG>
 const void* pick_pipelined(bool ta, bool tb) {
-    if (!ta && tb) return reinterpret_cast<const void*>(&gemm_mfma_large<T, TF, true, true>);
-    if (!ta) return reinterpret_cast<const void*>(&gemm_mfma_large<T, TF, true, false>);
-    if (tb) return reinterpret_cast<const void*>(&gemm_mfma_large<T, TF, false, true>);
-    return reinterpret_cast<const void*>(&gemm_mfma_large<T, TF, false, false>);
+    if (!ta && tb) return reinterpret_cast<const void*>(&gemm_mfma_large<T, TF, true, true, RAG>);
+    if (!ta) return reinterpret_cast<const void*>(&gemm_mfma_large<T, TF, true, false, RAG>);
+    if (tb) return reinterpret_cast<const void*>(&gemm_mfma_large<T, TF, false, true, RAG>);
+    return reinterpret_cast<const void*>(&gemm_mfma_large<T, TF, false, false, RAG>);
+}
+template <class T, int TF>
+const void* pick_pipelined(bool ta, bool tb, bool rag) {
+    return rag ? pick_pipelined<T, TF, true>(ta, tb) : pick_pipelined<T, TF, false>(ta, tb);
 }
 
 template <int TILE>
@@ -1184,8 +1205,8 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, Launched* L) {
     const int64_t span_b = a.tb ? (a.n - 1) * a.ldb + a.k : (a.k - 1) * a.ldb + a.n;
     const bool vec = aligned16(a.A) && aligned16(a.B) && a.lda % 8 == 0 && a.ldb % 8 == 0 &&
                      a.sa % 8 == 0 && a.sb % 8 == 0 && span_a < (1ll << 30) && span_b < (1ll << 30);
-    // Products on the DMA-pipelined MFMA kernel, any transpose layout: 256 x
-    // 256 tiles when at least 192 of them cover the batch, else 128 x 128
+    // Products on the DMA-pipelined MFMA kernel, any transpose layout and any
+    // m, n: 256 x 256 tiles when at least 192 of them cover the batch, else 128 x 128
     // tiles of the same pipeline (two blocks per CU). Measured on MI355X (NT):
     // 256 x 256 from 192 tiles on, 128 x 128 at 128 tiles and below, and
     // 128 x 128 ahead of the 128 x 128 register-staged kernel at every
@@ -1193,16 +1214,19 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, Launched* L) {
     const bool pipelined = vec && a.k % (LSTAGES * LBK) == 0 &&
                            a.k >= 2 * LSTAGES * LBK && a.lda < (1 << 22) && a.ldb < (1 << 22) &&
                            a.ldc % 4 == 0 && (reinterpret_cast<uintptr_t>(a.C) & 7) == 0 && a.sc % 4 == 0;
-    const int64_t big_tiles = (a.m / LTile<8>::BM) * (a.n / LTile<8>::BM);
-    const bool big = pipelined && a.m % LTile<8>::BM == 0 && a.n % LTile<8>::BM == 0 &&
-                     big_tiles * a.batch >= 192;
-    const bool mid = !big && pipelined && a.m % LTile<4>::BM == 0 && a.n % LTile<4>::BM == 0;
+    // m or n need not be multiples of the tile edge (edge tiles are cut at
+    // the operands' extents and masked at the store).
+    const int64_t big_tiles = ((a.m + 255) / 256) * ((a.n + 255) / 256);
+    const bool big = pipelined && big_tiles * a.batch >= 192;
+    const bool mid = !big && pipelined;
     if (big || mid) {
-        const int64_t tiles = big ? big_tiles : (a.m / LTile<4>::BM) * (a.n / LTile<4>::BM);
-        const void* fn = big ? (a.dtype == 1 ? pick_pipelined<TF16, 8>(a.ta, a.tb)
-                                             : pick_pipelined<TBF16, 8>(a.ta, a.tb))
-                             : (a.dtype == 1 ? pick_pipelined<TF16, 4>(a.ta, a.tb)
-                                             : pick_pipelined<TBF16, 4>(a.ta, a.tb));
+        const int edge = big ? LTile<8>::BM : LTile<4>::BM;
+        const bool rag = a.m % edge != 0 || a.n % edge != 0;
+        const int64_t tiles = big ? big_tiles : ((a.m + 127) / 128) * ((a.n + 127) / 128);
+        const void* fn = big ? (a.dtype == 1 ? pick_pipelined<TF16, 8>(a.ta, a.tb, rag)
+                                             : pick_pipelined<TBF16, 8>(a.ta, a.tb, rag))
+                             : (a.dtype == 1 ? pick_pipelined<TF16, 4>(a.ta, a.tb, rag)
+                                             : pick_pipelined<TBF16, 4>(a.ta, a.tb, rag));
         const unsigned grid = (unsigned)(((tiles + 7) / 8) * 8);
         L->kernel = MM_KERNEL_GEMM_LARGE;
         L->variant = big ? LTile<8>::BM : LTile<4>::BM;

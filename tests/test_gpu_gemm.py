@@ -282,13 +282,14 @@ def test_large_tile_route_ramp_exact():
     (wl.F16, 1, 1024, 2048, 512, mm.MM_KERNEL_GEMM_LARGE, 128),
     (wl.BF16, 3, 384, 640, 256, mm.MM_KERNEL_GEMM_LARGE, 128),   # 15 tiles per batch item
     (wl.F16, 1, 128, 128, 1024, mm.MM_KERNEL_GEMM_LARGE, 128),   # a single tile
-    (wl.F16, 1, 1000, 2048, 512, mm.MM_KERNEL_GEMM_TILED, 0),    # m not a multiple of 128
+    (wl.F16, 1, 1000, 2048, 512, mm.MM_KERNEL_GEMM_LARGE, 128),  # m not a multiple of 128
+    (wl.F16, 1, 1000, 2048, 320, mm.MM_KERNEL_GEMM_TILED, 0),    # k not a multiple of 128
 ])
 def test_large_tile_threshold(dt, b, m, n, k, kernel, variant):
-    """The pipelined kernel takes NT products whose m and n are multiples of
-    its tile edge: 256 x 256 tiles when at least 192 of them cover the batch,
-    else 128 x 128 tiles; other shapes go to the 128 x 128 register-staged
-    kernel. Every output against the oracle; the receipt names the tile edge."""
+    """The pipelined kernel takes NT products with k a multiple of 128 and
+    k >= 256: 256 x 256 tiles when at least 192 of them cover the batch, else
+    128 x 128 tiles; other k go to the 128 x 128 register-staged kernel.
+    Every output against the oracle; the receipt names the tile edge."""
     _say(f"large-tile threshold dt={wl.DTYPE_NAMES[dt]} b={b} m={m} n={n} k={k}")
     case = wl.random_gemm_case(46 + k, dt, b, m, n, k, False, True)
     rec = check_gemm(case, what=f"threshold {b}x{m}x{n}x{k}")
@@ -387,6 +388,46 @@ def test_pipelined_layouts_256_tiles(dt, ta, tb):
     _say(f"pipelined 256 layouts dt={wl.DTYPE_NAMES[dt]} ta={int(ta)} tb={int(tb)} {m}x{n}x{k}")
     case = wl.random_gemm_case(64 + 2 * ta + tb, dt, 1, m, n, k, ta, tb)
     _sampled_check(case, 4096, 15, kernel=mm.MM_KERNEL_GEMM_LARGE, variant=256)
+
+
+@pytest.mark.parametrize("dt,ta,tb,b,m,n,k,variant", [
+    (wl.F16, False, True, 1, 1000, 3000, 512, 128),
+    (wl.BF16, False, False, 1, 777, 1000, 256, 128),
+    (wl.F16, True, False, 2, 304, 520, 384, 128),
+    (wl.BF16, True, True, 1, 136, 200, 256, 128),
+    (wl.F16, False, False, 1, 100, 704, 256, 128),    # fewer rows than one tile
+    (wl.BF16, False, True, 3, 200, 72, 256, 128),     # fewer columns than one tile
+])
+def test_pipelined_ragged_edges(dt, ta, tb, b, m, n, k, variant):
+    """m and n not multiples of the tile edge on the pipelined kernel: edge
+    tiles read through buffer resources cut at each operand's extent and
+    store only inside C. (A K-strided operand's rows must still be whole
+    16-byte chunks, so its m or n is a multiple of 8.) Every output against
+    the oracle, and the NaN sentinel around C untouched (check_gemm)."""
+    _say(f"pipelined ragged dt={wl.DTYPE_NAMES[dt]} ta={int(ta)} tb={int(tb)} b={b} {m}x{n}x{k}")
+    case = wl.random_gemm_case(70 + m % 7 + n % 5, dt, b, m, n, k, ta, tb)
+    rec = check_gemm(case, what=f"ragged {b}x{m}x{n}x{k}")
+    assert (rec.kernel, rec.variant) == (mm.MM_KERNEL_GEMM_LARGE, variant), (rec.kernel, rec.variant)
+
+
+def test_pipelined_ragged_ramp_exact():
+    """A ragged NT product on the pipelined kernel, ramp inputs, bit for bit."""
+    m, n, k = 200, 136, 512
+    _say(f"pipelined ragged ramp {m}x{n}x{k}")
+    a = wl.ramp(m * k, 1).reshape(1, m, k)
+    b = wl.ramp(n * k, 2).reshape(1, n, k)
+    rec = check_gemm(wl.make_gemm_case(wl.F16, a, b, False, True), exact=True, what="ragged ramp")
+    assert (rec.kernel, rec.variant) == (mm.MM_KERNEL_GEMM_LARGE, 128), (rec.kernel, rec.variant)
+
+
+@pytest.mark.parametrize("ta,tb", [(False, True), (False, False)])
+def test_pipelined_ragged_256_tiles(ta, tb):
+    """A ragged product large enough for 256 x 256 tiles (16 x 12 = 192 of
+    them), sampled against the oracle plus both ends of every row."""
+    m, n, k = 4000, 3000, 256
+    _say(f"pipelined ragged 256 ta={int(ta)} tb={int(tb)} {m}x{n}x{k}")
+    case = wl.random_gemm_case(75 + tb, wl.F16, 1, m, n, k, ta, tb)
+    _sampled_check(case, 4096, 16, kernel=mm.MM_KERNEL_GEMM_LARGE, variant=256)
 
 
 def test_large_tile_route_batched_padded():
