@@ -88,7 +88,7 @@ typedef enum {
     MM_KERNEL_GEMV_ROWS_ELEM = 1,    /* matrix rows along K, element loads */
     MM_KERNEL_GEMV_COLS = 2,         /* outputs contiguous in the matrix */
     MM_KERNEL_GEMM_TILED = 3,        /* 128 x 128 MFMA tiles, any layout and edge */
-    MM_KERNEL_GEMM_LARGE = 4,        /* DMA-pipelined MFMA tiles of 256 x 256 or 128 x 128, any layout, divisible shapes */
+    MM_KERNEL_GEMM_LARGE = 4,        /* DMA-pipelined MFMA tiles of 256 x 256 or 128 x 128, any layout, any m, n; k % 128 == 0 */
     MM_KERNEL_GEMM_F32 = 5,          /* f32 FMA tiles */
     MM_KERNEL_ID_DIRECT_FAST = 6,    /* direct route, 16-byte loads, one id-row load */
     MM_KERNEL_ID_DIRECT = 7,         /* direct route, general */
