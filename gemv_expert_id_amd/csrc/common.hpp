@@ -49,10 +49,8 @@ __device__ __forceinline__ uint16_t narrow(TF16, float x) {
     return __builtin_bit_cast(uint16_t, (_Float16)x);
 }
 __device__ __forceinline__ uint16_t narrow(TBF16, float x) {
-    uint32_t u = __float_as_uint(x);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    // v_cvt_pk_bf16_f32 (gfx950) rounds to nearest even as well; NaN stays NaN.
+    return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
 // ---- output epilogue: alpha * acc + beta * C_old, rounded once ---------------

@@ -165,3 +165,38 @@ def test_axpby_ramp_bit_exact(dt):
         case = wl.make_gemm_case(dt, a, bv, ta, tb)
         c_old = wl.ramp(b * m * n, 3).reshape(b, m, n)
         _run(case, 2.0, 0.5, c_old, exact=True, what=f"ramp {(b, m, n, k)}")
+
+
+# The pipelined kernel (128 x 128 tiles here) in every transpose layout with
+# m and n off the tile edge: ragged edge tiles take the per-element epilogue.
+PIPELINED_CASES = [
+    # (batch, m, n, k, ta, tb)
+    (1, 200, 132, 256, False, True),
+    (1, 100, 136, 256, False, False),
+    (2, 136, 76, 384, True, True),
+    (1, 136, 200, 256, True, False),
+]
+
+
+@pytest.mark.parametrize("dt", [wl.F16, wl.BF16])
+@pytest.mark.parametrize("shape", PIPELINED_CASES)
+@pytest.mark.parametrize("alpha,beta", [(0.75, -1.25), (1.0, 1.0)])
+def test_axpby_pipelined_ragged_layouts(dt, shape, alpha, beta):
+    b, m, n, k, ta, tb = shape
+    _say(f"axpby pipelined {wl.DTYPE_NAMES[dt]} alpha={alpha} beta={beta} shape={shape}")
+    case = wl.random_gemm_case(87 + m % 5, dt, b, m, n, k, ta, tb)
+    c_old = np.random.default_rng(88).standard_normal((b, m, n))
+    rec = _run(case, alpha, beta, c_old, what=str(shape))
+    assert (rec.kernel, rec.variant) == (mm.MM_KERNEL_GEMM_LARGE, 128), (rec.kernel, rec.variant)
+
+
+def test_axpby_pipelined_ramp_bit_exact():
+    """Ramp operands and old values on the ragged pipelined kernel, alpha = 2,
+    beta = 0.5, bit for bit."""
+    b, m, n, k, ta, tb = PIPELINED_CASES[0]
+    a = wl.ramp(b * m * k, 1).reshape(b, m, k)
+    bv = wl.ramp(b * n * k, 2).reshape(b, n, k)
+    case = wl.make_gemm_case(wl.BF16, a, bv, ta, tb)
+    c_old = wl.ramp(b * m * n, 3).reshape(b, m, n)
+    rec = _run(case, 2.0, 0.5, c_old, exact=True, what="pipelined ramp")
+    assert rec.kernel == mm.MM_KERNEL_GEMM_LARGE, rec.kernel
