@@ -978,6 +978,209 @@ __global__ __launch_bounds__(LThreads, TF == 8 ? 1 : 2) void gemm_mfma_large(Gem
         __syncthreads();
     }
 }
+
+// NT form of the pipelined kernel with the four 32-k stages taken in pairs:
+// the two stages of a pair share one LDS region, each tile row holding 64 k
+// (128 B, chunk c at slot c ^ (row & 7)), so that one DMA instruction moves
+// 8 rows x 128 B instead of 16 rows x 64 B: HBM and L2 see 128-byte pieces
+// of each operand row. A region is refilled once both of its stages have been
+// read, which the barrier of every second k-tile establishes; the k-tiles in
+// between need no barrier. The DMA of pair P + 2 is issued during the second
+// half of k-tile 2P + 1 and the first half of k-tile 2P + 2.
+template <class T, int TF, bool RAG = false>
+__global__ __launch_bounds__(LThreads, TF == 8 ? 1 : 2) void gemm_mfma_pair(GemmArgs a) {
+    constexpr int BM = 32 * TF;
+    constexpr int HF = TF / 2;          // A fragments per half of the wave tile
+    constexpr int WT = 16 * TF;         // wave tile edge
+    constexpr int RH = 2 * LBK;         // halves per LDS tile row (one pair of stages)
+    constexpr int OPH = BM * RH;        // halves per operand per region
+    constexpr int REG = 2 * OPH;        // halves per region (A then B)
+    constexpr int NDP = BM / 32;        // DMA instructions per wave, operand and pair
+    constexpr int LPP = 2 * NDP;        // DMA instructions per wave and pair
+    constexpr int MPR = HF * TF / NDP;  // MFMAs per DMA instruction while a half-pair goes out
+    static_assert(2 * REG * sizeof(uint16_t) == LTile<TF>::LDS, "two regions fill the four-stage LDS");
+    extern __shared__ __attribute__((aligned(1024))) uint16_t lds[];  // [region][A | B][row][64]
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = w >> 1, wn = w & 1;
+    const int64_t tiles_m = RAG ? (a.m + BM - 1) / BM : a.m / BM;
+    const int64_t tiles_n = RAG ? (a.n + BM - 1) / BM : a.n / BM;
+    const int64_t ntiles = tiles_m * tiles_n;
+
+    // XCD-aware grouped tile order.
+    const int64_t bid = blockIdx.x;
+    const int64_t per_xcd = (ntiles + 7) / 8;
+    const int64_t t = (bid % 8) * per_xcd + bid / 8;
+    if (t >= ntiles) return;
+    const int64_t group = t / (LGM * tiles_n);
+    const int64_t first_m = group * LGM;
+    const int64_t gsize = tiles_m - first_m < LGM ? tiles_m - first_m : LGM;
+    const int64_t tm = first_m + (t % (LGM * tiles_n)) % gsize;
+    const int64_t tn = (t % (LGM * tiles_n)) / gsize;
+    const int64_t m0 = tm * BM, n0 = tn * BM;
+    const int nk = (int)(a.k / LBK);  // a multiple of LSTAGES, at least 2 * LSTAGES
+    const int lda = (int)a.lda, ldb = (int)a.ldb;
+
+    // DMA: instruction j of a wave covers tile rows w*BM/4 + 8j + lane/8; the
+    // lane fetches the chunk that belongs at slot lane%8 of its row.
+    const int dch = (lane & 7) ^ (lane >> 3);
+    const int voa = ((w * (BM / 4) + (lane >> 3)) * lda + dch * 8) * 2;
+    const int vob = ((w * (BM / 4) + (lane >> 3)) * ldb + dch * 8) * 2;
+    // Fragment reads: lane -> row lane%16 of a 16-row slab, chunk 4h + lane/16
+    // of the pair (h: the stage within the pair).
+    const int lr = lane & 15, lq = lane >> 4;
+    const int foff0 = lr * RH + ((lq ^ (lr & 7)) << 3);
+    const int foff1 = lr * RH + (((4 + lq) ^ (lr & 7)) << 3);
+
+    for (int64_t b = blockIdx.y; b < a.batch; b += gridDim.y) {
+        const uint16_t* A = reinterpret_cast<const uint16_t*>(a.A) + b * a.sa + m0 * a.lda;
+        const uint16_t* B = reinterpret_cast<const uint16_t*>(a.B) + b * a.sb + n0 * a.ldb;
+        const int64_t mrows = RAG && a.m - m0 < BM ? a.m - m0 : BM;
+        const int64_t nrows = RAG && a.n - n0 < BM ? a.n - n0 : BM;
+        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(A), (short)0,
+            RAG ? (int)(((mrows - 1) * a.lda + a.k) * 2) : BM * lda * 2, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(B), (short)0,
+            RAG ? (int)(((nrows - 1) * a.ldb + a.k) * 2) : BM * ldb * 2, 0x00020000);
+
+        // DMA instruction q (operand q % 2, rows 8 (q / 2) ..) of pair `pair` into region R.
+        auto dma = [&](auto R_, int pair, auto Q_) {
+            constexpr int q = decltype(Q_)::value, j = q / 2;
+            uint16_t* dst = lds + decltype(R_)::value * REG + (q % 2) * OPH + (w * (BM / 4) + j * 8) * RH;
+            if constexpr (q % 2 == 0)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, MM_LDS(dst), 16, voa,
+                                                         (j * 8 * lda + pair * RH) * 2, 0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, MM_LDS(dst), 16, vob,
+                                                         (j * 8 * ldb + pair * RH) * 2, 0, 0);
+        };
+        f32x4 acc[TF][TF];
+#pragma unroll
+        for (int i = 0; i < TF; ++i)
+#pragma unroll
+            for (int j = 0; j < TF; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // Stage s of the ring: region s / 2, half s % 2.
+        auto rda = [&](auto S_, int hh, u32x4 (&fa)[HF]) {
+            constexpr int s = decltype(S_)::value;
+            const uint16_t* sa = lds + (s / 2) * REG + (wm * WT + hh * (WT / 2)) * RH + (s % 2 ? foff1 : foff0);
+#pragma unroll
+            for (int i = 0; i < HF; ++i) fa[i] = *reinterpret_cast<const u32x4*>(sa + i * 16 * RH);
+        };
+        auto rdb = [&](auto S_, u32x4 (&fb)[TF]) {
+            constexpr int s = decltype(S_)::value;
+            const uint16_t* sb = lds + (s / 2) * REG + OPH + wn * WT * RH + (s % 2 ? foff1 : foff0);
+#pragma unroll
+            for (int j = 0; j < TF; ++j) fb[j] = *reinterpret_cast<const u32x4*>(sb + j * 16 * RH);
+        };
+        auto mm = [&](int hh, const u32x4 (&fa)[HF], const u32x4 (&fb)[TF]) {
+#pragma unroll
+            for (int i = 0; i < HF; ++i)
+#pragma unroll
+                for (int j = 0; j < TF; ++j) acc[hh * HF + i][j] = mfma16<T>(fb[j], fa[i], acc[hh * HF + i][j]);
+        };
+        // One half k-tile: its NDS fragment reads first, then NDP runs of MPR
+        // MFMAs, each followed by one DMA instruction when dma is set.
+        auto weave = [&](auto NDS, bool dma_on) {
+            __builtin_amdgcn_sched_group_barrier(0x100, decltype(NDS)::value, 0);
+#pragma unroll
+            for (int q = 0; q < NDP; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, MPR, 0);
+                if (dma_on) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            }
+        };
+        u32x4 fa0[HF], fa1[HF], fb0[TF], fb1[TF];
+        // k-tile kt in stage S_ (kt % 4). DQ: 2 = second half of pair PQ in
+        // the first half (even kt), 1 = first half of pair PQ in the second
+        // (odd kt), 0 = none. NEXT: tile kt+1 exists; an odd kt then waits
+        // for all DMA (pair (kt+1)/2) and holds the barrier.
+        auto ktile = [&](auto S_, auto NEXT, auto DQ, int pq) {
+            constexpr int s = decltype(S_)::value, sn = (s + 1) % LSTAGES;
+            constexpr int dq = decltype(DQ)::value;
+            constexpr bool nx = decltype(NEXT)::value;
+            constexpr int RQ = (s == 0 || s == 3) ? 1 : 0;  // region of the pair going out
+            auto& fb = (s % 2 == 0) ? fb0 : fb1;
+            auto& fbn = (s % 2 == 0) ? fb1 : fb0;
+            rda(S_, 1, fa1);
+            if constexpr (dq == 2)
+                static_for(std::make_integer_sequence<int, NDP>{},
+                           [&](auto Q_) { dma(ic<RQ>{}, pq, ic<NDP + decltype(Q_)::value>{}); });
+            mm(0, fa0, fb);
+            weave(ic<HF>{}, dq == 2);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (nx) {
+                if constexpr (s % 2 == 1) {
+                    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+                    __builtin_amdgcn_s_barrier();
+                }
+                rda(ic<sn>{}, 0, fa0);
+                rdb(ic<sn>{}, fbn);
+            }
+            if constexpr (dq == 1)
+                static_for(std::make_integer_sequence<int, NDP>{},
+                           [&](auto Q_) { dma(ic<RQ>{}, pq, ic<decltype(Q_)::value>{}); });
+            mm(1, fa1, fb);
+            weave(ic<nx ? HF + TF : 0>{}, dq == 1);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+
+        // Prologue: pairs 0 and 1 (k-tiles 0-3); wait for pair 0.
+        static_for(std::make_integer_sequence<int, LPP>{}, [&](auto Q_) { dma(ic<0>{}, 0, Q_); });
+        static_for(std::make_integer_sequence<int, LPP>{}, [&](auto Q_) { dma(ic<1>{}, 1, Q_); });
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(LPP));
+        __builtin_amdgcn_s_barrier();
+        rda(ic<0>{}, 0, fa0);
+        rdb(ic<0>{}, fb0);
+        // First round: pair 1's second half went out with the prologue.
+        ktile(ic<0>{}, bc<true>{}, ic<0>{}, 0);
+        ktile(ic<1>{}, bc<true>{}, ic<1>{}, 2);
+        ktile(ic<2>{}, bc<true>{}, ic<2>{}, 2);
+        ktile(ic<3>{}, bc<true>{}, ic<1>{}, 3);
+        int kt0 = LSTAGES;
+        for (; kt0 + 2 * LSTAGES <= nk; kt0 += LSTAGES) {
+            const int p0 = kt0 / 2;
+            ktile(ic<0>{}, bc<true>{}, ic<2>{}, p0 + 1);
+            ktile(ic<1>{}, bc<true>{}, ic<1>{}, p0 + 2);
+            ktile(ic<2>{}, bc<true>{}, ic<2>{}, p0 + 2);
+            ktile(ic<3>{}, bc<true>{}, ic<1>{}, p0 + 3);
+        }
+        // Last round: the second half of the last pair, then no new tiles.
+        ktile(ic<0>{}, bc<true>{}, ic<2>{}, kt0 / 2 + 1);
+        ktile(ic<1>{}, bc<true>{}, ic<0>{}, 0);
+        ktile(ic<2>{}, bc<true>{}, ic<0>{}, 0);
+        ktile(ic<3>{}, bc<false>{}, ic<0>{}, 0);
+
+        // Lane holds C[m = 16i-slab base + lane%16][n = 16j-slab base + 4 (lane/16) + q].
+        uint16_t* C = reinterpret_cast<uint16_t*>(a.C) + b * a.sc;
+#pragma unroll
+        for (int i = 0; i < TF; ++i) {
+            const int64_t gm = m0 + wm * WT + i * 16 + lr;
+            if (RAG && gm >= a.m) continue;
+#pragma unroll
+            for (int j = 0; j < TF; ++j) {
+                const int64_t gn = n0 + wn * WT + j * 16 + lq * 4;
+                uint16_t* dst = C + gm * a.ldc + gn;
+                if (RAG && gn + 4 > a.n) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        if (gn + q < a.n) dst[q] = axpby<T>(acc[i][j][q], a.alpha, a.beta, dst + q);
+                } else if (a.beta == 0.f) {
+                    u32x2 v;
+                    v[0] = (uint32_t)narrow(T{}, a.alpha * acc[i][j][0]) |
+                           ((uint32_t)narrow(T{}, a.alpha * acc[i][j][1]) << 16);
+                    v[1] = (uint32_t)narrow(T{}, a.alpha * acc[i][j][2]) |
+                           ((uint32_t)narrow(T{}, a.alpha * acc[i][j][3]) << 16);
+                    *reinterpret_cast<u32x2*>(dst) = v;
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) dst[q] = axpby<T>(acc[i][j][q], a.alpha, a.beta, dst + q);
+                }
+            }
+        }
+        // The next batch's prologue overwrites every region.
+        __syncthreads();
+    }
+}
 #undef MM_LDS
 
 // ---------------------------------------------------------------------------
@@ -1154,17 +1357,19 @@ __global__ __launch_bounds__(kWave) void gemm_f32_mfma_small(GemmArgs a) {
 }
 
 // The pipelined kernel for a transpose layout: A K-contiguous unless ta, B
-// K-contiguous when tb.
+// K-contiguous when tb; NT takes the paired-stage form when `pair`.
 template <class T, int TF, bool RAG>
-const void* pick_pipelined(bool ta, bool tb) {
-    if (!ta && tb) return reinterpret_cast<const void*>(&gemm_mfma_large<T, TF, true, true, RAG>);
+const void* pick_pipelined(bool ta, bool tb, bool pair) {
+    if (!ta && tb)
+        return pair ? reinterpret_cast<const void*>(&gemm_mfma_pair<T, TF, RAG>)
+                    : reinterpret_cast<const void*>(&gemm_mfma_large<T, TF, true, true, RAG>);
     if (!ta) return reinterpret_cast<const void*>(&gemm_mfma_large<T, TF, true, false, RAG>);
     if (tb) return reinterpret_cast<const void*>(&gemm_mfma_large<T, TF, false, true, RAG>);
     return reinterpret_cast<const void*>(&gemm_mfma_large<T, TF, false, false, RAG>);
 }
 template <class T, int TF>
-const void* pick_pipelined(bool ta, bool tb, bool rag) {
-    return rag ? pick_pipelined<T, TF, true>(ta, tb) : pick_pipelined<T, TF, false>(ta, tb);
+const void* pick_pipelined(bool ta, bool tb, bool rag, bool pair) {
+    return rag ? pick_pipelined<T, TF, true>(ta, tb, pair) : pick_pipelined<T, TF, false>(ta, tb, pair);
 }
 
 template <int TILE>
@@ -1223,10 +1428,17 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, Launched* L) {
         const int edge = big ? LTile<8>::BM : LTile<4>::BM;
         const bool rag = a.m % edge != 0 || a.n % edge != 0;
         const int64_t tiles = big ? big_tiles : ((a.m + 127) / 128) * ((a.n + 127) / 128);
-        const void* fn = big ? (a.dtype == 1 ? pick_pipelined<TF16, 8>(a.ta, a.tb, rag)
-                                             : pick_pipelined<TBF16, 8>(a.ta, a.tb, rag))
-                             : (a.dtype == 1 ? pick_pipelined<TF16, 4>(a.ta, a.tb, rag)
-                                             : pick_pipelined<TBF16, 4>(a.ta, a.tb, rag));
+        // NT: the paired-stage form (128-byte operand pieces, a barrier every
+        // second k-tile, DMA one k-tile less ahead). Measured on MI355X: faster
+        // for 256 x 256 tiles at every measured shape and for 128 x 128 tiles
+        // with more of them than CUs (two resident blocks per CU then hide the
+        // shorter lookahead); with at most one 128 x 128 tile per CU the
+        // four-stage form is faster.
+        const bool pair = big || tiles * a.batch > 256;
+        const void* fn = big ? (a.dtype == 1 ? pick_pipelined<TF16, 8>(a.ta, a.tb, rag, pair)
+                                             : pick_pipelined<TBF16, 8>(a.ta, a.tb, rag, pair))
+                             : (a.dtype == 1 ? pick_pipelined<TF16, 4>(a.ta, a.tb, rag, pair)
+                                             : pick_pipelined<TBF16, 4>(a.ta, a.tb, rag, pair));
         const unsigned grid = (unsigned)(((tiles + 7) / 8) * 8);
         L->kernel = MM_KERNEL_GEMM_LARGE;
         L->variant = big ? LTile<8>::BM : LTile<4>::BM;

@@ -296,6 +296,48 @@ def test_large_tile_threshold(dt, b, m, n, k, kernel, variant):
     assert (rec.kernel, rec.variant) == (kernel, variant), (rec.kernel, rec.variant)
 
 
+@pytest.mark.parametrize("dt,b,m,n,k", [
+    (wl.F16, 1, 2304, 2048, 256),   # 288 tiles of 128 x 128
+    (wl.BF16, 1, 2300, 2052, 384),  # ragged m and n, 306 tiles
+    (wl.F16, 4, 1152, 1024, 256),   # 72 tiles per batch item, 288 in all
+    (wl.BF16, 1, 2432, 2304, 512),  # the steady loop runs (k / 128 = 4 rounds)
+])
+def test_pair_kernel_128_tiles(dt, b, m, n, k):
+    """NT products with more 128 x 128 tiles than CUs take the paired-stage
+    form of the pipelined kernel (two k-stages per LDS region, 128-byte
+    operand pieces). Every output against the oracle."""
+    _say(f"pair 128 dt={wl.DTYPE_NAMES[dt]} b={b} {m}x{n}x{k}")
+    case = wl.random_gemm_case(90 + k % 7, dt, b, m, n, k, False, True)
+    rec = check_gemm(case, what=f"pair {b}x{m}x{n}x{k}")
+    assert (rec.kernel, rec.variant) == (mm.MM_KERNEL_GEMM_LARGE, 128), (rec.kernel, rec.variant)
+
+
+@pytest.mark.parametrize("dt", [wl.F16, wl.BF16])
+def test_pair_kernel_ramp_exact(dt):
+    """The paired-stage form at 128 x 128 tiles, ramp inputs, bit for bit."""
+    m, n, k = 2304, 2048, 256
+    _say(f"pair 128 ramp exact dt={wl.DTYPE_NAMES[dt]} {m}x{n}x{k}")
+    a = wl.ramp(m * k, 1).reshape(1, m, k)
+    b = wl.ramp(n * k, 2).reshape(1, n, k)
+    rec = check_gemm(wl.make_gemm_case(dt, a, b, False, True), exact=True, what="pair ramp")
+    assert (rec.kernel, rec.variant) == (mm.MM_KERNEL_GEMM_LARGE, 128), (rec.kernel, rec.variant)
+
+
+def test_pair_kernel_batched_padded_offsets():
+    """The paired-stage form with padded leading dimensions, gapped batch
+    strides and element offsets on every operand (270 tiles); every output."""
+    _say("pair 128 batched padded bf16")
+    rng = np.random.default_rng(14)
+    b_, m, n, k = 3, 1280, 1152, 256
+    a = rng.standard_normal((b_, m, k))
+    bb = rng.standard_normal((b_, n, k)) / np.sqrt(k)
+    case = wl.make_gemm_case(wl.BF16, a, bb, False, True, lda=k + 64, ldb=k + 8, ldc=n + 4,
+                             off_a=8, off_b=16, off_c=4, stride_a=m * (k + 64) + 64,
+                             stride_b=n * (k + 8) + 8, stride_c=m * (n + 4) + 12)
+    rec = check_gemm(case, what="pair batched padded")
+    assert (rec.kernel, rec.variant) == (mm.MM_KERNEL_GEMM_LARGE, 128), (rec.kernel, rec.variant)
+
+
 @pytest.mark.parametrize("dt", [wl.F16, wl.BF16])
 def test_mid_tile_ramp_exact(dt):
     """128 x 128 tiles of the pipelined kernel (k = 1024: the steady loop
