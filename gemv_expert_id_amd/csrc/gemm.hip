@@ -979,26 +979,31 @@ __global__ __launch_bounds__(LThreads, TF == 8 ? 1 : 2) void gemm_mfma_large(Gem
     }
 }
 
-// NT form of the pipelined kernel with the four 32-k stages taken in pairs:
-// the two stages of a pair share one LDS region, each tile row holding 64 k
-// (128 B, chunk c at slot c ^ (row & 7)), so that one DMA instruction moves
-// 8 rows x 128 B instead of 16 rows x 64 B: HBM and L2 see 128-byte pieces
-// of each operand row. A region is refilled once both of its stages have been
-// read, which the barrier of every second k-tile establishes; the k-tiles in
-// between need no barrier. The DMA of pair P + 2 is issued during the second
-// half of k-tile 2P + 1 and the first half of k-tile 2P + 2.
-template <class T, int TF, bool RAG = false>
+// Paired-stage form of the pipelined kernel: the four 32-k stages are taken
+// in pairs. A K-contiguous operand keeps both stages of a pair in one LDS
+// region with 128-byte tile rows (chunk c at slot c ^ (row & 7)), so that one
+// DMA instruction moves 8 rows x 128 B instead of 16 rows x 64 B: HBM and L2
+// see 128-byte pieces of each row. A K-strided operand keeps its k-major
+// stages (already 2 k-rows of 2 BM bytes per instruction). A pair's stages are
+// refilled once both have been read, which the barrier of every odd k-tile
+// establishes; even k-tiles need none. The DMA of pair P + 2 is issued during
+// the second half of k-tile 2P + 1 and the first half of k-tile 2P + 2.
+template <class T, int TF, bool KA = true, bool KB = true, bool RAG = false>
 __global__ __launch_bounds__(LThreads, TF == 8 ? 1 : 2) void gemm_mfma_pair(GemmArgs a) {
-    constexpr int BM = 32 * TF;
+    using L = LTile<TF>;
+    constexpr int BM = L::BM, IPW = L::IPW;
     constexpr int HF = TF / 2;          // A fragments per half of the wave tile
     constexpr int WT = 16 * TF;         // wave tile edge
-    constexpr int RH = 2 * LBK;         // halves per LDS tile row (one pair of stages)
-    constexpr int OPH = BM * RH;        // halves per operand per region
-    constexpr int REG = 2 * OPH;        // halves per region (A then B)
+    constexpr int RH = 2 * LBK;         // halves per K-contiguous tile row (one pair of stages)
+    constexpr int OPH = BM * RH;        // halves per K-contiguous operand and region
+    constexpr int REG = ((KA ? 1 : 0) + (KB ? 1 : 0)) * OPH;  // halves per region
+    constexpr int OFB = KA ? OPH : 0;   // B's offset inside a region
     constexpr int NDP = BM / 32;        // DMA instructions per wave, operand and pair
     constexpr int LPP = 2 * NDP;        // DMA instructions per wave and pair
     constexpr int MPR = HF * TF / NDP;  // MFMAs per DMA instruction while a half-pair goes out
-    static_assert(2 * REG * sizeof(uint16_t) == LTile<TF>::LDS, "two regions fill the four-stage LDS");
+    constexpr int DSA = KA ? 1 : 2, DSB = KB ? 1 : 2;  // LDS reads per fragment
+    static_assert(2 * IPW == NDP, "a pair of k-major stages takes as many DMA instructions");
+    static_assert(2 * REG * sizeof(uint16_t) == pipelined_lds_bytes<TF>(KA, KB), "same LDS as four stages");
     extern __shared__ __attribute__((aligned(1024))) uint16_t lds[];  // [region][A | B][row][64]
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1021,57 +1026,112 @@ __global__ __launch_bounds__(LThreads, TF == 8 ? 1 : 2) void gemm_mfma_pair(Gemm
     const int nk = (int)(a.k / LBK);  // a multiple of LSTAGES, at least 2 * LSTAGES
     const int lda = (int)a.lda, ldb = (int)a.ldb;
 
-    // DMA: instruction j of a wave covers tile rows w*BM/4 + 8j + lane/8; the
-    // lane fetches the chunk that belongs at slot lane%8 of its row.
+    // DMA, K-contiguous operand: instruction j of a wave covers tile rows
+    // w*BM/4 + 8j + lane/8; the lane fetches the chunk that belongs at slot
+    // lane%8 of its row.
     const int dch = (lane & 7) ^ (lane >> 3);
     const int voa = ((w * (BM / 4) + (lane >> 3)) * lda + dch * 8) * 2;
     const int vob = ((w * (BM / 4) + (lane >> 3)) * ldb + dch * 8) * 2;
-    // Fragment reads: lane -> row lane%16 of a 16-row slab, chunk 4h + lane/16
-    // of the pair (h: the stage within the pair).
+    // K-strided operand: as in the four-stage form (32 k-rows of BM elements
+    // per stage, chunk c of row r at slot c ^ kswz(r)).
+    constexpr int CPK = BM / 8, RPK = 64 / CPK;
+    const int kr0 = (w * IPW) * RPK + lane / CPK, kr1 = kr0 + RPK, kslot = lane % CPK;
+    const int voka0 = ((lane / CPK) * lda + 8 * (kslot ^ kswz(kr0))) * 2;
+    const int voka1 = ((lane / CPK) * lda + 8 * (kslot ^ kswz(kr1))) * 2;
+    const int vokb0 = ((lane / CPK) * ldb + 8 * (kslot ^ kswz(kr0))) * 2;
+    const int vokb1 = ((lane / CPK) * ldb + 8 * (kslot ^ kswz(kr1))) * 2;
+    // Fragment reads, K-contiguous: lane -> row lane%16 of a 16-row slab,
+    // chunk 4h + lane/16 of the pair (h: the stage within the pair).
     const int lr = lane & 15, lq = lane >> 4;
     const int foff0 = lr * RH + ((lq ^ (lr & 7)) << 3);
     const int foff1 = lr * RH + (((4 + lq) ^ (lr & 7)) << 3);
+    // K-strided: two transposing reads per fragment, as in the four-stage form.
+    const int kg = lane >> 4, ks = lane & 15, kx = (ks & 3) >> 1;
+    const int kr_0 = 8 * kg + (ks >> 2), kr_1 = kr_0 + 4;
+    const int kb0 = kr_0 * 2 * BM + 8 * (ks & 1) + 16 * (kx ^ kswz(kr_0));
+    const int kb1 = kr_1 * 2 * BM + 8 * (ks & 1) + 16 * (kx ^ kswz(kr_1));
+    const int kA0 = kb0 ^ (32 * TF * wm), kA1 = kb1 ^ (32 * TF * wm);
+    const int kB0 = kb0 ^ (32 * TF * wn), kB1 = kb1 ^ (32 * TF * wn);
 
     for (int64_t b = blockIdx.y; b < a.batch; b += gridDim.y) {
-        const uint16_t* A = reinterpret_cast<const uint16_t*>(a.A) + b * a.sa + m0 * a.lda;
-        const uint16_t* B = reinterpret_cast<const uint16_t*>(a.B) + b * a.sb + n0 * a.ldb;
+        const uint16_t* A = reinterpret_cast<const uint16_t*>(a.A) + b * a.sa + (KA ? m0 * a.lda : m0);
+        const uint16_t* B = reinterpret_cast<const uint16_t*>(a.B) + b * a.sb + (KB ? n0 * a.ldb : n0);
         const int64_t mrows = RAG && a.m - m0 < BM ? a.m - m0 : BM;
         const int64_t nrows = RAG && a.n - n0 < BM ? a.n - n0 : BM;
         const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t*>(A), (short)0,
-            RAG ? (int)(((mrows - 1) * a.lda + a.k) * 2) : BM * lda * 2, 0x00020000);
+            RAG ? (int)((KA ? (mrows - 1) * a.lda + a.k : (a.k - 1) * a.lda + mrows) * 2)
+                : (KA ? BM * lda * 2 : (int)(((a.k - 1) * a.lda + BM) * 2)),
+            0x00020000);
         const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t*>(B), (short)0,
-            RAG ? (int)(((nrows - 1) * a.ldb + a.k) * 2) : BM * ldb * 2, 0x00020000);
+            RAG ? (int)((KB ? (nrows - 1) * a.ldb + a.k : (a.k - 1) * a.ldb + nrows) * 2)
+                : (KB ? BM * ldb * 2 : (int)(((a.k - 1) * a.ldb + BM) * 2)),
+            0x00020000);
 
-        // DMA instruction q (operand q % 2, rows 8 (q / 2) ..) of pair `pair` into region R.
+        // DMA instruction q (operand q % 2, its instruction q / 2) of pair
+        // `pair` into region R (stages 2R and 2R + 1).
         auto dma = [&](auto R_, int pair, auto Q_) {
-            constexpr int q = decltype(Q_)::value, j = q / 2;
-            uint16_t* dst = lds + decltype(R_)::value * REG + (q % 2) * OPH + (w * (BM / 4) + j * 8) * RH;
-            if constexpr (q % 2 == 0)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, MM_LDS(dst), 16, voa,
-                                                         (j * 8 * lda + pair * RH) * 2, 0, 0);
-            else
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, MM_LDS(dst), 16, vob,
-                                                         (j * 8 * ldb + pair * RH) * 2, 0, 0);
+            constexpr int R = decltype(R_)::value, q = decltype(Q_)::value, j = q / 2;
+            constexpr int h = j / IPW, jj = j % IPW;  // k-major form: stage 2R + h, instruction jj
+            const int kr = (w * IPW + jj) * RPK;
+            if constexpr (q % 2 == 0) {
+                if constexpr (KA)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        ra, MM_LDS(lds + R * REG + (w * (BM / 4) + j * 8) * RH), 16, voa,
+                        (j * 8 * lda + pair * RH) * 2, 0, 0);
+                else
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        ra, MM_LDS((kmajor_stage<BM * LBK, 2 * R + h, 0>() + kr * BM)), 16,
+                        jj % 2 ? voka1 : voka0, ((2 * pair + h) * LBK + kr) * lda * 2, 0, 0);
+            } else {
+                if constexpr (KB)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        rb, MM_LDS(lds + R * REG + OFB + (w * (BM / 4) + j * 8) * RH), 16, vob,
+                        (j * 8 * ldb + pair * RH) * 2, 0, 0);
+                else
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        rb, MM_LDS((kmajor_stage<BM * LBK, 2 * R + h, 1>() + kr * BM)), 16,
+                        jj % 2 ? vokb1 : vokb0, ((2 * pair + h) * LBK + kr) * ldb * 2, 0, 0);
+            }
         };
         f32x4 acc[TF][TF];
 #pragma unroll
         for (int i = 0; i < TF; ++i)
 #pragma unroll
             for (int j = 0; j < TF; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // Stage s of the ring: region s / 2, half s % 2.
+        // Stage s of the ring: region s / 2, half s % 2 (K-contiguous), or
+        // k-major array s (K-strided).
         auto rda = [&](auto S_, int hh, u32x4 (&fa)[HF]) {
             constexpr int s = decltype(S_)::value;
-            const uint16_t* sa = lds + (s / 2) * REG + (wm * WT + hh * (WT / 2)) * RH + (s % 2 ? foff1 : foff0);
+            if constexpr (KA) {
+                const uint16_t* sa = lds + (s / 2) * REG + (wm * WT + hh * (WT / 2)) * RH + (s % 2 ? foff1 : foff0);
 #pragma unroll
-            for (int i = 0; i < HF; ++i) fa[i] = *reinterpret_cast<const u32x4*>(sa + i * 16 * RH);
+                for (int i = 0; i < HF; ++i) fa[i] = *reinterpret_cast<const u32x4*>(sa + i * 16 * RH);
+            } else {
+                const char* sa = reinterpret_cast<const char*>(kmajor_stage<BM * LBK, s, 0>());
+#pragma unroll
+                for (int i = 0; i < HF; ++i) {
+                    const int f = 16 * TF * hh + 32 * i;
+                    const u32x2 lo = lds_read_tr16(sa + (kA0 ^ f)), hi = lds_read_tr16(sa + (kA1 ^ f));
+                    fa[i] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+                }
+            }
         };
         auto rdb = [&](auto S_, u32x4 (&fb)[TF]) {
             constexpr int s = decltype(S_)::value;
-            const uint16_t* sb = lds + (s / 2) * REG + OPH + wn * WT * RH + (s % 2 ? foff1 : foff0);
+            if constexpr (KB) {
+                const uint16_t* sb = lds + (s / 2) * REG + OFB + wn * WT * RH + (s % 2 ? foff1 : foff0);
 #pragma unroll
-            for (int j = 0; j < TF; ++j) fb[j] = *reinterpret_cast<const u32x4*>(sb + j * 16 * RH);
+                for (int j = 0; j < TF; ++j) fb[j] = *reinterpret_cast<const u32x4*>(sb + j * 16 * RH);
+            } else {
+                const char* sb = reinterpret_cast<const char*>(kmajor_stage<BM * LBK, s, 1>());
+#pragma unroll
+                for (int j = 0; j < TF; ++j) {
+                    const u32x2 lo = lds_read_tr16(sb + (kB0 ^ (32 * j))), hi = lds_read_tr16(sb + (kB1 ^ (32 * j)));
+                    fb[j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+                }
+            }
         };
         auto mm = [&](int hh, const u32x4 (&fa)[HF], const u32x4 (&fb)[TF]) {
 #pragma unroll
@@ -1090,8 +1150,8 @@ __global__ __launch_bounds__(LThreads, TF == 8 ? 1 : 2) void gemm_mfma_pair(Gemm
             }
         };
         u32x4 fa0[HF], fa1[HF], fb0[TF], fb1[TF];
-        // k-tile kt in stage S_ (kt % 4). DQ: 2 = second half of pair PQ in
-        // the first half (even kt), 1 = first half of pair PQ in the second
+        // k-tile kt in stage S_ (kt % 4). DQ: 2 = second half of pair pq in
+        // the first half (even kt), 1 = first half of pair pq in the second
         // (odd kt), 0 = none. NEXT: tile kt+1 exists; an odd kt then waits
         // for all DMA (pair (kt+1)/2) and holds the barrier.
         auto ktile = [&](auto S_, auto NEXT, auto DQ, int pq) {
@@ -1106,7 +1166,7 @@ __global__ __launch_bounds__(LThreads, TF == 8 ? 1 : 2) void gemm_mfma_pair(Gemm
                 static_for(std::make_integer_sequence<int, NDP>{},
                            [&](auto Q_) { dma(ic<RQ>{}, pq, ic<NDP + decltype(Q_)::value>{}); });
             mm(0, fa0, fb);
-            weave(ic<HF>{}, dq == 2);
+            weave(ic<HF * DSA>{}, dq == 2);
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (nx) {
                 if constexpr (s % 2 == 1) {
@@ -1120,7 +1180,7 @@ __global__ __launch_bounds__(LThreads, TF == 8 ? 1 : 2) void gemm_mfma_pair(Gemm
                 static_for(std::make_integer_sequence<int, NDP>{},
                            [&](auto Q_) { dma(ic<RQ>{}, pq, ic<decltype(Q_)::value>{}); });
             mm(1, fa1, fb);
-            weave(ic<nx ? HF + TF : 0>{}, dq == 1);
+            weave(ic<nx ? HF * DSA + TF * DSB : 0>{}, dq == 1);
             __builtin_amdgcn_sched_barrier(0);
         };
 
@@ -1177,7 +1237,7 @@ __global__ __launch_bounds__(LThreads, TF == 8 ? 1 : 2) void gemm_mfma_pair(Gemm
                 }
             }
         }
-        // The next batch's prologue overwrites every region.
+        // The next batch's prologue overwrites every stage.
         __syncthreads();
     }
 }
@@ -1357,12 +1417,18 @@ __global__ __launch_bounds__(kWave) void gemm_f32_mfma_small(GemmArgs a) {
 }
 
 // The pipelined kernel for a transpose layout: A K-contiguous unless ta, B
-// K-contiguous when tb; NT takes the paired-stage form when `pair`.
+// K-contiguous when tb; the paired-stage form when `pair` (NT, and NN / TT
+// that are not ragged).
 template <class T, int TF, bool RAG>
 const void* pick_pipelined(bool ta, bool tb, bool pair) {
-    if (!ta && tb)
-        return pair ? reinterpret_cast<const void*>(&gemm_mfma_pair<T, TF, RAG>)
-                    : reinterpret_cast<const void*>(&gemm_mfma_large<T, TF, true, true, RAG>);
+    if (pair && !(ta && !tb)) {  // (the launcher never pairs TN, nor ragged NN / TT)
+        if (!ta && tb) return reinterpret_cast<const void*>(&gemm_mfma_pair<T, TF, true, true, RAG>);
+        if constexpr (!RAG) {
+            if (!ta) return reinterpret_cast<const void*>(&gemm_mfma_pair<T, TF, true, false, false>);
+            return reinterpret_cast<const void*>(&gemm_mfma_pair<T, TF, false, true, false>);
+        }
+    }
+    if (!ta && tb) return reinterpret_cast<const void*>(&gemm_mfma_large<T, TF, true, true, RAG>);
     if (!ta) return reinterpret_cast<const void*>(&gemm_mfma_large<T, TF, true, false, RAG>);
     if (tb) return reinterpret_cast<const void*>(&gemm_mfma_large<T, TF, false, true, RAG>);
     return reinterpret_cast<const void*>(&gemm_mfma_large<T, TF, false, false, RAG>);
@@ -1428,13 +1494,18 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, Launched* L) {
         const int edge = big ? LTile<8>::BM : LTile<4>::BM;
         const bool rag = a.m % edge != 0 || a.n % edge != 0;
         const int64_t tiles = big ? big_tiles : ((a.m + 127) / 128) * ((a.n + 127) / 128);
-        // NT: the paired-stage form (128-byte operand pieces, a barrier every
-        // second k-tile, DMA one k-tile less ahead). Measured on MI355X: faster
-        // for 256 x 256 tiles at every measured shape and for 128 x 128 tiles
-        // with more of them than CUs (two resident blocks per CU then hide the
-        // shorter lookahead); with at most one 128 x 128 tile per CU the
-        // four-stage form is faster.
-        const bool pair = big || tiles * a.batch > 256;
+        // The paired-stage form (128-byte pieces of K-contiguous operands, a
+        // barrier every second k-tile, DMA one k-tile less ahead). Measured on
+        // MI355X: for NT faster with 256 x 256 tiles at every measured shape
+        // and with 128 x 128 tiles when there are more of them than CUs (two
+        // resident blocks per CU then hide the shorter lookahead); with at
+        // most one 128 x 128 tile per CU the four-stage form is faster. NN and
+        // TT (one K-strided operand) gain 2-3% at 4096^3 and 8192^3, but a
+        // ragged NN product lost 9%, so ragged NN / TT keep the four-stage
+        // form; TN (both K-strided) spills registers in the paired form's loop
+        // and keeps it too.
+        const bool ka = !a.ta, kb = a.tb;  // operands K-contiguous
+        const bool pair = (big || tiles * a.batch > 256) && ((ka && kb) || (ka != kb && !rag));
         const void* fn = big ? (a.dtype == 1 ? pick_pipelined<TF16, 8>(a.ta, a.tb, rag, pair)
                                              : pick_pipelined<TBF16, 8>(a.ta, a.tb, rag, pair))
                              : (a.dtype == 1 ? pick_pipelined<TF16, 4>(a.ta, a.tb, rag, pair)
@@ -1442,7 +1513,6 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, Launched* L) {
         const unsigned grid = (unsigned)(((tiles + 7) / 8) * 8);
         L->kernel = MM_KERNEL_GEMM_LARGE;
         L->variant = big ? LTile<8>::BM : LTile<4>::BM;
-        const bool ka = !a.ta, kb = a.tb;  // operands K-contiguous
         return hipLaunchKernel(fn, dim3(grid, gy), dim3(LThreads), args,
                                big ? pipelined_lds_bytes<8>(ka, kb) : pipelined_lds_bytes<4>(ka, kb), s);
     }

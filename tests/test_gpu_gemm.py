@@ -296,18 +296,21 @@ def test_large_tile_threshold(dt, b, m, n, k, kernel, variant):
     assert (rec.kernel, rec.variant) == (kernel, variant), (rec.kernel, rec.variant)
 
 
-@pytest.mark.parametrize("dt,b,m,n,k", [
-    (wl.F16, 1, 2304, 2048, 256),   # 288 tiles of 128 x 128
-    (wl.BF16, 1, 2300, 2052, 384),  # ragged m and n, 306 tiles
-    (wl.F16, 4, 1152, 1024, 256),   # 72 tiles per batch item, 288 in all
-    (wl.BF16, 1, 2432, 2304, 512),  # the steady loop runs (k / 128 = 4 rounds)
+@pytest.mark.parametrize("dt,ta,tb,b,m,n,k", [
+    (wl.F16, False, True, 1, 2304, 2048, 256),   # NT, 288 tiles of 128 x 128
+    (wl.BF16, False, True, 1, 2300, 2052, 384),  # NT, ragged m and n, 306 tiles
+    (wl.F16, False, True, 4, 1152, 1024, 256),   # NT, 72 tiles per batch item, 288 in all
+    (wl.BF16, False, True, 1, 2432, 2304, 512),  # NT, the steady loop runs (k / 128 = 4 rounds)
+    (wl.F16, False, False, 1, 2304, 2048, 512),  # NN: B K-strided
+    (wl.BF16, True, True, 2, 1152, 1280, 256),   # TT: A K-strided, 180 tiles per item
 ])
-def test_pair_kernel_128_tiles(dt, b, m, n, k):
-    """NT products with more 128 x 128 tiles than CUs take the paired-stage
+def test_pair_kernel_128_tiles(dt, ta, tb, b, m, n, k):
+    """Products with more 128 x 128 tiles than CUs take the paired-stage
     form of the pipelined kernel (two k-stages per LDS region, 128-byte
-    operand pieces). Every output against the oracle."""
-    _say(f"pair 128 dt={wl.DTYPE_NAMES[dt]} b={b} {m}x{n}x{k}")
-    case = wl.random_gemm_case(90 + k % 7, dt, b, m, n, k, False, True)
+    pieces of K-contiguous operands; NT, and NN / TT when not ragged).
+    Every output against the oracle."""
+    _say(f"pair 128 dt={wl.DTYPE_NAMES[dt]} ta={int(ta)} tb={int(tb)} b={b} {m}x{n}x{k}")
+    case = wl.random_gemm_case(90 + k % 7, dt, b, m, n, k, ta, tb)
     rec = check_gemm(case, what=f"pair {b}x{m}x{n}x{k}")
     assert (rec.kernel, rec.variant) == (mm.MM_KERNEL_GEMM_LARGE, 128), (rec.kernel, rec.variant)
 
@@ -423,10 +426,12 @@ def test_pipelined_layouts_batched_padded(ta, tb):
 
 @pytest.mark.parametrize("dt", [wl.F16, wl.BF16])
 @pytest.mark.parametrize("ta,tb", LAYOUTS[1:])
-def test_pipelined_layouts_256_tiles(dt, ta, tb):
+@pytest.mark.parametrize("k", [256, 512])
+def test_pipelined_layouts_256_tiles(dt, ta, tb, k):
     """NN, TN and TT products large enough for 256 x 256 tiles (192 of them),
-    sampled against the oracle."""
-    m, n, k = 3072, 4096, 256
+    sampled against the oracle (NN and TT on the paired-stage form; k = 512
+    runs its steady loop)."""
+    m, n = 3072, 4096
     _say(f"pipelined 256 layouts dt={wl.DTYPE_NAMES[dt]} ta={int(ta)} tb={int(tb)} {m}x{n}x{k}")
     case = wl.random_gemm_case(64 + 2 * ta + tb, dt, 1, m, n, k, ta, tb)
     _sampled_check(case, 4096, 15, kernel=mm.MM_KERNEL_GEMM_LARGE, variant=256)
