@@ -1512,7 +1512,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, Launched* L) {
                                              : pick_pipelined<TBF16, 4>(a.ta, a.tb, rag, pair));
         const unsigned grid = (unsigned)(((tiles + 7) / 8) * 8);
         L->kernel = MM_KERNEL_GEMM_LARGE;
-        L->variant = big ? LTile<8>::BM : LTile<4>::BM;
+        L->variant = (big ? LTile<8>::BM : LTile<4>::BM) + (pair ? 1 : 0);
         return hipLaunchKernel(fn, dim3(grid, gy), dim3(LThreads), args,
                                big ? pipelined_lds_bytes<8>(ka, kb) : pipelined_lds_bytes<4>(ka, kb), s);
     }

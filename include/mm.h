@@ -122,7 +122,9 @@ typedef struct {
                                  a panel's B tiles are split over, plus 256
                                  times the panel height in rows (64 or 128);
                                  for MM_KERNEL_GEMM_LARGE the tile edge
-                                 (256 or 128); 0 for every other family */
+                                 (256 or 128), plus 1 for the paired-stage
+                                 form (two k-stages per LDS region); 0 for
+                                 every other family */
 } mm_receipt;
 
 /* ------------------------------------------------------------------------ */

@@ -234,7 +234,9 @@ def _sampled_check(case, n_samples, seed, exact=False, kernel=None, variant=None
     if kernel is not None:
         assert rec.kernel == kernel, f"kernel {rec.kernel}, expected {kernel}"
     if variant is not None:
-        assert rec.variant == variant, f"variant {rec.variant}, expected {variant}"
+        # (the large kernel's low bit names its paired-stage form)
+        got = rec.variant & ~1 if rec.kernel == mm.MM_KERNEL_GEMM_LARGE else rec.variant
+        assert got == variant, f"variant {rec.variant}, expected {variant}"
     bits = run.c_bits()
     rng = np.random.default_rng(seed)
     bs = rng.integers(0, case.batch, n_samples)
@@ -293,7 +295,8 @@ def test_large_tile_threshold(dt, b, m, n, k, kernel, variant):
     _say(f"large-tile threshold dt={wl.DTYPE_NAMES[dt]} b={b} m={m} n={n} k={k}")
     case = wl.random_gemm_case(46 + k, dt, b, m, n, k, False, True)
     rec = check_gemm(case, what=f"threshold {b}x{m}x{n}x{k}")
-    assert (rec.kernel, rec.variant) == (kernel, variant), (rec.kernel, rec.variant)
+    got = rec.variant & ~1 if rec.kernel == mm.MM_KERNEL_GEMM_LARGE else rec.variant
+    assert (rec.kernel, got) == (kernel, variant), (rec.kernel, rec.variant)
 
 
 @pytest.mark.parametrize("dt,ta,tb,b,m,n,k", [
@@ -302,7 +305,7 @@ def test_large_tile_threshold(dt, b, m, n, k, kernel, variant):
     (wl.F16, False, True, 4, 1152, 1024, 256),   # NT, 72 tiles per batch item, 288 in all
     (wl.BF16, False, True, 1, 2432, 2304, 512),  # NT, the steady loop runs (k / 128 = 4 rounds)
     (wl.F16, False, False, 1, 2304, 2048, 512),  # NN: B K-strided
-    (wl.BF16, True, True, 2, 1152, 1280, 256),   # TT: A K-strided, 180 tiles per item
+    (wl.BF16, True, True, 2, 1152, 2304, 256),   # TT: A K-strided, 162 tiles per item, 324 in all
 ])
 def test_pair_kernel_128_tiles(dt, ta, tb, b, m, n, k):
     """Products with more 128 x 128 tiles than CUs take the paired-stage
@@ -312,7 +315,7 @@ def test_pair_kernel_128_tiles(dt, ta, tb, b, m, n, k):
     _say(f"pair 128 dt={wl.DTYPE_NAMES[dt]} ta={int(ta)} tb={int(tb)} b={b} {m}x{n}x{k}")
     case = wl.random_gemm_case(90 + k % 7, dt, b, m, n, k, ta, tb)
     rec = check_gemm(case, what=f"pair {b}x{m}x{n}x{k}")
-    assert (rec.kernel, rec.variant) == (mm.MM_KERNEL_GEMM_LARGE, 128), (rec.kernel, rec.variant)
+    assert (rec.kernel, rec.variant) == (mm.MM_KERNEL_GEMM_LARGE, 129), (rec.kernel, rec.variant)
 
 
 @pytest.mark.parametrize("dt", [wl.F16, wl.BF16])
@@ -323,7 +326,7 @@ def test_pair_kernel_ramp_exact(dt):
     a = wl.ramp(m * k, 1).reshape(1, m, k)
     b = wl.ramp(n * k, 2).reshape(1, n, k)
     rec = check_gemm(wl.make_gemm_case(dt, a, b, False, True), exact=True, what="pair ramp")
-    assert (rec.kernel, rec.variant) == (mm.MM_KERNEL_GEMM_LARGE, 128), (rec.kernel, rec.variant)
+    assert (rec.kernel, rec.variant) == (mm.MM_KERNEL_GEMM_LARGE, 129), (rec.kernel, rec.variant)
 
 
 def test_pair_kernel_batched_padded_offsets():
@@ -338,7 +341,34 @@ def test_pair_kernel_batched_padded_offsets():
                              off_a=8, off_b=16, off_c=4, stride_a=m * (k + 64) + 64,
                              stride_b=n * (k + 8) + 8, stride_c=m * (n + 4) + 12)
     rec = check_gemm(case, what="pair batched padded")
-    assert (rec.kernel, rec.variant) == (mm.MM_KERNEL_GEMM_LARGE, 128), (rec.kernel, rec.variant)
+    assert (rec.kernel, rec.variant) == (mm.MM_KERNEL_GEMM_LARGE, 129), (rec.kernel, rec.variant)
+
+
+@pytest.mark.parametrize("ta,tb,b,m,n,k,variant", [
+    (False, True, 1, 3072, 4096, 256, 257),   # NT, 256 x 256 tiles: paired
+    (False, True, 1, 2048, 4096, 256, 129),   # NT, 128 tiles of 256 (< 192): 512 of 128 x 128, paired
+    (False, True, 1, 1024, 2048, 256, 128),   # NT, 128 tiles of 128 x 128: four stages
+    (False, True, 1, 2304, 2048, 256, 129),   # NT, 288 tiles of 128 x 128: paired
+    (False, True, 1, 4000, 3000, 256, 257),   # NT ragged: paired
+    (False, False, 1, 3072, 4096, 256, 257),  # NN: paired
+    (False, False, 1, 4000, 3000, 256, 256),  # NN ragged: four stages
+    (True, True, 2, 1152, 2304, 256, 129),    # TT, 324 tiles of 128 x 128: paired
+    (True, True, 2, 1152, 1280, 256, 128),    # TT, 180 tiles of 128 x 128: four stages
+    (True, True, 1, 1000, 2304, 256, 128),    # TT ragged: four stages
+    (True, False, 1, 3072, 4096, 256, 256),   # TN: four stages
+])
+def test_pipelined_form_rule(ta, tb, b, m, n, k, variant):
+    """The receipt names the pipelined kernel's tile edge and, in its low bit,
+    the paired-stage form: NT with 256 x 256 tiles or more than 256 tiles of
+    128 x 128; NN and TT the same unless ragged; TN never."""
+    import torch
+    from gpu_util import GemmRun
+    _say(f"pipelined form rule ta={int(ta)} tb={int(tb)} b={b} {m}x{n}x{k}")
+    case = wl.random_gemm_case(98, wl.F16, b, m, n, k, ta, tb)
+    run = GemmRun(case)
+    rec = run.run()
+    torch.cuda.synchronize()
+    assert (rec.kernel, rec.variant) == (mm.MM_KERNEL_GEMM_LARGE, variant), (rec.kernel, rec.variant)
 
 
 @pytest.mark.parametrize("dt", [wl.F16, wl.BF16])
@@ -350,7 +380,7 @@ def test_mid_tile_ramp_exact(dt):
     a = wl.ramp(m * k, 1).reshape(1, m, k)
     b = wl.ramp(n * k, 2).reshape(1, n, k)
     rec = check_gemm(wl.make_gemm_case(dt, a, b, False, True), exact=True, what="mid ramp")
-    assert (rec.kernel, rec.variant) == (mm.MM_KERNEL_GEMM_LARGE, 128), (rec.kernel, rec.variant)
+    assert (rec.kernel, rec.variant & ~1) == (mm.MM_KERNEL_GEMM_LARGE, 128), (rec.kernel, rec.variant)
 
 
 @pytest.mark.parametrize("dt", [wl.F16, wl.BF16])
@@ -366,7 +396,7 @@ def test_mid_tile_batched_padded_offsets(dt):
                              off_a=8, off_b=16, off_c=4, stride_a=m * (k + 64) + 64,
                              stride_b=n * (k + 8) + 8, stride_c=m * (n + 4) + 12)
     rec = check_gemm(case, what="mid batched padded")
-    assert (rec.kernel, rec.variant) == (mm.MM_KERNEL_GEMM_LARGE, 128), (rec.kernel, rec.variant)
+    assert (rec.kernel, rec.variant & ~1) == (mm.MM_KERNEL_GEMM_LARGE, 128), (rec.kernel, rec.variant)
 
 
 def test_mid_tile_broadcast_b():
@@ -380,7 +410,7 @@ def test_mid_tile_broadcast_b():
                              broadcast_b=True)
     assert case.stride_b == 0
     rec = check_gemm(case, what="mid broadcast")
-    assert (rec.kernel, rec.variant) == (mm.MM_KERNEL_GEMM_LARGE, 128), (rec.kernel, rec.variant)
+    assert (rec.kernel, rec.variant & ~1) == (mm.MM_KERNEL_GEMM_LARGE, 128), (rec.kernel, rec.variant)
 
 
 LAYOUTS = [(False, True), (False, False), (True, True), (True, False)]  # (trans_a, trans_b)
@@ -397,11 +427,11 @@ def test_pipelined_layouts_128_tiles(dt, ta, tb):
     _say(f"pipelined 128 layouts dt={wl.DTYPE_NAMES[dt]} ta={int(ta)} tb={int(tb)} {m}x{n}x{k}")
     case = wl.random_gemm_case(60 + 2 * ta + tb, dt, 1, m, n, k, ta, tb)
     rec = check_gemm(case, what=f"layout {int(ta)}{int(tb)}")
-    assert (rec.kernel, rec.variant) == (mm.MM_KERNEL_GEMM_LARGE, 128), (rec.kernel, rec.variant)
+    assert (rec.kernel, rec.variant & ~1) == (mm.MM_KERNEL_GEMM_LARGE, 128), (rec.kernel, rec.variant)
     a = wl.ramp(m * k, 1).reshape((1, k, m) if ta else (1, m, k))
     b = wl.ramp(n * k, 2).reshape((1, n, k) if tb else (1, k, n))
     rec = check_gemm(wl.make_gemm_case(dt, a, b, ta, tb), exact=True, what="layout ramp")
-    assert (rec.kernel, rec.variant) == (mm.MM_KERNEL_GEMM_LARGE, 128), (rec.kernel, rec.variant)
+    assert (rec.kernel, rec.variant & ~1) == (mm.MM_KERNEL_GEMM_LARGE, 128), (rec.kernel, rec.variant)
 
 
 @pytest.mark.parametrize("ta,tb", LAYOUTS)
@@ -421,7 +451,7 @@ def test_pipelined_layouts_batched_padded(ta, tb):
                              off_b=16, off_c=4, stride_a=rows_a * lda + 64,
                              stride_b=rows_b * ldb + 8, stride_c=m * (n + 4) + 12)
     rec = check_gemm(case, what="layouts batched padded")
-    assert (rec.kernel, rec.variant) == (mm.MM_KERNEL_GEMM_LARGE, 128), (rec.kernel, rec.variant)
+    assert (rec.kernel, rec.variant & ~1) == (mm.MM_KERNEL_GEMM_LARGE, 128), (rec.kernel, rec.variant)
 
 
 @pytest.mark.parametrize("dt", [wl.F16, wl.BF16])
@@ -454,7 +484,7 @@ def test_pipelined_ragged_edges(dt, ta, tb, b, m, n, k, variant):
     _say(f"pipelined ragged dt={wl.DTYPE_NAMES[dt]} ta={int(ta)} tb={int(tb)} b={b} {m}x{n}x{k}")
     case = wl.random_gemm_case(70 + m % 7 + n % 5, dt, b, m, n, k, ta, tb)
     rec = check_gemm(case, what=f"ragged {b}x{m}x{n}x{k}")
-    assert (rec.kernel, rec.variant) == (mm.MM_KERNEL_GEMM_LARGE, variant), (rec.kernel, rec.variant)
+    assert (rec.kernel, rec.variant & ~1) == (mm.MM_KERNEL_GEMM_LARGE, variant), (rec.kernel, rec.variant)
 
 
 def test_pipelined_ragged_ramp_exact():
@@ -464,7 +494,7 @@ def test_pipelined_ragged_ramp_exact():
     a = wl.ramp(m * k, 1).reshape(1, m, k)
     b = wl.ramp(n * k, 2).reshape(1, n, k)
     rec = check_gemm(wl.make_gemm_case(wl.F16, a, b, False, True), exact=True, what="ragged ramp")
-    assert (rec.kernel, rec.variant) == (mm.MM_KERNEL_GEMM_LARGE, 128), (rec.kernel, rec.variant)
+    assert (rec.kernel, rec.variant & ~1) == (mm.MM_KERNEL_GEMM_LARGE, 128), (rec.kernel, rec.variant)
 
 
 @pytest.mark.parametrize("ta,tb", [(False, True), (False, False)])
@@ -510,7 +540,7 @@ def test_large_tile_route_full_compare(dt, seed):
     case = wl.random_gemm_case(seed, dt, 1, 4096, 8192, 256, False, True, dist="uniform")
     run = GemmRun(case)
     rec = run.run()
-    assert rec.kernel == mm.MM_KERNEL_GEMM_LARGE and rec.variant == 256, (rec.kernel, rec.variant)
+    assert rec.kernel == mm.MM_KERNEL_GEMM_LARGE and rec.variant & ~1 == 256, (rec.kernel, rec.variant)
     bits = run.c_bits()
     got, mask = run.logical_c(bits)
     run.check_untouched(bits, mask)
