@@ -692,6 +692,77 @@ constexpr size_t pipelined_lds_bytes(bool ka, bool kb) {
                     : (ka || kb ? (size_t)LSTAGES * LTile<TF>::BM * LBK * sizeof(uint16_t) : 0);
 }
 
+// Tile of this block in the pipelined kernels' order: groups of LGM
+// tile-rows, column-major inside a group, each XCD (blockIdx % 8) taking a
+// contiguous run so that its resident blocks share A and B panels in its L2.
+// False when the block has no tile.
+template <int BM, bool RAG>
+__device__ __forceinline__ bool pipelined_tile(const GemmArgs& a, int64_t& m0, int64_t& n0) {
+    const int64_t tiles_m = RAG ? (a.m + BM - 1) / BM : a.m / BM;
+    const int64_t tiles_n = RAG ? (a.n + BM - 1) / BM : a.n / BM;
+    const int64_t ntiles = tiles_m * tiles_n;
+    const int64_t bid = blockIdx.x;
+    const int64_t per_xcd = (ntiles + 7) / 8;
+    const int64_t t = (bid % 8) * per_xcd + bid / 8;
+    if (t >= ntiles) return false;
+    const int64_t group = t / (LGM * tiles_n);
+    const int64_t first_m = group * LGM;
+    const int64_t gsize = tiles_m - first_m < LGM ? tiles_m - first_m : LGM;
+    m0 = (first_m + (t % (LGM * tiles_n)) % gsize) * BM;
+    n0 = ((t % (LGM * tiles_n)) / gsize) * BM;
+    return true;
+}
+
+// Buffer resource over one operand's tile of batch item b: BM rows from row0
+// (K-contiguous: rows of k elements ld apart) or BM columns from column col0
+// of k rows ld apart (K-strided). With RAG the range stops at the operand's
+// true extent (`rows` of the BM inside it), so reads past it return zeros.
+template <int BM, bool KC, bool RAG>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t pipelined_rsrc(const void* base, int64_t batch_off,
+                                                                 int64_t first, int64_t ld, int64_t k,
+                                                                 int64_t rows) {
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(base) + batch_off + (KC ? first * ld : first);
+    const int bytes = RAG ? (int)((KC ? (rows - 1) * ld + k : (k - 1) * ld + rows) * 2)
+                          : (KC ? BM * (int)ld * 2 : (int)(((k - 1) * ld + BM) * 2));
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p), (short)0, bytes, 0x00020000);
+}
+
+// Epilogue of the pipelined kernels: the wave's TF x TF fragments (lane holds
+// C[m = 16i-slab base + lane%16][n = 16j-slab base + 4 (lane/16) + q]) into C
+// of batch item b as alpha * acc + beta * C_old; four-element stores when
+// beta == 0 and the piece lies inside C, element stores otherwise.
+template <class T, int TF, bool RAG>
+__device__ __forceinline__ void pipelined_store(const GemmArgs& a, int64_t b, int64_t m0, int64_t n0,
+                                                int wm, int wn, int lr, int lq, const f32x4 (&acc)[TF][TF]) {
+    constexpr int WT = 16 * TF;
+    uint16_t* C = reinterpret_cast<uint16_t*>(a.C) + b * a.sc;
+#pragma unroll
+    for (int i = 0; i < TF; ++i) {
+        const int64_t gm = m0 + wm * WT + i * 16 + lr;
+        if (RAG && gm >= a.m) continue;
+#pragma unroll
+        for (int j = 0; j < TF; ++j) {
+            const int64_t gn = n0 + wn * WT + j * 16 + lq * 4;
+            uint16_t* dst = C + gm * a.ldc + gn;
+            if (RAG && gn + 4 > a.n) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (gn + q < a.n) dst[q] = axpby<T>(acc[i][j][q], a.alpha, a.beta, dst + q);
+            } else if (a.beta == 0.f) {
+                u32x2 v;
+                v[0] = (uint32_t)narrow(T{}, a.alpha * acc[i][j][0]) |
+                       ((uint32_t)narrow(T{}, a.alpha * acc[i][j][1]) << 16);
+                v[1] = (uint32_t)narrow(T{}, a.alpha * acc[i][j][2]) |
+                       ((uint32_t)narrow(T{}, a.alpha * acc[i][j][3]) << 16);
+                *reinterpret_cast<u32x2*>(dst) = v;
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) dst[q] = axpby<T>(acc[i][j][q], a.alpha, a.beta, dst + q);
+            }
+        }
+    }
+}
+
 // RAG: m or n not a multiple of the tile edge. Edge tiles then read through
 // buffer resources cut at the operand's true extent (rows or columns past it
 // read zeros, and any other data in padding columns only feeds outputs that
@@ -709,21 +780,8 @@ __global__ __launch_bounds__(LThreads, TF == 8 ? 1 : 2) void gemm_mfma_large(Gem
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = w >> 1, wn = w & 1;
-    const int64_t tiles_m = RAG ? (a.m + BM - 1) / BM : a.m / BM;
-    const int64_t tiles_n = RAG ? (a.n + BM - 1) / BM : a.n / BM;
-    const int64_t ntiles = tiles_m * tiles_n;
-
-    // XCD-aware grouped tile order.
-    const int64_t bid = blockIdx.x;
-    const int64_t per_xcd = (ntiles + 7) / 8;
-    const int64_t t = (bid % 8) * per_xcd + bid / 8;
-    if (t >= ntiles) return;
-    const int64_t group = t / (LGM * tiles_n);
-    const int64_t first_m = group * LGM;
-    const int64_t gsize = tiles_m - first_m < LGM ? tiles_m - first_m : LGM;
-    const int64_t tm = first_m + (t % (LGM * tiles_n)) % gsize;
-    const int64_t tn = (t % (LGM * tiles_n)) / gsize;
-    const int64_t m0 = tm * BM, n0 = tn * BM;
+    int64_t m0, n0;
+    if (!pipelined_tile<BM, RAG>(a, m0, n0)) return;
     const int nk = (int)(a.k / LBK);  // a multiple of LSTAGES, at least 2 * LSTAGES
     const int lda = (int)a.lda, ldb = (int)a.ldb;
 
@@ -774,21 +832,11 @@ __global__ __launch_bounds__(LThreads, TF == 8 ? 1 : 2) void gemm_mfma_large(Gem
     };
 
     for (int64_t b = blockIdx.y; b < a.batch; b += gridDim.y) {
-        const uint16_t* A = reinterpret_cast<const uint16_t*>(a.A) + b * a.sa + (KA ? m0 * a.lda : m0);
-        const uint16_t* B = reinterpret_cast<const uint16_t*>(a.B) + b * a.sb + (KB ? n0 * a.ldb : n0);
         // Rows (K-contiguous) or columns (K-strided) of this tile inside the operand.
         const int64_t mrows = RAG && a.m - m0 < BM ? a.m - m0 : BM;
         const int64_t nrows = RAG && a.n - n0 < BM ? a.n - n0 : BM;
-        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(A), (short)0,
-            RAG ? (int)((KA ? (mrows - 1) * a.lda + a.k : (a.k - 1) * a.lda + mrows) * 2)
-                : (KA ? BM * lda * 2 : (int)(((a.k - 1) * a.lda + BM) * 2)),
-            0x00020000);
-        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(B), (short)0,
-            RAG ? (int)((KB ? (nrows - 1) * a.ldb + a.k : (a.k - 1) * a.ldb + nrows) * 2)
-                : (KB ? BM * ldb * 2 : (int)(((a.k - 1) * a.ldb + BM) * 2)),
-            0x00020000);
+        const __amdgpu_buffer_rsrc_t ra = pipelined_rsrc<BM, KA, RAG>(a.A, b * a.sa, m0, a.lda, a.k, mrows);
+        const __amdgpu_buffer_rsrc_t rb = pipelined_rsrc<BM, KB, RAG>(a.B, b * a.sb, n0, a.ldb, a.k, nrows);
 
         // Half p (instructions IPW/2 * p .. of each operand) of k-tile kt into a stage.
         auto dma_half = [&](auto S_, int kt, int p) {
@@ -947,33 +995,7 @@ __global__ __launch_bounds__(LThreads, TF == 8 ? 1 : 2) void gemm_mfma_large(Gem
                   ic<LLPS * (LSTAGES - 2 - s < 0 ? 0 : LSTAGES - 2 - s)>{}, kt0 + s);
         });
 
-        // Lane holds C[m = 16i-slab base + lane%16][n = 16j-slab base + 4 (lane/16) + q].
-        uint16_t* C = reinterpret_cast<uint16_t*>(a.C) + b * a.sc;
-#pragma unroll
-        for (int i = 0; i < TF; ++i) {
-            const int64_t gm = m0 + wm * WT + i * 16 + lr;
-            if (RAG && gm >= a.m) continue;
-#pragma unroll
-            for (int j = 0; j < TF; ++j) {
-                const int64_t gn = n0 + wn * WT + j * 16 + lq * 4;
-                uint16_t* dst = C + gm * a.ldc + gn;
-                if (RAG && gn + 4 > a.n) {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        if (gn + q < a.n) dst[q] = axpby<T>(acc[i][j][q], a.alpha, a.beta, dst + q);
-                } else if (a.beta == 0.f) {
-                    u32x2 v;
-                    v[0] = (uint32_t)narrow(T{}, a.alpha * acc[i][j][0]) |
-                           ((uint32_t)narrow(T{}, a.alpha * acc[i][j][1]) << 16);
-                    v[1] = (uint32_t)narrow(T{}, a.alpha * acc[i][j][2]) |
-                           ((uint32_t)narrow(T{}, a.alpha * acc[i][j][3]) << 16);
-                    *reinterpret_cast<u32x2*>(dst) = v;
-                } else {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) dst[q] = axpby<T>(acc[i][j][q], a.alpha, a.beta, dst + q);
-                }
-            }
-        }
+        pipelined_store<T, TF, RAG>(a, b, m0, n0, wm, wn, lr, lq, acc);
         // The next batch's prologue overwrites every stage.
         __syncthreads();
     }
@@ -1008,21 +1030,8 @@ __global__ __launch_bounds__(LThreads, TF == 8 ? 1 : 2) void gemm_mfma_pair(Gemm
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = w >> 1, wn = w & 1;
-    const int64_t tiles_m = RAG ? (a.m + BM - 1) / BM : a.m / BM;
-    const int64_t tiles_n = RAG ? (a.n + BM - 1) / BM : a.n / BM;
-    const int64_t ntiles = tiles_m * tiles_n;
-
-    // XCD-aware grouped tile order.
-    const int64_t bid = blockIdx.x;
-    const int64_t per_xcd = (ntiles + 7) / 8;
-    const int64_t t = (bid % 8) * per_xcd + bid / 8;
-    if (t >= ntiles) return;
-    const int64_t group = t / (LGM * tiles_n);
-    const int64_t first_m = group * LGM;
-    const int64_t gsize = tiles_m - first_m < LGM ? tiles_m - first_m : LGM;
-    const int64_t tm = first_m + (t % (LGM * tiles_n)) % gsize;
-    const int64_t tn = (t % (LGM * tiles_n)) / gsize;
-    const int64_t m0 = tm * BM, n0 = tn * BM;
+    int64_t m0, n0;
+    if (!pipelined_tile<BM, RAG>(a, m0, n0)) return;
     const int nk = (int)(a.k / LBK);  // a multiple of LSTAGES, at least 2 * LSTAGES
     const int lda = (int)a.lda, ldb = (int)a.ldb;
 
@@ -1054,20 +1063,11 @@ __global__ __launch_bounds__(LThreads, TF == 8 ? 1 : 2) void gemm_mfma_pair(Gemm
     const int kB0 = kb0 ^ (32 * TF * wn), kB1 = kb1 ^ (32 * TF * wn);
 
     for (int64_t b = blockIdx.y; b < a.batch; b += gridDim.y) {
-        const uint16_t* A = reinterpret_cast<const uint16_t*>(a.A) + b * a.sa + (KA ? m0 * a.lda : m0);
-        const uint16_t* B = reinterpret_cast<const uint16_t*>(a.B) + b * a.sb + (KB ? n0 * a.ldb : n0);
+        // Rows (K-contiguous) or columns (K-strided) of this tile inside the operand.
         const int64_t mrows = RAG && a.m - m0 < BM ? a.m - m0 : BM;
         const int64_t nrows = RAG && a.n - n0 < BM ? a.n - n0 : BM;
-        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(A), (short)0,
-            RAG ? (int)((KA ? (mrows - 1) * a.lda + a.k : (a.k - 1) * a.lda + mrows) * 2)
-                : (KA ? BM * lda * 2 : (int)(((a.k - 1) * a.lda + BM) * 2)),
-            0x00020000);
-        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(B), (short)0,
-            RAG ? (int)((KB ? (nrows - 1) * a.ldb + a.k : (a.k - 1) * a.ldb + nrows) * 2)
-                : (KB ? BM * ldb * 2 : (int)(((a.k - 1) * a.ldb + BM) * 2)),
-            0x00020000);
+        const __amdgpu_buffer_rsrc_t ra = pipelined_rsrc<BM, KA, RAG>(a.A, b * a.sa, m0, a.lda, a.k, mrows);
+        const __amdgpu_buffer_rsrc_t rb = pipelined_rsrc<BM, KB, RAG>(a.B, b * a.sb, n0, a.ldb, a.k, nrows);
 
         // DMA instruction q (operand q % 2, its instruction q / 2) of pair
         // `pair` into region R (stages 2R and 2R + 1).
@@ -1210,33 +1210,7 @@ __global__ __launch_bounds__(LThreads, TF == 8 ? 1 : 2) void gemm_mfma_pair(Gemm
         ktile(ic<2>{}, bc<true>{}, ic<0>{}, 0);
         ktile(ic<3>{}, bc<false>{}, ic<0>{}, 0);
 
-        // Lane holds C[m = 16i-slab base + lane%16][n = 16j-slab base + 4 (lane/16) + q].
-        uint16_t* C = reinterpret_cast<uint16_t*>(a.C) + b * a.sc;
-#pragma unroll
-        for (int i = 0; i < TF; ++i) {
-            const int64_t gm = m0 + wm * WT + i * 16 + lr;
-            if (RAG && gm >= a.m) continue;
-#pragma unroll
-            for (int j = 0; j < TF; ++j) {
-                const int64_t gn = n0 + wn * WT + j * 16 + lq * 4;
-                uint16_t* dst = C + gm * a.ldc + gn;
-                if (RAG && gn + 4 > a.n) {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        if (gn + q < a.n) dst[q] = axpby<T>(acc[i][j][q], a.alpha, a.beta, dst + q);
-                } else if (a.beta == 0.f) {
-                    u32x2 v;
-                    v[0] = (uint32_t)narrow(T{}, a.alpha * acc[i][j][0]) |
-                           ((uint32_t)narrow(T{}, a.alpha * acc[i][j][1]) << 16);
-                    v[1] = (uint32_t)narrow(T{}, a.alpha * acc[i][j][2]) |
-                           ((uint32_t)narrow(T{}, a.alpha * acc[i][j][3]) << 16);
-                    *reinterpret_cast<u32x2*>(dst) = v;
-                } else {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) dst[q] = axpby<T>(acc[i][j][q], a.alpha, a.beta, dst + q);
-                }
-            }
-        }
+        pipelined_store<T, TF, RAG>(a, b, m0, n0, wm, wn, lr, lq, acc);
         // The next batch's prologue overwrites every stage.
         __syncthreads();
     }
