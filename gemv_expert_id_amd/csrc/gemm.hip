@@ -1010,8 +1010,8 @@ __global__ __launch_bounds__(LThreads, TF == 8 ? 1 : 2) void gemm_mfma_large(Gem
 // refilled once both have been read, which the barrier of every odd k-tile
 // establishes; even k-tiles need none. The DMA of pair P + 2 is issued during
 // the second half of k-tile 2P + 1 and the first half of k-tile 2P + 2.
-template <class T, int TF, bool KA = true, bool KB = true, bool RAG = false>
-__global__ __launch_bounds__(LThreads, TF == 8 ? 1 : 2) void gemm_mfma_pair(GemmArgs a) {
+template <class T, int TF, bool KA = true, bool KB = true, bool RAG = false, int NREG = 2>
+__global__ __launch_bounds__(LThreads, TF == 8 || NREG > 2 ? 1 : 2) void gemm_mfma_pair(GemmArgs a) {
     using L = LTile<TF>;
     constexpr int BM = L::BM, IPW = L::IPW;
     constexpr int HF = TF / 2;          // A fragments per half of the wave tile
@@ -1025,14 +1025,16 @@ __global__ __launch_bounds__(LThreads, TF == 8 ? 1 : 2) void gemm_mfma_pair(Gemm
     constexpr int MPR = HF * TF / NDP;  // MFMAs per DMA instruction while a half-pair goes out
     constexpr int DSA = KA ? 1 : 2, DSB = KB ? 1 : 2;  // LDS reads per fragment
     static_assert(2 * IPW == NDP, "a pair of k-major stages takes as many DMA instructions");
-    static_assert(2 * REG * sizeof(uint16_t) == pipelined_lds_bytes<TF>(KA, KB), "same LDS as four stages");
+    static_assert(NREG > 2 || 2 * REG * sizeof(uint16_t) == pipelined_lds_bytes<TF>(KA, KB),
+                  "two regions take the LDS of four stages");
+    constexpr int NS = 2 * NREG;        // stages in the ring
     extern __shared__ __attribute__((aligned(1024))) uint16_t lds[];  // [region][A | B][row][64]
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = w >> 1, wn = w & 1;
     int64_t m0, n0;
     if (!pipelined_tile<BM, RAG>(a, m0, n0)) return;
-    const int nk = (int)(a.k / LBK);  // a multiple of LSTAGES, at least 2 * LSTAGES
+    const int nk = (int)(a.k / LBK);  // a multiple of NS, at least 2 * NS
     const int lda = (int)a.lda, ldb = (int)a.ldb;
 
     // DMA, K-contiguous operand: instruction j of a wave covers tile rows
@@ -1154,11 +1156,11 @@ __global__ __launch_bounds__(LThreads, TF == 8 ? 1 : 2) void gemm_mfma_pair(Gemm
         // the first half (even kt), 1 = first half of pair pq in the second
         // (odd kt), 0 = none. NEXT: tile kt+1 exists; an odd kt then waits
         // for all DMA (pair (kt+1)/2) and holds the barrier.
-        auto ktile = [&](auto S_, auto NEXT, auto DQ, int pq) {
-            constexpr int s = decltype(S_)::value, sn = (s + 1) % LSTAGES;
+        auto ktile = [&](auto S_, auto NEXT, auto DQ, auto VM, int pq) {
+            constexpr int s = decltype(S_)::value, sn = (s + 1) % NS;
             constexpr int dq = decltype(DQ)::value;
             constexpr bool nx = decltype(NEXT)::value;
-            constexpr int RQ = (s == 0 || s == 3) ? 1 : 0;  // region of the pair going out
+            constexpr int RQ = s % 2 ? s / 2 : (s / 2 + NREG - 1) % NREG;  // region of the pair going out
             auto& fb = (s % 2 == 0) ? fb0 : fb1;
             auto& fbn = (s % 2 == 0) ? fb1 : fb0;
             rda(S_, 1, fa1);
@@ -1170,7 +1172,7 @@ __global__ __launch_bounds__(LThreads, TF == 8 ? 1 : 2) void gemm_mfma_pair(Gemm
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (nx) {
                 if constexpr (s % 2 == 1) {
-                    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+                    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(decltype(VM)::value));
                     __builtin_amdgcn_s_barrier();
                 }
                 rda(ic<sn>{}, 0, fa0);
@@ -1184,31 +1186,35 @@ __global__ __launch_bounds__(LThreads, TF == 8 ? 1 : 2) void gemm_mfma_pair(Gemm
             __builtin_amdgcn_sched_barrier(0);
         };
 
-        // Prologue: pairs 0 and 1 (k-tiles 0-3); wait for pair 0.
-        static_for(std::make_integer_sequence<int, LPP>{}, [&](auto Q_) { dma(ic<0>{}, 0, Q_); });
-        static_for(std::make_integer_sequence<int, LPP>{}, [&](auto Q_) { dma(ic<1>{}, 1, Q_); });
-        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(LPP));
+        // Prologue: pairs 0 .. NREG-1 (k-tiles 0 .. NS-1); wait for pair 0.
+        static_for(std::make_integer_sequence<int, NREG>{}, [&](auto R_) {
+            static_for(std::make_integer_sequence<int, LPP>{}, [&](auto Q_) { dma(R_, decltype(R_)::value, Q_); });
+        });
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((NREG - 1) * LPP));
         __builtin_amdgcn_s_barrier();
         rda(ic<0>{}, 0, fa0);
         rdb(ic<0>{}, fb0);
-        // First round: pair 1's second half went out with the prologue.
-        ktile(ic<0>{}, bc<true>{}, ic<0>{}, 0);
-        ktile(ic<1>{}, bc<true>{}, ic<1>{}, 2);
-        ktile(ic<2>{}, bc<true>{}, ic<2>{}, 2);
-        ktile(ic<3>{}, bc<true>{}, ic<1>{}, 3);
-        int kt0 = LSTAGES;
-        for (; kt0 + 2 * LSTAGES <= nk; kt0 += LSTAGES) {
-            const int p0 = kt0 / 2;
-            ktile(ic<0>{}, bc<true>{}, ic<2>{}, p0 + 1);
-            ktile(ic<1>{}, bc<true>{}, ic<1>{}, p0 + 2);
-            ktile(ic<2>{}, bc<true>{}, ic<2>{}, p0 + 2);
-            ktile(ic<3>{}, bc<true>{}, ic<1>{}, p0 + 3);
-        }
+        // Odd k-tile kt = 2P + 1 sends out the first half of pair P + NREG,
+        // the even k-tile after it the second half; an odd k-tile's barrier
+        // lets the pairs after P + 1 stay in flight (VMS instructions).
+        constexpr int VMS = (NREG - 2) * LPP;
+        auto round = [&](auto FIRST, int kt0) {
+            static_for(std::make_integer_sequence<int, NS>{}, [&](auto S_) {
+                constexpr int s = decltype(S_)::value;
+                constexpr int dq = s % 2 ? 1 : (decltype(FIRST)::value && s == 0 ? 0 : 2);
+                ktile(S_, bc<true>{}, ic<dq>{}, ic<VMS>{}, kt0 / 2 + s / 2 + (s % 2 ? NREG : NREG - 1));
+            });
+        };
+        // First round: pair NREG-1's second half went out with the prologue.
+        round(bc<true>{}, 0);
+        int kt0 = NS;
+        for (; kt0 + 2 * NS <= nk; kt0 += NS) round(bc<false>{}, kt0);
         // Last round: the second half of the last pair, then no new tiles.
-        ktile(ic<0>{}, bc<true>{}, ic<2>{}, kt0 / 2 + 1);
-        ktile(ic<1>{}, bc<true>{}, ic<0>{}, 0);
-        ktile(ic<2>{}, bc<true>{}, ic<0>{}, 0);
-        ktile(ic<3>{}, bc<false>{}, ic<0>{}, 0);
+        static_for(std::make_integer_sequence<int, NS>{}, [&](auto S_) {
+            constexpr int s = decltype(S_)::value;
+            constexpr int vm = NREG - 2 - s / 2 > 0 ? (NREG - 2 - s / 2) * LPP : 0;
+            ktile(S_, bc<(s < NS - 1)>{}, ic<s == 0 ? 2 : 0>{}, ic<vm>{}, kt0 / 2 + NREG - 1);
+        });
 
         pipelined_store<T, TF, RAG>(a, b, m0, n0, wm, wn, lr, lq, acc);
         // The next batch's prologue overwrites every stage.
@@ -1393,13 +1399,13 @@ __global__ __launch_bounds__(kWave) void gemm_f32_mfma_small(GemmArgs a) {
 // The pipelined kernel for a transpose layout: A K-contiguous unless ta, B
 // K-contiguous when tb; the paired-stage form when `pair` (NT, and NN / TT
 // that are not ragged).
-template <class T, int TF, bool RAG>
+template <class T, int TF, bool RAG, int NREG = 2>
 const void* pick_pipelined(bool ta, bool tb, bool pair) {
     if (pair && !(ta && !tb)) {  // (the launcher never pairs TN, nor ragged NN / TT)
-        if (!ta && tb) return reinterpret_cast<const void*>(&gemm_mfma_pair<T, TF, true, true, RAG>);
+        if (!ta && tb) return reinterpret_cast<const void*>(&gemm_mfma_pair<T, TF, true, true, RAG, NREG>);
         if constexpr (!RAG) {
-            if (!ta) return reinterpret_cast<const void*>(&gemm_mfma_pair<T, TF, true, false, false>);
-            return reinterpret_cast<const void*>(&gemm_mfma_pair<T, TF, false, true, false>);
+            if (!ta) return reinterpret_cast<const void*>(&gemm_mfma_pair<T, TF, true, false, false, NREG>);
+            return reinterpret_cast<const void*>(&gemm_mfma_pair<T, TF, false, true, false, NREG>);
         }
     }
     if (!ta && tb) return reinterpret_cast<const void*>(&gemm_mfma_large<T, TF, true, true, RAG>);
@@ -1410,6 +1416,16 @@ const void* pick_pipelined(bool ta, bool tb, bool pair) {
 template <class T, int TF>
 const void* pick_pipelined(bool ta, bool tb, bool rag, bool pair) {
     return rag ? pick_pipelined<T, TF, true>(ta, tb, pair) : pick_pipelined<T, TF, false>(ta, tb, pair);
+}
+// 128 x 128 tiles, paired stages in four regions (one block per CU).
+template <class T>
+const void* pick_pair4(bool ta, bool tb, bool rag) {
+    return rag ? pick_pipelined<T, 4, true, 4>(ta, tb, true) : pick_pipelined<T, 4, false, 4>(ta, tb, true);
+}
+// Dynamic LDS of the paired-stage form with NREG regions.
+template <int TF, int NREG>
+constexpr size_t pair_lds_bytes(bool ka, bool kb) {
+    return (size_t)NREG * ((ka ? 1 : 0) + (kb ? 1 : 0)) * LTile<TF>::BM * 2 * LBK * sizeof(uint16_t);
 }
 
 template <int TILE>
@@ -1479,16 +1495,25 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, Launched* L) {
         // form; TN (both K-strided) spills registers in the paired form's loop
         // and keeps it too.
         const bool ka = !a.ta, kb = a.tb;  // operands K-contiguous
-        const bool pair = (big || tiles * a.batch > 256) && ((ka && kb) || (ka != kb && !rag));
-        const void* fn = big ? (a.dtype == 1 ? pick_pipelined<TF16, 8>(a.ta, a.tb, rag, pair)
-                                             : pick_pipelined<TBF16, 8>(a.ta, a.tb, rag, pair))
-                             : (a.dtype == 1 ? pick_pipelined<TF16, 4>(a.ta, a.tb, rag, pair)
-                                             : pick_pipelined<TBF16, 4>(a.ta, a.tb, rag, pair));
+        const bool pairable = (ka && kb) || (ka != kb && !rag);
+        const bool pair = (big || tiles * a.batch > 256) && pairable;
+        // At most one 128 x 128 tile per CU: the paired form in four regions
+        // (three pairs of lookahead) when k allows whole rounds of them.
+        const bool pair4 = !big && !pair && pairable && a.k % (8 * LBK) == 0 && a.k >= 16 * LBK;
+        const void* fn = big    ? (a.dtype == 1 ? pick_pipelined<TF16, 8>(a.ta, a.tb, rag, pair)
+                                                : pick_pipelined<TBF16, 8>(a.ta, a.tb, rag, pair))
+                       : pair4 ? (a.dtype == 1 ? pick_pair4<TF16>(a.ta, a.tb, rag)
+                                               : pick_pair4<TBF16>(a.ta, a.tb, rag))
+                               : (a.dtype == 1 ? pick_pipelined<TF16, 4>(a.ta, a.tb, rag, pair)
+                                               : pick_pipelined<TBF16, 4>(a.ta, a.tb, rag, pair));
         const unsigned grid = (unsigned)(((tiles + 7) / 8) * 8);
         L->kernel = MM_KERNEL_GEMM_LARGE;
-        L->variant = (big ? LTile<8>::BM : LTile<4>::BM) + (pair ? 1 : 0);
+        L->variant = (big ? LTile<8>::BM : LTile<4>::BM) + (pair || pair4 ? 1 : 0);
         return hipLaunchKernel(fn, dim3(grid, gy), dim3(LThreads), args,
-                               big ? pipelined_lds_bytes<8>(ka, kb) : pipelined_lds_bytes<4>(ka, kb), s);
+                               big     ? pipelined_lds_bytes<8>(ka, kb)
+                               : pair4 ? pair_lds_bytes<4, 4>(ka, kb)
+                                       : pipelined_lds_bytes<4>(ka, kb),
+                               s);
     }
     constexpr int PNW = 64;  // B tile rows of the panel kernel
     const int64_t panel_items = (a.m / 64) * a.batch;

@@ -356,11 +356,17 @@ def test_pair_kernel_batched_padded_offsets():
     (True, True, 2, 1152, 1280, 256, 128),    # TT, 180 tiles of 128 x 128: four stages
     (True, True, 1, 1000, 2304, 256, 128),    # TT ragged: four stages
     (True, False, 1, 3072, 4096, 256, 256),   # TN: four stages
+    (False, True, 1, 1024, 2048, 512, 129),   # NT, 128 tiles, k % 256 == 0, k >= 512: four regions
+    (False, False, 1, 1024, 2048, 512, 129),  # NN, the same
+    (False, False, 1, 1000, 2048, 512, 128),  # NN ragged: four stages
+    (True, False, 1, 1024, 2048, 512, 128),   # TN: four stages
+    (False, True, 1, 1024, 2048, 384, 128),   # k not a multiple of 256: four stages
 ])
 def test_pipelined_form_rule(ta, tb, b, m, n, k, variant):
     """The receipt names the pipelined kernel's tile edge and, in its low bit,
     the paired-stage form: NT with 256 x 256 tiles or more than 256 tiles of
-    128 x 128; NN and TT the same unless ragged; TN never."""
+    128 x 128, or (four regions) at most 256 of them with k a multiple of 256
+    and at least 512; NN and TT the same unless ragged; TN never."""
     import torch
     from gpu_util import GemmRun
     _say(f"pipelined form rule ta={int(ta)} tb={int(tb)} b={b} {m}x{n}x{k}")
@@ -369,6 +375,23 @@ def test_pipelined_form_rule(ta, tb, b, m, n, k, variant):
     rec = run.run()
     torch.cuda.synchronize()
     assert (rec.kernel, rec.variant) == (mm.MM_KERNEL_GEMM_LARGE, variant), (rec.kernel, rec.variant)
+
+
+@pytest.mark.parametrize("dt,ta,tb,b,m,n,k", [
+    (wl.F16, False, True, 1, 512, 1024, 1024),   # NT, 32 tiles; the steady loop runs twice
+    (wl.BF16, False, False, 1, 384, 640, 512),   # NN, first and last rounds only
+    (wl.F16, True, True, 2, 256, 384, 1536),     # TT
+    (wl.F16, False, True, 1, 200, 300, 512),     # NT ragged
+    (wl.BF16, False, True, 3, 256, 128, 768),    # NT batched, one steady round
+])
+def test_pair_kernel_four_regions(dt, ta, tb, b, m, n, k):
+    """At most one 128 x 128 tile per CU and k a multiple of 256 (>= 512):
+    the paired-stage form with four LDS regions. Every output against the
+    oracle."""
+    _say(f"pair4 dt={wl.DTYPE_NAMES[dt]} ta={int(ta)} tb={int(tb)} b={b} {m}x{n}x{k}")
+    case = wl.random_gemm_case(97 + k % 5, dt, b, m, n, k, ta, tb)
+    rec = check_gemm(case, what=f"pair4 {b}x{m}x{n}x{k}")
+    assert (rec.kernel, rec.variant) == (mm.MM_KERNEL_GEMM_LARGE, 129), (rec.kernel, rec.variant)
 
 
 @pytest.mark.parametrize("dt", [wl.F16, wl.BF16])
