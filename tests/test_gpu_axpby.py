@@ -168,13 +168,17 @@ def test_axpby_ramp_bit_exact(dt):
 
 
 # The pipelined kernel (128 x 128 tiles here) in every transpose layout with
-# m and n off the tile edge: ragged edge tiles take the per-element epilogue.
+# m and n off the tile edge: ragged edge tiles take the per-element epilogue;
+# the last three cases run its paired-stage forms.
 PIPELINED_CASES = [
     # (batch, m, n, k, ta, tb)
     (1, 200, 132, 256, False, True),
     (1, 100, 136, 256, False, False),
     (2, 136, 76, 384, True, True),
     (1, 136, 200, 256, True, False),
+    (1, 1000, 516, 512, False, True),   # paired stages, four regions, ragged
+    (1, 256, 384, 1024, False, False),  # paired stages, four regions, NN
+    (1, 2304, 2052, 256, False, True),  # paired stages, two regions (306 tiles), ragged
 ]
 
 
